@@ -1,0 +1,125 @@
+"""ctypes front end of the fp64 paged-attention oracle.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  The HIP library and
+its Python binding never do; a product path that reached this code would not be
+a GPU result.
+
+The arithmetic lives in ``paged_attn_oracle.c``: the plain definition
+out = softmax(scale * q K^T) V and lse = ln(sum exp(scale * q K^T)) over the
+tokens a request's block table names, in fp64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_LIB_CACHE: dict[str, ctypes.CDLL] = {}
+
+
+class OracleShape(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("max_blocks", ctypes.c_int32),
+    ]
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load (building first if it is absent) the oracle library at ``path``."""
+    path = path or _build.LIB
+    if path in _LIB_CACHE:
+        return _LIB_CACHE[path]
+    if path == _build.LIB and not os.path.exists(path):
+        _build.build()
+    lib = ctypes.CDLL(path)
+    p = ctypes.c_void_p
+    lib.oracle_validate.argtypes = [ctypes.POINTER(OracleShape), p, p]
+    lib.oracle_validate.restype = ctypes.c_int
+    lib.oracle_attend_one.argtypes = [ctypes.POINTER(OracleShape), p, p, p, p, p, ctypes.c_double,
+                                      ctypes.c_int32, ctypes.c_int32, p, p]
+    lib.oracle_attend_one.restype = ctypes.c_int
+    lib.oracle_paged_attn.argtypes = [ctypes.POINTER(OracleShape), p, p, p, p, p, ctypes.c_double, p, p]
+    lib.oracle_paged_attn.restype = ctypes.c_int
+    lib.oracle_paged_attn_pairs.argtypes = [ctypes.POINTER(OracleShape), p, p, p, p, p, ctypes.c_double,
+                                            p, ctypes.c_int32, p, p]
+    lib.oracle_paged_attn_pairs.restype = ctypes.c_int
+    lib.oracle_max_threads.argtypes = []
+    lib.oracle_max_threads.restype = ctypes.c_int
+    _LIB_CACHE[path] = lib
+    return lib
+
+
+def _prep(q, k_pool, v_pool, block_table, context_lens):
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    k_pool = np.ascontiguousarray(k_pool, dtype=np.uint16)
+    v_pool = np.ascontiguousarray(v_pool, dtype=np.uint16)
+    block_table = np.ascontiguousarray(block_table, dtype=np.int32)
+    context_lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    if q.ndim != 3 or k_pool.ndim != 4 or k_pool.shape != v_pool.shape:
+        raise OracleError("q must be [B,Hq,D]; pools must be [P,page,Hkv,D] and equal in shape")
+    B, Hq, D = q.shape
+    P, page, Hkv, Dk = k_pool.shape
+    if Dk != D or block_table.ndim != 2 or block_table.shape[0] != B or context_lens.shape != (B,):
+        raise OracleError("inconsistent shapes")
+    shape = OracleShape(B, Hq, Hkv, D, page, P, block_table.shape[1])
+    return shape, q, k_pool, v_pool, block_table, context_lens
+
+
+def paged_attn(q, k_pool, v_pool, block_table, context_lens, scale, *, lib: ctypes.CDLL | None = None):
+    """fp64 (out [B,Hq,D], lse [B,Hq]) for every request and query head."""
+    lib = lib or load()
+    shape, q, k_pool, v_pool, block_table, context_lens = _prep(q, k_pool, v_pool, block_table, context_lens)
+    out = np.zeros((shape.num_seqs, shape.num_q_heads, shape.head_dim), dtype=np.float64)
+    lse = np.zeros((shape.num_seqs, shape.num_q_heads), dtype=np.float64)
+    rc = lib.oracle_paged_attn(ctypes.byref(shape), q.ctypes.data, k_pool.ctypes.data, v_pool.ctypes.data,
+                               block_table.ctypes.data, context_lens.ctypes.data, float(scale),
+                               out.ctypes.data, lse.ctypes.data)
+    if rc != 0:
+        raise OracleError(f"oracle_paged_attn returned {rc}")
+    return out, lse
+
+
+def paged_attn_pairs(q, k_pool, v_pool, block_table, context_lens, scale, pairs, *,
+                     lib: ctypes.CDLL | None = None):
+    """fp64 (out [n,D], lse [n]) for the (request, query head) pairs listed."""
+    lib = lib or load()
+    shape, q, k_pool, v_pool, block_table, context_lens = _prep(q, k_pool, v_pool, block_table, context_lens)
+    pairs = np.ascontiguousarray(np.asarray(pairs, dtype=np.int32).reshape(-1, 2))
+    n = pairs.shape[0]
+    out = np.zeros((n, shape.head_dim), dtype=np.float64)
+    lse = np.zeros((n,), dtype=np.float64)
+    rc = lib.oracle_paged_attn_pairs(ctypes.byref(shape), q.ctypes.data, k_pool.ctypes.data,
+                                     v_pool.ctypes.data, block_table.ctypes.data, context_lens.ctypes.data,
+                                     float(scale), pairs.ctypes.data, n, out.ctypes.data, lse.ctypes.data)
+    if rc != 0:
+        raise OracleError(f"oracle_paged_attn_pairs returned {rc}")
+    return out, lse
+
+
+def run_case(case, *, lib: ctypes.CDLL | None = None):
+    """Oracle over a ``workloads.Case`` (any object with the same fields)."""
+    return paged_attn(case.q, case.k_pool, case.v_pool, case.block_table, case.context_lens,
+                      case.scale, lib=lib)
+
+
+def validate(q, k_pool, v_pool, block_table, context_lens, *, lib: ctypes.CDLL | None = None) -> int:
+    lib = lib or load()
+    shape, q, k_pool, v_pool, block_table, context_lens = _prep(q, k_pool, v_pool, block_table, context_lens)
+    return int(lib.oracle_validate(ctypes.byref(shape), block_table.ctypes.data, context_lens.ctypes.data))
+
+
+def max_threads(lib: ctypes.CDLL | None = None) -> int:
+    return int((lib or load()).oracle_max_threads())

@@ -1,0 +1,14 @@
+"""Seeded synthetic inputs for paged GQA decode attention.
+
+This package only draws random numbers and lays them out as a paged KV cache;
+it performs none of the attention arithmetic.  Both the CPU oracle (``oracle/``)
+and the HIP library are fed from here, and neither imports the other.
+"""
+from .gen import (  # noqa: F401
+    CONFIGS,
+    Case,
+    bf16_bits_to_f32,
+    f32_to_bf16_bits,
+    make_case,
+    make_config,
+)
