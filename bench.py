@@ -1,0 +1,259 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark on one MI355X.
+
+A step is one decode step's attention over all 28 layers of the
+Qwen3-0.6B-shaped decoder (audio.cpp "Fun-ASR-Nano Native Runtime Design",
+"Decoder And Prompt": 28 layers, 16 query / 8 KV heads): 28 calls of
+``hipdecode_paged_attn``, layer i reading its own KV pools.  The pools are
+rotated over R distinct device copies so that every call streams from HBM
+rather than from the 256 MB last-level cache.  All inputs are resident in HBM
+before the timed region starts.
+
+value   = decode tokens/s = B * steps / (timed seconds)
+roofline.achieved = algorithmic bytes per call / average call duration,
+          timed with HIP events on the stream the kernel runs on.
+cpu_baseline = the fp64 oracle, unmodified, on this host's cores, over one
+          layer's worth of (request, head) pairs, scaled to tokens/s.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode attn tokens/s and achieved HBM GB/s (% of peak) at 28k/64k ctx"
+PEAK_HBM_GBS = 8000.0
+LAYERS = 28
+ROTATE_MIN_BYTES = 1.5e9
+KERNEL_SOURCES = ["paged_kv_decode_gqa_amd/csrc/paged_decode.hip",
+                  "paged_kv_decode_gqa_amd/csrc/api.hip",
+                  "paged_kv_decode_gqa_amd/csrc/internal.h"]
+KERNEL_NAME = "paged_decode_kernel"
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(case, out_bytes: int) -> int:
+    """Bytes the method must move per call: every cached K and V row of the
+    context once, q, out, lse, the block-table entries used and the lengths."""
+    import numpy as np
+    ctx = case.context_lens.astype(np.int64)
+    kv_per_token = 2 * case.Hkv * case.D * 2
+    blocks = int(((ctx + case.page - 1) // case.page).sum())
+    rows = case.B * case.Hq
+    return int(kv_per_token * ctx.sum() + rows * case.D * 2 + rows * case.D * out_bytes + rows * 4
+               + 4 * blocks + 4 * case.B)
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken on the kernel as it is now."""
+    path = os.path.join(ROOT, "profiles", f"{KERNEL_NAME}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        line = line.strip()
+        if line and not line.startswith("#") and "=" in line:
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        fetch = float(kv["fetch_kib_per_dispatch"]) * float(kv.get("copy_scale_fetch", 1.0))
+        write = float(kv["write_kib_per_dispatch"]) * float(kv.get("copy_scale_write", 1.0))
+    except (KeyError, ValueError):
+        return None
+    return (fetch + write) * 1024.0
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c3", "c4", "c5", "c3b"])
+    ap.add_argument("--partition", type=int, default=0, help="split-K partition tokens (0 = planner)")
+    ap.add_argument("--rotate", type=int, default=0, help="distinct KV pool copies (0 = auto)")
+    ap.add_argument("--graph", action="store_true", help="replay one captured step per step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path has no multi-GPU sharding in this build)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import paged_kv_decode_gqa_amd as hd
+    from workloads import make_config
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    hd.library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t0 = time.time()
+    case = make_config(args.workload)
+    t_gen = time.time() - t0
+    out_dtype = torch.float32 if case.out_dtype == "f32" else torch.bfloat16
+    out_bytes = 4 if case.out_dtype == "f32" else 2
+    alg_bytes = algorithmic_bytes(case, out_bytes)
+    kv_bytes_call = 2 * case.Hkv * case.D * 2 * case.total_tokens
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    pool_bytes = 2 * case.k_pool.nbytes
+    R = args.rotate or max(2, min(LAYERS, math.ceil(ROTATE_MIN_BYTES / max(1, kv_bytes_call))))
+    q = bf(case.q)
+    k0, v0 = bf(case.k_pool), bf(case.v_pool)
+    pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(R - 1)]
+    table = torch.from_numpy(case.block_table).to(dev)
+    ctx = torch.from_numpy(case.context_lens).to(dev)
+    params = hd.make_params(num_seqs=case.B, num_q_heads=case.Hq, num_kv_heads=case.Hkv,
+                            num_pages=case.num_pages, max_blocks_per_seq=case.max_blocks,
+                            max_context_len=case.max_context_len, scale=case.scale,
+                            partition_tokens=args.partition,
+                            out_dtype=hd.HIPDECODE_F32 if out_bytes == 4 else hd.HIPDECODE_BF16)
+    st = hd.hipdecode_check_params(params)
+    if st != 0:
+        raise hd.HipDecodeError(st, "params")
+    part = hd.hipdecode_partition_tokens(params)
+    ws = torch.zeros(hd.hipdecode_workspace_bytes(params) // 4 + 4, dtype=torch.int32, device=dev)
+    out = torch.empty((case.B, case.Hq, case.D), dtype=out_dtype, device=dev)
+    lse = torch.empty((case.B, case.Hq), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def one_step():
+        for layer in range(LAYERS):
+            kp, vp = pools[layer % R]
+            hd.hipdecode_paged_attn(params, q, kp, vp, table, ctx, out, lse, ws, stream)
+
+    graph = None
+    if args.graph:
+        one_step()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            one_step()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+    run = graph.replay if graph is not None else one_step
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        run()
+    ev1.record(stream)
+    ev1.synchronize()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = ev0.elapsed_time(ev1)
+    calls = args.steps * LAYERS
+    call_s = ms * 1e-3 / calls
+    value = case.B * args.steps / (ms * 1e-3)
+    achieved = alg_bytes / call_s / 1e9
+
+    # parity of the last call against the oracle, and the oracle's own speed
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 KV pages, shuffled pools; no dataset)",
+        "config": {
+            "workload": case.name,
+            "batch": case.B,
+            "context_tokens_total": case.total_tokens,
+            "max_context": case.max_context_len,
+            "num_q_heads": case.Hq,
+            "num_kv_heads": case.Hkv,
+            "head_dim": case.D,
+            "page_size": case.page,
+            "layers_per_step": LAYERS,
+            "partition_tokens": part,
+            "kv_pool_copies": R,
+            "mode": "hipgraph" if graph is not None else "eager",
+            "out_dtype": case.out_dtype,
+        },
+        "us_per_layer": round(call_s * 1e6, 3),
+        "kv_tokens_per_s": round(case.total_tokens / call_s, 1),
+        "wall_s_timed": round(wall, 4),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": KERNEL_NAME,
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": alg_bytes,
+            "avg_launch_us": round(call_s * 1e6, 3),
+        },
+        "cpu_baseline": None,
+    }
+    traffic = read_traffic(args.workload)
+    if traffic is not None:
+        result["roofline"]["traffic"] = round(traffic)
+
+    if not args.no_cpu_baseline:
+        import oracle
+        o_gpu = out.float().cpu().numpy().astype(np.float64)
+        reps, t_cpu = 0, 0.0
+        ref_out = None
+        while reps < 50 and (t_cpu < 10.0 or reps == 0):
+            c0 = time.perf_counter()
+            ref_out, _ = oracle.run_case(case)
+            t_cpu += time.perf_counter() - c0
+            reps += 1
+        t_layer = t_cpu / reps
+        result["cpu_baseline"] = {
+            "value": round(case.B / (LAYERS * t_layer), 4),
+            "unit": "tokens/s",
+            "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"fp64 oracle over all {case.B * case.Hq} (request, head) pairs of one layer call, "
+                      f"{reps} run(s), {t_layer:.3f} s per layer, scaled to {LAYERS} layers per token",
+            "parity_max_abs_err": float(np.abs(o_gpu - ref_out).max()),
+        }
+    result["setup_s"] = round(t_gen, 2)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,135 @@
+/*
+ * hipdecode.h -- C ABI of the MI355X (gfx950) paged GQA decode-attention library.
+ *
+ * One call computes the attention of one decode step for one layer: every
+ * request's single new query attends to all tokens of that request's paged KV
+ * cache.  This is the step that dominates long-audio transcription (MOSS-TD
+ * article, "Time spent: profiling": decode is over 94% of total time for long
+ * audio at concurrency 1), over a cache that prefill builds and decode extends
+ * one token per step ("ASR model basics"; "Chunked prefill for long audio"),
+ * stored in on-demand pages (FunASR vLLM guide, "Why vLLM?": PagedAttention).
+ * The decoder is Qwen3-0.6B-shaped (audio.cpp "Fun-ASR-Nano Native Runtime
+ * Design", "Decoder And Prompt": 16 query heads over 8 KV heads), so query
+ * heads share KV heads in groups of G = num_q_heads / num_kv_heads.
+ *
+ * For request b, query head h, G = num_q_heads / num_kv_heads, g = h / G,
+ * n = context_lens[b], and cached token t in [0, n) stored at
+ *     page = block_table[b * max_blocks_per_seq + t / 16], slot = t % 16:
+ *     z_t       = scale * dot(q[b][h][:], K[page][slot][g][:])
+ *     out[b][h] = sum_t softmax(z)_t * V[page][slot][g][:]
+ *     lse[b][h] = ln(sum_t exp(z_t))                 (natural log)
+ * n == 0 gives out = 0 and lse = -inf.
+ *
+ * Layouts (row-major, contiguous; element types in brackets):
+ *   q             [num_seqs][num_q_heads][128]               bf16
+ *   k_pool,v_pool [num_pages][16][num_kv_heads][128]         bf16
+ *   block_table   [num_seqs][max_blocks_per_seq]             int32
+ *   context_lens  [num_seqs]                                 int32
+ *   out           [num_seqs][num_q_heads][128]               bf16 or fp32 (out_dtype)
+ *   lse           [num_seqs][num_q_heads]                    fp32, may be NULL
+ *   workspace     hipdecode_workspace_bytes(params) bytes, zero-filled before
+ *                 its first use (hipdecode_workspace_init or any zero fill);
+ *                 every completed call leaves its counters at zero again.
+ * q, k_pool, v_pool, out and workspace must be 16-byte aligned; all of them are
+ * device memory.  Supported shapes: head_dim 128, page size 16, G in {1, 2, 4}.
+ *
+ * Ownership and ordering.  The caller owns every buffer.  The library
+ * allocates nothing, keeps no per-call state, never synchronises the host and
+ * enqueues its work on `stream` (a hipStream_t; NULL is the null stream), so a
+ * call may be captured into a HIP graph.  Calls that share a workspace must be
+ * ordered (same stream, or synchronised); `out` and `lse` must not alias any
+ * input.
+ *
+ * Errors.  Argument errors are returned synchronously, before anything is
+ * enqueued.  HIPDECODE_ERR_HIP means the launch itself failed.  Faults while
+ * the kernel runs surface at the caller's next synchronisation.  Device-side
+ * contents are the caller's contract: context_lens[b] <= max_context_len and
+ * 0 <= block_table entries < num_pages for the ceil(n/16) blocks a request
+ * uses.  The kernel does not read memory outside the pools when that contract
+ * is broken (it clamps n to max_context_len and skips page indices outside
+ * the pool), but the values it then returns are unspecified.  Nothing aborts
+ * and no C++ exception crosses this interface.
+ */
+#ifndef HIPDECODE_H
+#define HIPDECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HIPDECODE_ABI_VERSION 1
+
+typedef enum {
+    HIPDECODE_OK = 0,
+    HIPDECODE_ERR_NULL = 1,        /* a required pointer is NULL */
+    HIPDECODE_ERR_SHAPE = 2,       /* inconsistent or out-of-range sizes */
+    HIPDECODE_ERR_UNSUPPORTED = 3, /* valid but not built: head_dim, page size, group, dtype */
+    HIPDECODE_ERR_ALIGN = 4,       /* a buffer is not 16-byte aligned */
+    HIPDECODE_ERR_WORKSPACE = 5,   /* workspace smaller than hipdecode_workspace_bytes */
+    HIPDECODE_ERR_SCALE = 6,       /* scale is not finite */
+    HIPDECODE_ERR_HIP = 7          /* the HIP runtime refused the launch */
+} hipdecode_status;
+
+typedef enum {
+    HIPDECODE_BF16 = 0,            /* out rounded to bf16, nearest-even */
+    HIPDECODE_F32 = 1
+} hipdecode_dtype;
+
+typedef struct {
+    int32_t num_seqs;              /* B >= 0; B == 0 is a no-op */
+    int32_t num_q_heads;           /* Hq */
+    int32_t num_kv_heads;          /* Hkv; Hq % Hkv == 0 */
+    int32_t head_dim;              /* must be 128 */
+    int32_t page_size;             /* tokens per page; must be 16 */
+    int32_t num_pages;             /* P, rows of each pool */
+    int32_t max_blocks_per_seq;    /* row stride of block_table, in int32 elements */
+    int32_t max_context_len;       /* host upper bound of context_lens[]; sizes the grid */
+    int32_t partition_tokens;      /* split-K partition: 0 = planner's choice, else a multiple of 64 */
+    int32_t out_dtype;             /* hipdecode_dtype */
+    float scale;                   /* applied to q.k, e.g. 1/sqrt(128) */
+} hipdecode_params;
+
+/* HIPDECODE_ABI_VERSION of the built library. */
+int hipdecode_abi_version(void);
+
+/* Pure host check of the parameter block (no HIP calls): HIPDECODE_OK or the
+ * first problem found.  A NULL pointer gives HIPDECODE_ERR_NULL. */
+hipdecode_status hipdecode_check_params(const hipdecode_params *params);
+
+/* Tokens per split-K partition that a call with these parameters uses (the
+ * planner's choice when partition_tokens is 0); 0 if the parameters are
+ * invalid.  Pure host function. */
+int32_t hipdecode_partition_tokens(const hipdecode_params *params);
+
+/* Bytes of workspace a call with these parameters needs; 0 if they are
+ * invalid.  Pure host function. */
+size_t hipdecode_workspace_bytes(const hipdecode_params *params);
+
+/* Zero-fills `bytes` bytes of workspace on `stream` with a fill kernel (no
+ * hipMemset node, so it is safe under graph capture). */
+hipdecode_status hipdecode_workspace_init(void *workspace, size_t bytes, void *stream);
+
+/* One decode step of paged GQA attention (see the top of this file). */
+hipdecode_status hipdecode_paged_attn(const hipdecode_params *params,
+                                      const void *q,
+                                      const void *k_pool,
+                                      const void *v_pool,
+                                      const int32_t *block_table,
+                                      const int32_t *context_lens,
+                                      void *out,
+                                      float *lse,
+                                      void *workspace,
+                                      size_t workspace_bytes,
+                                      void *stream);
+
+/* Static English text for a status code; never NULL. */
+const char *hipdecode_status_string(hipdecode_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HIPDECODE_H */

@@ -1,0 +1,188 @@
+"""Python binding of ``libhipdecode.so`` (the C ABI in ``include/hipdecode.h``).
+
+Argument marshalling only: every step of the attention runs in the library's
+HIP kernels.  The functions carry the C names; tensors are PyTorch device
+tensors and are passed as raw pointers on the current HIP stream.
+
+If the library has not been built, importing works but every call raises
+``RuntimeError``; there is no fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libhipdecode.so")
+
+HIPDECODE_OK = 0
+HIPDECODE_ERR_NULL = 1
+HIPDECODE_ERR_SHAPE = 2
+HIPDECODE_ERR_UNSUPPORTED = 3
+HIPDECODE_ERR_ALIGN = 4
+HIPDECODE_ERR_WORKSPACE = 5
+HIPDECODE_ERR_SCALE = 6
+HIPDECODE_ERR_HIP = 7
+HIPDECODE_BF16 = 0
+HIPDECODE_F32 = 1
+
+EXPORTED = (
+    "hipdecode_abi_version",
+    "hipdecode_check_params",
+    "hipdecode_partition_tokens",
+    "hipdecode_workspace_bytes",
+    "hipdecode_workspace_init",
+    "hipdecode_paged_attn",
+    "hipdecode_status_string",
+)
+
+
+class hipdecode_params(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("max_context_len", ctypes.c_int32),
+        ("partition_tokens", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+    ]
+
+
+class HipDecodeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({hipdecode_status_string(status)})")
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """The loaded HIP library; raises RuntimeError if it was never built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m paged_kv_decode_gqa_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(hipdecode_params)
+    vp = ctypes.c_void_p
+    lib.hipdecode_abi_version.argtypes = []
+    lib.hipdecode_abi_version.restype = ctypes.c_int
+    lib.hipdecode_check_params.argtypes = [P]
+    lib.hipdecode_check_params.restype = ctypes.c_int
+    lib.hipdecode_partition_tokens.argtypes = [P]
+    lib.hipdecode_partition_tokens.restype = ctypes.c_int32
+    lib.hipdecode_workspace_bytes.argtypes = [P]
+    lib.hipdecode_workspace_bytes.restype = ctypes.c_size_t
+    lib.hipdecode_workspace_init.argtypes = [vp, ctypes.c_size_t, vp]
+    lib.hipdecode_workspace_init.restype = ctypes.c_int
+    lib.hipdecode_paged_attn.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.hipdecode_paged_attn.restype = ctypes.c_int
+    lib.hipdecode_status_string.argtypes = [ctypes.c_int]
+    lib.hipdecode_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def make_params(*, num_seqs, num_q_heads, num_kv_heads, num_pages, max_blocks_per_seq,
+                max_context_len, scale, head_dim=128, page_size=16, partition_tokens=0,
+                out_dtype=HIPDECODE_BF16) -> hipdecode_params:
+    return hipdecode_params(int(num_seqs), int(num_q_heads), int(num_kv_heads), int(head_dim),
+                            int(page_size), int(num_pages), int(max_blocks_per_seq),
+                            int(max_context_len), int(partition_tokens), int(out_dtype), float(scale))
+
+
+def hipdecode_abi_version() -> int:
+    return int(library().hipdecode_abi_version())
+
+
+def hipdecode_check_params(params: hipdecode_params | None) -> int:
+    return int(library().hipdecode_check_params(ctypes.byref(params) if params is not None else None))
+
+
+def hipdecode_partition_tokens(params: hipdecode_params) -> int:
+    return int(library().hipdecode_partition_tokens(ctypes.byref(params)))
+
+
+def hipdecode_workspace_bytes(params: hipdecode_params) -> int:
+    return int(library().hipdecode_workspace_bytes(ctypes.byref(params)))
+
+
+def hipdecode_status_string(status: int) -> str:
+    return library().hipdecode_status_string(int(status)).decode()
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream) if hasattr(stream, "cuda_stream") else ctypes.c_void_p(stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def hipdecode_workspace_init(workspace, stream=None) -> None:
+    nbytes = workspace.numel() * workspace.element_size()
+    st = library().hipdecode_workspace_init(_ptr(workspace), nbytes, _stream_handle(stream))
+    if st != HIPDECODE_OK:
+        raise HipDecodeError(st, "hipdecode_workspace_init")
+
+
+def hipdecode_paged_attn(params: hipdecode_params, q, k_pool, v_pool, block_table, context_lens,
+                         out, lse, workspace, stream=None) -> None:
+    """Enqueue one call on ``stream`` (default: torch's current stream).
+
+    Tensors must be contiguous device tensors laid out as ``include/hipdecode.h``
+    states; ``lse`` may be None.  Raises HipDecodeError on a non-OK status."""
+    for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool), ("block_table", block_table),
+                    ("context_lens", context_lens), ("out", out), ("lse", lse), ("workspace", workspace)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = library().hipdecode_paged_attn(ctypes.byref(params), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                        _ptr(block_table), _ptr(context_lens), _ptr(out), _ptr(lse),
+                                        _ptr(workspace), ws_bytes, _stream_handle(stream))
+    if st != HIPDECODE_OK:
+        raise HipDecodeError(st, "hipdecode_paged_attn")
+
+
+def paged_attn(q, k_pool, v_pool, block_table, context_lens, scale, *, max_context_len,
+               out_dtype=None, partition_tokens=0, out=None, lse=None, workspace=None):
+    """Allocate outputs (and a zeroed workspace) as needed and run one call.
+
+    q: bf16 [B,Hq,128]; k_pool, v_pool: bf16 [P,16,Hkv,128]; block_table: int32
+    [B, max_blocks]; context_lens: int32 [B].  Returns (out, lse)."""
+    import torch
+    if q.dtype != torch.bfloat16 or k_pool.dtype != torch.bfloat16 or v_pool.dtype != torch.bfloat16:
+        raise ValueError("q, k_pool and v_pool must be bfloat16")
+    if block_table.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_table and context_lens must be int32")
+    B, Hq, D = q.shape
+    P, page, Hkv, Dk = k_pool.shape
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else torch.bfloat16
+    code = HIPDECODE_F32 if out_dtype == torch.float32 else HIPDECODE_BF16
+    params = make_params(num_seqs=B, num_q_heads=Hq, num_kv_heads=Hkv, num_pages=P,
+                         max_blocks_per_seq=block_table.shape[1], max_context_len=max_context_len,
+                         scale=scale, head_dim=D, page_size=page, partition_tokens=partition_tokens,
+                         out_dtype=code)
+    st = hipdecode_check_params(params)
+    if st != HIPDECODE_OK:
+        raise HipDecodeError(st, "hipdecode_check_params")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nbytes = hipdecode_workspace_bytes(params)
+        workspace = torch.zeros(max(nbytes, 16) // 4 + 4, dtype=torch.int32, device=q.device)
+    hipdecode_paged_attn(params, q, k_pool, v_pool, block_table, context_lens, out, lse, workspace)
+    return out, lse

@@ -1,0 +1,213 @@
+// api.hip -- the extern "C" interface declared in include/hipdecode.h:
+// parameter checks, the split-K planner, the workspace layout and the launch.
+#include "hipdecode.h"
+#include "internal.h"
+
+#include <math.h>
+
+#define HIPDECODE_API extern "C" __attribute__((visibility("default")))
+
+namespace hipdecode {
+namespace {
+
+constexpr int64_t kTargetWorkgroups = 1024;   // ~4 per CU for the longest request's share
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Partition size: enough splits that B * Hkv * nsplit reaches the workgroup
+// target for the longest context, in multiples of 64 tokens, at least 256
+// tokens so each wavefront folds a few pages, at most 4096.
+int32_t plan_partition(const hipdecode_params &p)
+{
+    if (p.partition_tokens > 0)
+        return p.partition_tokens;
+    const int64_t pairs = (int64_t)p.num_seqs * p.num_kv_heads;
+    if (pairs <= 0 || p.max_context_len <= 0)
+        return 256;
+    const int64_t want_splits = ceil_div(kTargetWorkgroups, pairs);
+    int64_t part = ceil_div(p.max_context_len, want_splits);
+    part = ceil_div(part, kMinPartition) * kMinPartition;
+    if (part < 256)
+        part = 256;
+    if (part > kMaxPartition)
+        part = kMaxPartition;
+    return (int32_t)part;
+}
+
+int32_t nsplit_max_of(const hipdecode_params &p, int32_t part)
+{
+    const int64_t n = ceil_div(p.max_context_len, part);
+    return n < 1 ? 1 : (int32_t)n;
+}
+
+WorkspaceLayout layout_of(const hipdecode_params &p, int32_t nsplit)
+{
+    WorkspaceLayout w;
+    const size_t rows = (size_t)p.num_seqs * (size_t)p.num_q_heads;
+    w.counters = 0;
+    w.part_ml = align256((size_t)p.num_seqs * (size_t)p.num_kv_heads * sizeof(int32_t));
+    if (nsplit <= 1) {
+        w.part_acc = w.part_ml;
+        w.total = w.part_ml;   // a single partition per request needs only the counters
+        return w;
+    }
+    w.part_acc = w.part_ml + align256(rows * (size_t)nsplit * 2 * sizeof(float));
+    w.total = w.part_acc + rows * (size_t)nsplit * kHeadDim * sizeof(float);
+    return w;
+}
+
+hipdecode_status check(const hipdecode_params *pp)
+{
+    if (pp == nullptr)
+        return HIPDECODE_ERR_NULL;
+    const hipdecode_params &p = *pp;
+    if (p.num_seqs < 0 || p.num_q_heads <= 0 || p.num_kv_heads <= 0 || p.num_pages < 0 ||
+        p.max_blocks_per_seq < 0 || p.max_context_len < 0 || p.partition_tokens < 0)
+        return HIPDECODE_ERR_SHAPE;
+    if (p.num_q_heads % p.num_kv_heads != 0)
+        return HIPDECODE_ERR_SHAPE;
+    if (p.head_dim <= 0 || p.page_size <= 0)
+        return HIPDECODE_ERR_SHAPE;
+    if (p.head_dim != kHeadDim || p.page_size != kPageSize)
+        return HIPDECODE_ERR_UNSUPPORTED;
+    const int group = p.num_q_heads / p.num_kv_heads;
+    if (group != 1 && group != 2 && group != 4)
+        return HIPDECODE_ERR_UNSUPPORTED;
+    if (p.out_dtype != HIPDECODE_BF16 && p.out_dtype != HIPDECODE_F32)
+        return HIPDECODE_ERR_UNSUPPORTED;
+    if (!isfinite(p.scale))
+        return HIPDECODE_ERR_SCALE;
+    if ((int64_t)p.max_context_len > (int64_t)p.max_blocks_per_seq * kPageSize)
+        return HIPDECODE_ERR_SHAPE;
+    if (p.num_seqs > 0 && p.max_context_len > 0 && p.num_pages == 0)
+        return HIPDECODE_ERR_SHAPE;
+    if (p.partition_tokens != 0 &&
+        (p.partition_tokens % kMinPartition != 0 || p.partition_tokens > kMaxPartition))
+        return HIPDECODE_ERR_SHAPE;
+    // index arithmetic inside the kernel: rows of q/out and the grid stay in 31 bits
+    const int64_t rows = (int64_t)p.num_seqs * p.num_q_heads;
+    if (rows * kHeadDim > INT32_MAX)
+        return HIPDECODE_ERR_SHAPE;
+    const int64_t grid = (int64_t)p.num_seqs * p.num_kv_heads *
+                         nsplit_max_of(p, plan_partition(p));
+    if (grid > INT32_MAX)
+        return HIPDECODE_ERR_SHAPE;
+    return HIPDECODE_OK;
+}
+
+}  // namespace
+}  // namespace hipdecode
+
+using namespace hipdecode;
+
+HIPDECODE_API int hipdecode_abi_version(void) { return HIPDECODE_ABI_VERSION; }
+
+HIPDECODE_API hipdecode_status hipdecode_check_params(const hipdecode_params *params)
+{
+    return check(params);
+}
+
+HIPDECODE_API int32_t hipdecode_partition_tokens(const hipdecode_params *params)
+{
+    if (check(params) != HIPDECODE_OK)
+        return 0;
+    return plan_partition(*params);
+}
+
+HIPDECODE_API size_t hipdecode_workspace_bytes(const hipdecode_params *params)
+{
+    if (check(params) != HIPDECODE_OK)
+        return 0;
+    const int32_t part = plan_partition(*params);
+    return layout_of(*params, nsplit_max_of(*params, part)).total;
+}
+
+HIPDECODE_API hipdecode_status hipdecode_workspace_init(void *workspace, size_t bytes, void *stream)
+{
+    if (bytes == 0)
+        return HIPDECODE_OK;
+    if (workspace == nullptr)
+        return HIPDECODE_ERR_NULL;
+    if (!aligned16(workspace))
+        return HIPDECODE_ERR_ALIGN;
+    return launch_zero_fill(workspace, bytes, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? HIPDECODE_OK
+               : HIPDECODE_ERR_HIP;
+}
+
+HIPDECODE_API hipdecode_status hipdecode_paged_attn(const hipdecode_params *params, const void *q,
+                                                    const void *k_pool, const void *v_pool,
+                                                    const int32_t *block_table,
+                                                    const int32_t *context_lens, void *out,
+                                                    float *lse, void *workspace,
+                                                    size_t workspace_bytes, void *stream)
+{
+    const hipdecode_status st = check(params);
+    if (st != HIPDECODE_OK)
+        return st;
+    const hipdecode_params &p = *params;
+    if (p.num_seqs == 0)
+        return HIPDECODE_OK;
+    if (q == nullptr || out == nullptr || context_lens == nullptr || block_table == nullptr ||
+        workspace == nullptr)
+        return HIPDECODE_ERR_NULL;
+    if (p.max_context_len > 0 && (k_pool == nullptr || v_pool == nullptr))
+        return HIPDECODE_ERR_NULL;
+    if (!aligned16(q) || !aligned16(out) || !aligned16(workspace) ||
+        (k_pool != nullptr && !aligned16(k_pool)) || (v_pool != nullptr && !aligned16(v_pool)) ||
+        (reinterpret_cast<uintptr_t>(lse) & 3u) != 0 ||
+        (reinterpret_cast<uintptr_t>(block_table) & 3u) != 0 ||
+        (reinterpret_cast<uintptr_t>(context_lens) & 3u) != 0)
+        return HIPDECODE_ERR_ALIGN;
+
+    const int32_t part = plan_partition(p);
+    const int32_t nsplit = nsplit_max_of(p, part);
+    const WorkspaceLayout w = layout_of(p, nsplit);
+    if (workspace_bytes < w.total)
+        return HIPDECODE_ERR_WORKSPACE;
+
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    DecodeArgs a;
+    a.q = static_cast<const uint16_t *>(q);
+    a.k_pool = static_cast<const uint16_t *>(k_pool);
+    a.v_pool = static_cast<const uint16_t *>(v_pool);
+    a.block_table = block_table;
+    a.context_lens = context_lens;
+    a.out = out;
+    a.lse = lse;
+    a.counters = reinterpret_cast<int32_t *>(ws + w.counters);
+    a.part_ml = reinterpret_cast<float *>(ws + w.part_ml);
+    a.part_acc = reinterpret_cast<float *>(ws + w.part_acc);
+    a.num_q_heads = p.num_q_heads;
+    a.num_kv_heads = p.num_kv_heads;
+    a.num_pages = p.num_pages;
+    a.max_blocks = p.max_blocks_per_seq;
+    a.max_context_len = p.max_context_len;
+    a.partition_pages = part / kPageSize;
+    a.nsplit_max = nsplit;
+    a.scale_log2 = p.scale * 1.44269504088896340736f;
+
+    const hipError_t e = launch_paged_decode(a, p.num_q_heads / p.num_kv_heads,
+                                             p.out_dtype == HIPDECODE_F32, p.num_seqs,
+                                             static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? HIPDECODE_OK : HIPDECODE_ERR_HIP;
+}
+
+HIPDECODE_API const char *hipdecode_status_string(hipdecode_status status)
+{
+    switch (status) {
+    case HIPDECODE_OK: return "ok";
+    case HIPDECODE_ERR_NULL: return "a required pointer is NULL";
+    case HIPDECODE_ERR_SHAPE: return "inconsistent or out-of-range sizes";
+    case HIPDECODE_ERR_UNSUPPORTED: return "unsupported head_dim, page size, group size or dtype";
+    case HIPDECODE_ERR_ALIGN: return "a buffer is not suitably aligned";
+    case HIPDECODE_ERR_WORKSPACE: return "workspace smaller than hipdecode_workspace_bytes()";
+    case HIPDECODE_ERR_SCALE: return "scale is not finite";
+    case HIPDECODE_ERR_HIP: return "the HIP runtime refused the launch";
+    }
+    return "unknown status";
+}

@@ -1,0 +1,162 @@
+"""Host-side checks of the C ABI: the library loads, exports what the header
+declares, and rejects every bad parameter block.  No GPU call is made."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import paged_kv_decode_gqa_amd as hd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hipdecode.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hipdecode_[a-z_0-9]+)\s*\(", text)))
+
+
+def base(**kw):
+    p = dict(num_seqs=16, num_q_heads=16, num_kv_heads=8, num_pages=28672, max_blocks_per_seq=1792,
+             max_context_len=28672, scale=1 / math.sqrt(128))
+    p.update(kw)
+    return hd.make_params(**p)
+
+
+def test_library_exports_every_declared_function():
+    lib = hd.library()
+    names = declared_functions()
+    assert set(names) == set(hd.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", hd.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (hipdecode_\w+)", out))
+    assert exported == set(names), f"exported {exported ^ set(names)} differ from the header"
+
+
+def test_abi_version():
+    assert hd.hipdecode_abi_version() == 1
+
+
+def test_struct_layout_matches_header():
+    # 10 int32 fields then a float, no padding
+    assert ctypes.sizeof(hd.hipdecode_params) == 44
+
+
+def test_status_strings():
+    for s in range(8):
+        assert hd.hipdecode_status_string(s)
+    assert hd.hipdecode_status_string(99) == "unknown status"
+
+
+GOOD = [
+    {},
+    dict(num_seqs=0),
+    dict(max_context_len=0),
+    dict(num_q_heads=8, num_kv_heads=8),
+    dict(num_q_heads=16, num_kv_heads=4),
+    dict(partition_tokens=64),
+    dict(partition_tokens=4096),
+    dict(out_dtype=hd.HIPDECODE_F32),
+    dict(scale=-0.5),
+    dict(scale=0.0),
+]
+
+BAD = [
+    (dict(num_seqs=-1), hd.HIPDECODE_ERR_SHAPE),
+    (dict(num_q_heads=0), hd.HIPDECODE_ERR_SHAPE),
+    (dict(num_kv_heads=0), hd.HIPDECODE_ERR_SHAPE),
+    (dict(num_q_heads=12, num_kv_heads=8), hd.HIPDECODE_ERR_SHAPE),
+    (dict(num_q_heads=16, num_kv_heads=2), hd.HIPDECODE_ERR_UNSUPPORTED),
+    (dict(head_dim=64), hd.HIPDECODE_ERR_UNSUPPORTED),
+    (dict(head_dim=0), hd.HIPDECODE_ERR_SHAPE),
+    (dict(page_size=32), hd.HIPDECODE_ERR_UNSUPPORTED),
+    (dict(out_dtype=7), hd.HIPDECODE_ERR_UNSUPPORTED),
+    (dict(scale=float("nan")), hd.HIPDECODE_ERR_SCALE),
+    (dict(scale=float("inf")), hd.HIPDECODE_ERR_SCALE),
+    (dict(max_context_len=1792 * 16 + 1), hd.HIPDECODE_ERR_SHAPE),
+    (dict(max_context_len=-5), hd.HIPDECODE_ERR_SHAPE),
+    (dict(num_pages=0), hd.HIPDECODE_ERR_SHAPE),
+    (dict(num_pages=-1), hd.HIPDECODE_ERR_SHAPE),
+    (dict(partition_tokens=100), hd.HIPDECODE_ERR_SHAPE),
+    (dict(partition_tokens=8192), hd.HIPDECODE_ERR_SHAPE),
+    (dict(partition_tokens=-64), hd.HIPDECODE_ERR_SHAPE),
+    (dict(max_blocks_per_seq=-1, max_context_len=0), hd.HIPDECODE_ERR_SHAPE),
+]
+
+
+@pytest.mark.parametrize("kw", GOOD, ids=lambda k: ",".join(f"{a}={b}" for a, b in k.items()) or "base")
+def test_check_params_accepts(kw):
+    p = base(**kw)
+    assert hd.hipdecode_check_params(p) == hd.HIPDECODE_OK
+    assert hd.hipdecode_partition_tokens(p) % 64 == 0
+
+
+@pytest.mark.parametrize("kw,status", BAD, ids=lambda x: str(x))
+def test_check_params_rejects(kw, status):
+    p = base(**kw)
+    assert hd.hipdecode_check_params(p) == status
+    assert hd.hipdecode_workspace_bytes(p) == 0
+    assert hd.hipdecode_partition_tokens(p) == 0
+
+
+def test_null_params():
+    assert hd.hipdecode_check_params(None) == hd.HIPDECODE_ERR_NULL
+
+
+def test_call_rejects_before_any_launch():
+    lib = hd.library()
+    p = base()
+    ws = hd.hipdecode_workspace_bytes(p)
+    fake = ctypes.c_void_p(1 << 20)          # never dereferenced: rejected on the host
+    odd = ctypes.c_void_p((1 << 20) + 2)
+    args = [fake] * 5 + [fake, fake, fake]
+    # NULL q
+    assert lib.hipdecode_paged_attn(ctypes.byref(p), None, *args[1:5], fake, fake, fake, ws, None) == hd.HIPDECODE_ERR_NULL
+    # misaligned q
+    assert lib.hipdecode_paged_attn(ctypes.byref(p), odd, *args[1:5], fake, fake, fake, ws, None) == hd.HIPDECODE_ERR_ALIGN
+    # workspace too small
+    assert lib.hipdecode_paged_attn(ctypes.byref(p), *args[:5], fake, fake, fake, ws - 1, None) == hd.HIPDECODE_ERR_WORKSPACE
+    # bad params are reported before pointers are looked at
+    bad = base(head_dim=64)
+    assert lib.hipdecode_paged_attn(ctypes.byref(bad), None, None, None, None, None, None, None, None, 0, None) \
+        == hd.HIPDECODE_ERR_UNSUPPORTED
+    # B == 0 is a no-op that needs no pointers
+    zero = base(num_seqs=0)
+    assert lib.hipdecode_paged_attn(ctypes.byref(zero), None, None, None, None, None, None, None, None, 0, None) \
+        == hd.HIPDECODE_OK
+
+
+def test_planner_and_workspace_sizes():
+    # long meetings at B=16: 128 (request, KV head) pairs
+    p = base()
+    part = hd.hipdecode_partition_tokens(p)
+    nsplit = -(-28672 // part)
+    assert 256 <= part <= 4096 and part % 64 == 0
+    assert 16 * 8 * nsplit >= 1024
+    rows = 16 * 16
+    expect = 512 + ((rows * nsplit * 8 + 255) // 256) * 256 + rows * nsplit * 128 * 4
+    assert hd.hipdecode_workspace_bytes(p) == expect
+    # B=1 at 28672: splits so that 8 * nsplit >= 1024 workgroups
+    p1 = base(num_seqs=1, num_pages=2048)
+    part1 = hd.hipdecode_partition_tokens(p1)
+    assert 8 * (-(-28672 // part1)) >= 1024 * 0.85
+    # one partition per request: only the counters
+    p2 = base(num_seqs=1, max_context_len=200, num_pages=64, max_blocks_per_seq=13)
+    assert hd.hipdecode_workspace_bytes(p2) == 256
+    # explicit partition is honoured
+    assert hd.hipdecode_partition_tokens(base(partition_tokens=128)) == 128
+
+
+def test_product_path_does_not_reach_the_oracle():
+    """The binding and the library never name the oracle."""
+    pkg = os.path.dirname(hd.__file__)
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), f"{f} mentions the oracle"

@@ -1,0 +1,187 @@
+"""HIP path against the fp64 oracle, element by element, through the C ABI.
+
+Full-size workloads run at the planner's default partition (the launch
+configuration the benchmark times) and are compared on every output.  The edge
+matrix covers empty and one-token contexts, page and partition boundaries,
+NaN-poisoned unused slots, split-count invariance, page relabelling,
+duplicates, CFG pairs, aliased pages, the three group sizes, fp32 output,
+B = 0, workspace reuse and HIP-graph replay.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_decode_gqa_amd as hd
+from tests.gpu_util import DeviceCase, compare, log, run_hip
+from workloads import make_case, make_config
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    hd.library()   # fail loudly if the HIP library is missing
+
+
+def _check(case, what, **kw):
+    log(f"[parity] {what}: B={case.B} max_ctx={case.max_context_len} pages={case.num_pages} {kw}")
+    dc = DeviceCase(case)
+    out, lse = run_hip(dc, **kw)
+    ref_out, ref_lse = oracle.run_case(case)
+    e, le = compare(out, lse, ref_out, ref_lse, what=what)
+    log(f"[parity] {what}: max|dout|={e:.3e} max rel dlse={le:.3e}")
+    return out, lse
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5", "c3b"])
+def test_workload_parity(name):
+    case = make_config(name)
+    _check(case, name)
+
+
+@pytest.mark.parametrize("partition", [0, 64, 256, 4096])
+def test_edge_lengths_poisoned(partition):
+    ctx = [0, 1, 15, 16, 17, 63, 64, 65, 4095, 4096, 4097, 0]
+    case = make_case(ctx, seed=11, poison=True, pool_pages=sum((n + 15) // 16 for n in ctx) + 7)
+    _check(case, f"edge lengths, partition {partition}", partition_tokens=partition)
+
+
+def test_split_count_invariance():
+    case = make_case([200, 1000, 3333, 8191, 17], seed=12, poison=True)
+    dc = DeviceCase(case)
+    ref_out, ref_lse = oracle.run_case(case)
+    outs = []
+    for part in (64, 128, 256, 512, 1024, 2048, 4096, 0):
+        log(f"[parity] split invariance, partition {part}")
+        out, lse = run_hip(dc, partition_tokens=part)
+        compare(out, lse, ref_out, ref_lse, what=f"partition {part}")
+        outs.append(out.float().cpu().numpy())
+    spread = max(float(np.abs(o - outs[0]).max()) for o in outs)
+    assert spread <= 2e-2
+
+
+def test_page_relabel_bit_identical():
+    case = make_case([700, 33, 2048], seed=13, pool_pages=300)
+    dc = DeviceCase(case)
+    out1, lse1 = run_hip(dc)
+    rng = np.random.default_rng(99)
+    perm = rng.permutation(case.num_pages)
+    k2 = np.empty_like(case.k_pool)
+    v2 = np.empty_like(case.v_pool)
+    k2[perm] = case.k_pool
+    v2[perm] = case.v_pool
+    t2 = np.where(case.block_table >= 0, perm[np.maximum(case.block_table, 0)], -1).astype(np.int32)
+    case2 = make_case([700, 33, 2048], seed=13, pool_pages=300)
+    case2.k_pool, case2.v_pool, case2.block_table = k2, v2, t2
+    log("[parity] page relabel")
+    out2, lse2 = run_hip(DeviceCase(case2))
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+
+
+def test_duplicates_and_cfg_pairs():
+    case = make_case([1500, 1500, 900, 900], seed=14, shared_q_pairs=True)
+    # requests 2 and 3: same q (pair) and, made here, the same KV pages
+    case.block_table[3] = case.block_table[2]
+    out, lse = _check(case, "duplicates and CFG pairs")
+    assert torch.equal(out[2], out[3]) and torch.equal(lse[2], lse[3])
+    assert not torch.equal(out[0], out[1])
+
+
+def test_shared_prefix_pages():
+    case = make_case([600, 900, 300, 64], seed=15, shared_prefix_pages=10, poison=True)
+    _check(case, "aliased prefix pages")
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 4), (32, 16)])
+def test_group_sizes(hq, hkv):
+    case = make_case([777, 3000, 1], seed=16, Hq=hq, Hkv=hkv)
+    _check(case, f"Hq={hq} Hkv={hkv}")
+
+
+def test_fp32_output_long():
+    case = make_case([20000, 5], seed=17, out_dtype="f32")
+    _check(case, "fp32 out")
+
+
+def test_batch_zero_is_noop():
+    q = torch.zeros((0, 16, 128), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((4, 16, 8, 128), dtype=torch.bfloat16, device="cuda")
+    table = torch.zeros((0, 1), dtype=torch.int32, device="cuda")
+    ctx = torch.zeros((0,), dtype=torch.int32, device="cuda")
+    out, lse = hd.paged_attn(q, k, k, table, ctx, 0.1, max_context_len=0)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 16, 128) and lse.shape == (0, 16)
+
+
+def test_workspace_reuse_leaves_counters_zero():
+    case = make_case([5000, 12000, 64], seed=18)
+    dc = DeviceCase(case)
+    p = hd.make_params(num_seqs=case.B, num_q_heads=16, num_kv_heads=8, num_pages=case.num_pages,
+                       max_blocks_per_seq=case.max_blocks, max_context_len=case.max_context_len,
+                       scale=case.scale)
+    nbytes = hd.hipdecode_workspace_bytes(p)
+    ws = torch.full((nbytes // 4 + 4,), 12345, dtype=torch.int32, device="cuda")
+    hd.hipdecode_workspace_init(ws)
+    ref_out, ref_lse = oracle.run_case(case)
+    first = None
+    for it in range(3):
+        log(f"[parity] workspace reuse, call {it}")
+        out, lse = run_hip(dc, workspace=ws)
+        compare(out, lse, ref_out, ref_lse, what=f"reuse {it}")
+        assert int(ws[: case.B * 8].abs().sum().item()) == 0, "tickets must return to zero"
+        if first is None:
+            first = (out.clone(), lse.clone())
+        else:
+            assert torch.equal(out, first[0]) and torch.equal(lse, first[1]), "not deterministic"
+
+
+def test_context_above_bound_is_clamped():
+    # context_lens past max_context_len: the kernel uses the first max_context_len tokens
+    case = make_case([3000, 1200], seed=19)
+    dc = DeviceCase(case)
+    log("[parity] clamp to max_context_len")
+    out, lse = run_hip(dc, max_context_len=2000)
+    clamped = make_case([3000, 1200], seed=19)
+    clamped.context_lens = np.minimum(clamped.context_lens, 2000).astype(np.int32)
+    ref_out, ref_lse = oracle.run_case(clamped)
+    compare(out, lse, ref_out, ref_lse, what="clamped")
+
+
+def test_graph_capture_replay():
+    # every request owns pages for 9000 tokens; replays change only context_lens
+    case = make_case([9000, 9000, 9000, 9000], seed=20, pool_pages=2300)
+    dc = DeviceCase(case)
+    p = hd.make_params(num_seqs=case.B, num_q_heads=16, num_kv_heads=8, num_pages=case.num_pages,
+                       max_blocks_per_seq=case.max_blocks, max_context_len=9000, scale=case.scale)
+    ws = torch.zeros(hd.hipdecode_workspace_bytes(p) // 4 + 4, dtype=torch.int32, device="cuda")
+    out = torch.empty((case.B, 16, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((case.B, 16), dtype=torch.float32, device="cuda")
+    ctx_dev = dc.ctx.clone()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):   # warm-up outside the graph
+        hd.hipdecode_paged_attn(p, dc.q, dc.k, dc.v, dc.table, ctx_dev, out, lse, ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        hd.hipdecode_paged_attn(p, dc.q, dc.k, dc.v, dc.table, ctx_dev, out, lse, ws)
+    torch.cuda.synchronize()
+    # replay with new context lengths written into the captured buffer
+    for it, lens in enumerate([[4000, 9000, 100, 0], [3999, 17, 8191, 1], [0, 9000, 4096, 2500]]):
+        log(f"[parity] graph replay {it}: {lens}")
+        ctx_dev.copy_(torch.tensor(lens, dtype=torch.int32))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref_case = make_case([9000, 9000, 9000, 9000], seed=20, pool_pages=2300)
+        ref_case.context_lens = np.array(lens, dtype=np.int32)
+        ref_out, ref_lse = oracle.run_case(ref_case)
+        compare(out, lse, ref_out, ref_lse, what=f"graph replay {it}")
+        eager_out, eager_lse = hd.paged_attn(dc.q, dc.k, dc.v, dc.table, ctx_dev, case.scale,
+                                             max_context_len=9000)
+        torch.cuda.synchronize()
+        assert torch.equal(eager_out, out) and torch.equal(eager_lse, lse), "replay differs from eager"
