@@ -154,6 +154,30 @@ def hipdecode_paged_attn(params: hipdecode_params, q, k_pool, v_pool, block_tabl
         raise HipDecodeError(st, "hipdecode_paged_attn")
 
 
+class PreparedCall:
+    """The marshalled argument list of one ``hipdecode_paged_attn`` call.
+
+    Built once from tensors that stay alive (and in place) across calls, then
+    invoked many times; each invocation enqueues the kernel on the current
+    stream (or ``stream``) without re-marshalling the tensors."""
+
+    def __init__(self, params, q, k_pool, v_pool, block_table, context_lens, out, lse, workspace):
+        self._keep = (params, q, k_pool, v_pool, block_table, context_lens, out, lse, workspace)
+        for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool), ("block_table", block_table),
+                        ("context_lens", context_lens), ("out", out), ("lse", lse), ("workspace", workspace)):
+            if t is not None and not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+        ws_bytes = workspace.numel() * workspace.element_size()
+        self._args = (ctypes.byref(params), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+                      _ptr(context_lens), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes)
+        self._fn = library().hipdecode_paged_attn
+
+    def __call__(self, stream=None) -> None:
+        st = self._fn(*self._args, _stream_handle(stream))
+        if st != HIPDECODE_OK:
+            raise HipDecodeError(st, "hipdecode_paged_attn")
+
+
 def paged_attn(q, k_pool, v_pool, block_table, context_lens, scale, *, max_context_len,
                out_dtype=None, partition_tokens=0, out=None, lse=None, workspace=None):
     """Allocate outputs (and a zeroed workspace) as needed and run one call.

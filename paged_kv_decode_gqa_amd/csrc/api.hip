@@ -30,9 +30,13 @@ int32_t plan_partition(const hipdecode_params &p)
         return 256;
     const int64_t want_splits = ceil_div(kTargetWorkgroups, pairs);
     int64_t part = ceil_div(p.max_context_len, want_splits);
-    part = ceil_div(part, kMinPartition) * kMinPartition;
     if (part < 256)
         part = 256;
+    // the final merge weighs at most kMaxMergeSplits partials per request
+    const int64_t floor_part = ceil_div(p.max_context_len, kMaxMergeSplits);
+    if (part < floor_part)
+        part = floor_part;
+    part = ceil_div(part, kMinPartition) * kMinPartition;
     if (part > kMaxPartition)
         part = kMaxPartition;
     return (int32_t)part;
@@ -92,8 +96,10 @@ hipdecode_status check(const hipdecode_params *pp)
     const int64_t rows = (int64_t)p.num_seqs * p.num_q_heads;
     if (rows * kHeadDim > INT32_MAX)
         return HIPDECODE_ERR_SHAPE;
-    const int64_t grid = (int64_t)p.num_seqs * p.num_kv_heads *
-                         nsplit_max_of(p, plan_partition(p));
+    const int32_t nsplit = nsplit_max_of(p, plan_partition(p));
+    if (nsplit > kMaxMergeSplits)
+        return HIPDECODE_ERR_SHAPE;
+    const int64_t grid = (int64_t)p.num_seqs * p.num_kv_heads * nsplit;
     if (grid > INT32_MAX)
         return HIPDECODE_ERR_SHAPE;
     return HIPDECODE_OK;

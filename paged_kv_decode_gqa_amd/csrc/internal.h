@@ -13,6 +13,7 @@ constexpr int kWaves = 4;       // wavefronts per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMinPartition = 64;     // split-K partitions are multiples of this many tokens
 constexpr int kMaxPartition = 4096;   // at most 256 pages: 64 per wavefront, one table entry per lane
+constexpr int kMaxMergeSplits = 1024; // partitions per request the final merge can weigh in LDS
 
 // Byte offsets inside the caller's workspace.
 struct WorkspaceLayout {

@@ -1,187 +1,93 @@
-// paged_decode.hip -- gfx950 kernels for one decode step of paged GQA attention.
+// paged_decode.hip -- gfx950 kernel for one decode step of paged GQA attention,
+// split by (request, KV head, partition of the context).
 //
 // One workgroup owns one (request b, KV head g, split-K partition) triple and
 // serves all G query heads that read KV head g (the 16-query/8-KV grouping of
 // the audio.cpp "Decoder And Prompt" section), so every K/V byte of the cache
 // is fetched from HBM exactly once per call.  The work is bound by HBM
 // bandwidth: per cached token and query head it is 2x128 multiply-adds against
-// 256 bytes of K and 256 bytes of V shared by the G heads.
+// 256 bytes of K and 256 bytes of V shared by the G heads.  Page-level work is
+// in page_fold.h.
 //
-// Wavefront layout.  A page holds 16 tokens of one KV head, each a 256-byte
-// row, with rows num_kv_heads*256 bytes apart.  The 64 lanes of a wavefront
-// form 8 octets; octet o owns tokens o and o+8 of the page and lane s of the
-// octet owns dims [8s, 8s+8) and [64+8s, 64+8s+8) of those rows.  Each of the
-// four 16-byte loads per lane per tensor (token pair x dim half) therefore
-// moves eight whole 128-byte lines.  q.k uses v_dot2c_f32_bf16 on packed bf16
-// pairs and is summed across the octet with three DPP steps; p.v runs in fp32
-// FMAs so the softmax weights are never rounded to bf16.
-//
-// Online softmax.  Each octet is an independent softmax stream with its own
-// running max m and sum l (base-2 units: scores are pre-multiplied by
-// scale*log2(e)), so no cross-octet traffic happens inside the page loop.  At
-// the end the 32 streams of the workgroup are merged through LDS with the
-// usual (m, l, acc) rule
+// The four wavefronts take the partition's pages round-robin, each with one
+// page in flight while it folds the previous one; their 16 row-group streams
+// are merged through LDS with the rule
 //     M = max m_i,  L = sum l_i 2^(m_i - M),  A = sum acc_i 2^(m_i - M).
-// A request whose context spans several partitions writes its partial
+// A request whose context spans several partitions writes each partition's
 // (M, L, A) to the workspace; the last workgroup of a (request, KV head) to
-// arrive, found with an atomic ticket, merges the partials with the same rule,
-// writes out = A/L and lse = ln2 * (M + log2 L), and resets the ticket, so a
-// call is a single kernel launch.
-#include "internal.h"
-
-#include <math.h>
+// arrive, found with an atomic ticket, merges the partials with the same rule
+// (all threads loading in parallel), writes out = A/L and
+// lse = ln2 * (M + log2 L), and resets the ticket, so a call is one launch.
+// The partials travel through device-scope atomics (see page_fold.h), not
+// through fences, so no workgroup flushes or invalidates the L2.
+#include "page_fold.h"
 
 namespace hipdecode {
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+using namespace dev;
 
-constexpr int kStreams = kWaves * 8;   // softmax streams per workgroup (octets)
+constexpr int kRowStreams = kWaves * 4;
 
-__device__ __forceinline__ u32x4 load16(const uint16_t *p)
+__device__ __forceinline__ float wave_max(float v)
 {
-    return *reinterpret_cast<const u32x4 *>(p);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        v = fmaxf(v, __shfl_xor(v, o));
+    return v;
 }
 
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c)
+__device__ __forceinline__ float wave_sum(float v)
 {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
-                                           __builtin_bit_cast(bf16x2, b), c, false);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        v += __shfl_xor(v, o);
+    return v;
 }
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float x)
+// Block-wide reductions over kThreads; `red` is kWaves floats of LDS.
+__device__ __forceinline__ float block_max(float v, float *red)
 {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-        0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+    v = wave_max(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0)
+        red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float r = red[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w)
+        r = fmaxf(r, red[w]);
+    return r;
 }
 
-// Sum over the 8 lanes of an aligned octet; every lane of the octet gets it.
-__device__ __forceinline__ float octet_sum(float x)
+__device__ __forceinline__ float block_sum(float v, float *red)
 {
-    x += dpp_f32<0xB1>(x);    // quad_perm [1,0,3,2]: lane ^ 1
-    x += dpp_f32<0x4E>(x);    // quad_perm [2,3,0,1]: lane ^ 2
-    x += dpp_f32<0x141>(x);   // row_half_mirror: lane i <- lane 7-i, i.e. the other quad
-    return x;
-}
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// dim of acc index i (0..15) for lane s of an octet
-__device__ __forceinline__ int acc_dim(int s, int i) { return s * 8 + (i >> 3) * 64 + (i & 7); }
-
-template <bool F32>
-__device__ __forceinline__ void store_out(void *out, size_t idx, float v)
-{
-    if constexpr (F32)
-        static_cast<float *>(out)[idx] = v;
-    else
-        static_cast<__bf16 *>(out)[idx] = static_cast<__bf16>(v);   // round to nearest even
-}
-
-struct PageRegs {
-    u32x4 k[2][2];   // [token o / o+8][dim half]
-    u32x4 v[2][2];
-};
-
-__device__ __forceinline__ void load_page(PageRegs &r, const uint16_t *kb, const uint16_t *vb,
-                                          size_t page_off, size_t tok8)
-{
+    v = wave_sum(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0)
+        red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float r = red[0];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            r.k[t][j] = load16(kb + page_off + t * tok8 + j * 64);
-            r.v[t][j] = load16(vb + page_off + t * tok8 + j * 64);
-        }
-}
-
-template <int G>
-struct Stream {
-    float m[G];
-    float l[G];
-    float acc[G][16];
-};
-
-// Fold one page into the octet's softmax stream.  MASK: tokens at or past ctx
-// (only on a request's last page) get weight 0 and their K/V are never used
-// arithmetically, so garbage or NaN in unused slots cannot leak in.
-template <int G, bool MASK>
-__device__ __forceinline__ void consume(Stream<G> &st, const PageRegs &r, const u32x4 (&qv)[G][2],
-                                        float scale_log2, int tok_first, int ctx)
-{
-    float s[G][2];
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            float d = 0.f;
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int w = 0; w < 4; ++w)
-                    d = dot2_bf16(r.k[t][j][w], qv[h][j][w], d);
-            s[h][t] = octet_sum(d) * scale_log2;
-        }
-
-    bool valid[2] = {true, true};
-    if constexpr (MASK) {
-        valid[0] = tok_first < ctx;
-        valid[1] = tok_first + 8 < ctx;
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-                s[h][t] = valid[t] ? s[h][t] : -INFINITY;
-    }
-
-    float p[G][2];
-    float alpha[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        const float m_new = fmaxf(st.m[h], fmaxf(s[h][0], s[h][1]));
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        alpha[h] = exp2_fast(st.m[h] - m_use);
-        p[h][0] = exp2_fast(s[h][0] - m_use);
-        p[h][1] = exp2_fast(s[h][1] - m_use);
-        st.l[h] = st.l[h] * alpha[h] + p[h][0] + p[h][1];
-        st.m[h] = m_new;
-    }
-
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const int i = j * 8 + w * 2;
-            float v0l = bf16_lo(r.v[0][j][w]), v0h = bf16_hi(r.v[0][j][w]);
-            float v1l = bf16_lo(r.v[1][j][w]), v1h = bf16_hi(r.v[1][j][w]);
-            if constexpr (MASK) {
-                v0l = valid[0] ? v0l : 0.f;
-                v0h = valid[0] ? v0h : 0.f;
-                v1l = valid[1] ? v1l : 0.f;
-                v1h = valid[1] ? v1h : 0.f;
-            }
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                st.acc[h][i] = fmaf(p[h][1], v1l, fmaf(p[h][0], v0l, st.acc[h][i] * alpha[h]));
-                st.acc[h][i + 1] = fmaf(p[h][1], v1h, fmaf(p[h][0], v0h, st.acc[h][i + 1] * alpha[h]));
-            }
-        }
+    for (int w = 1; w < kWaves; ++w)
+        r += red[w];
+    return r;
 }
 
 template <int G, bool OUT_F32>
-__global__ __launch_bounds__(kThreads) void paged_decode_kernel(DecodeArgs a)
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void paged_decode_kernel(DecodeArgs a)
 {
-    __shared__ float s_acc[kStreams][G][kHeadDim];
-    __shared__ float s_m[kStreams][G];
-    __shared__ float s_l[kStreams][G];
+    __shared__ f32x4 s_acc4[kRowStreams * G * kHeadDim / 4];
+    __shared__ float s_m[kRowStreams][G];
+    __shared__ float s_l[kRowStreams][G];
+    __shared__ float s_w[G][kMaxMergeSplits];
+    __shared__ float s_red[kWaves];
     __shared__ int s_last;
+    float *s_acc = reinterpret_cast<float *>(s_acc4);   // [kRowStreams][G][kHeadDim]
 
     // Workgroup -> (b, split, g) with the KV head fastest: consecutive
-    // workgroups read the same pages' neighbouring head rows.
+    // workgroups read neighbouring head rows of the same pages.
     const int Hkv = a.num_kv_heads;
     const int g = blockIdx.x % Hkv;
     const int rest = blockIdx.x / Hkv;
@@ -209,38 +115,31 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(DecodeArgs a)
 
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int oct = lane >> 3;
-    const int sub = lane & 7;
+    const int row = lane >> 4;
+    const int sub = lane & 15;
 
-    u32x4 qv[G][2];
+    u32x4 qv[G];
 #pragma unroll
     for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-            qv[h][j] = load16(a.q + (row0 + h) * kHeadDim + sub * 8 + j * 64);
+        qv[h] = load16(a.q + (row0 + h) * kHeadDim + sub * 8);
 
     Stream<G> st;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        st.m[h] = -INFINITY;
-        st.l[h] = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-            st.acc[h][i] = 0.f;
-    }
+    st.init();
 
-    const size_t tok_stride = (size_t)Hkv * kHeadDim;   // elements between slots of a page
-    const size_t page_stride = (size_t)kPageSize * tok_stride;
-    const size_t lane_off = (size_t)g * kHeadDim + (size_t)oct * tok_stride + (size_t)sub * 8;
-    const uint16_t *kb = a.k_pool + lane_off;
-    const uint16_t *vb = a.v_pool + lane_off;
-    const size_t tok8 = 8 * tok_stride;
+    const uint32_t tok_bytes = (uint32_t)Hkv * kHeadDim * 2;   // bytes between slots of a page
+    const size_t page_elems = (size_t)kPageSize * Hkv * kHeadDim;
+    const uint32_t lane_off = (uint32_t)g * kHeadDim * 2 + (uint32_t)row * tok_bytes + (uint32_t)sub * 16;
+    const uint32_t tok4 = 4 * tok_bytes;
 
-    // Pages of this partition, dealt to the wavefronts round-robin; lane i of
-    // a wavefront holds the block-table entry of its i-th page.
+    // Full pages of this partition, dealt to the wavefronts round-robin; lane
+    // i of a wavefront holds the block-table entry of its i-th page.  A
+    // request's last page may be partly filled: it is folded separately,
+    // with masking, after the loop.
     const int p_begin = split * a.partition_pages;
     const int p_end = min(p_begin + a.partition_pages, n_pages);
-    const int span = p_end - p_begin;
+    const bool tail_partial = (p_end == n_pages) && (ctx % kPageSize != 0);
+    const int full_end = tail_partial ? p_end - 1 : p_end;
+    const int span = full_end - p_begin;
     const int npw = span > wave ? (span - wave + kWaves - 1) / kWaves : 0;
     const int32_t *trow = a.block_table + (size_t)b * a.max_blocks;
     const int my_entry = lane < npw ? trow[p_begin + wave + kWaves * lane] : -1;
@@ -250,17 +149,13 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(DecodeArgs a)
     auto issue = [&](PageRegs &r, int i) {
         const int phys = __builtin_amdgcn_readlane(my_entry, i);
         if ((unsigned)phys < num_pages)
-            load_page(r, kb, vb, (size_t)phys * page_stride, tok8);
+            load_page(r, a.k_pool + (size_t)phys * page_elems, a.v_pool + (size_t)phys * page_elems,
+                      lane_off, tok4);
     };
     auto fold = [&](const PageRegs &r, int i) {
         const int phys = __builtin_amdgcn_readlane(my_entry, i);
-        if ((unsigned)phys >= num_pages)
-            return;   // outside the pool: skipped, never read
-        const int pg = p_begin + wave + kWaves * i;
-        if ((pg + 1) * kPageSize <= ctx)
-            consume<G, false>(st, r, qv, a.scale_log2, 0, 0);
-        else
-            consume<G, true>(st, r, qv, a.scale_log2, pg * kPageSize + oct, ctx);
+        if ((unsigned)phys < num_pages)   // a page outside the pool is skipped, never read
+            fold_page<G, false>(st, r, qv, a.scale_log2, 0, 0);
     };
 
     if (npw > 0)
@@ -275,14 +170,22 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(DecodeArgs a)
             issue(ra, i + 2);
         fold(rb, i + 1);
     }
+    if (tail_partial && wave == kWaves - 1) {
+        const int phys = trow[full_end];
+        if ((unsigned)phys < num_pages) {
+            load_page(ra, a.k_pool + (size_t)phys * page_elems, a.v_pool + (size_t)phys * page_elems,
+                      lane_off, tok4);
+            fold_page<G, true>(st, ra, qv, a.scale_log2, full_end * kPageSize + row, ctx);
+        }
+    }
 
-    // ---- merge the workgroup's 32 streams through LDS ----
-    const int sid = wave * 8 + oct;
+    // ---- merge the workgroup's 16 row-group streams through LDS ----
+    const int sid = wave * 4 + row;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-            s_acc[sid][h][acc_dim(sub, i)] = st.acc[h][i];
+        f32x4 *dst = s_acc4 + ((sid * G + h) * kHeadDim + sub * 8) / 4;
+        dst[0] = f32x4{st.acc[h][0], st.acc[h][1], st.acc[h][2], st.acc[h][3]};
+        dst[1] = f32x4{st.acc[h][4], st.acc[h][5], st.acc[h][6], st.acc[h][7]};
         if (sub == 0) {
             s_m[sid][h] = st.m[h];
             s_l[sid][h] = st.l[h];
@@ -295,25 +198,27 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(DecodeArgs a)
         const int h = idx / kHeadDim;
         const int d = idx % kHeadDim;
         float M = -INFINITY;
-        for (int s = 0; s < kStreams; ++s)
+#pragma unroll
+        for (int s = 0; s < kRowStreams; ++s)
             M = fmaxf(M, s_m[s][h]);
         const float M_use = (M == -INFINITY) ? 0.f : M;
         float L = 0.f, A = 0.f;
-        for (int s = 0; s < kStreams; ++s) {
-            const float w = exp2_fast(s_m[s][h] - M_use);
+#pragma unroll
+        for (int s = 0; s < kRowStreams; ++s) {
+            const float w = merge_weight(s_m[s][h], M_use);
             L = fmaf(s_l[s][h], w, L);
-            A = fmaf(s_acc[s][h][d], w, A);
+            A = fmaf(s_acc[(s * G + h) * kHeadDim + d], w, A);
         }
         if (single) {
             store_out<OUT_F32>(a.out, (row0 + h) * kHeadDim + d, A / L);
             if (d == 0 && a.lse != nullptr)
-                a.lse[row0 + h] = (M + log2f(L)) * 0.69314718055994530942f;
+                a.lse[row0 + h] = (M + log2f(L)) * kLn2;
         } else {
             const size_t pi = (row0 + h) * (size_t)a.nsplit_max + split;
-            a.part_acc[pi * kHeadDim + d] = A;
+            coherent_store(a.part_acc + pi * kHeadDim + d, A);
             if (d == 0) {
-                a.part_ml[pi * 2 + 0] = M;
-                a.part_ml[pi * 2 + 1] = L;
+                coherent_store(a.part_ml + pi * 2 + 0, M);
+                coherent_store(a.part_ml + pi * 2 + 1, L);
             }
         }
     }
@@ -321,43 +226,74 @@ __global__ __launch_bounds__(kThreads) void paged_decode_kernel(DecodeArgs a)
         return;
 
     // ---- the last partition of (b, g) to finish merges all partials ----
-    __threadfence();
+    // every wavefront's partial stores have completed before the ticket moves
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     int32_t *ticket = a.counters + (size_t)b * Hkv + g;
     if (tid == 0)
-        s_last = (atomicAdd(ticket, 1) == nsplit_b - 1);
+        s_last = (__hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                  nsplit_b - 1);
     __syncthreads();
     if (!s_last)
         return;
-    __threadfence();
 
-    for (int idx = tid; idx < G * kHeadDim; idx += kThreads) {
-        const int h = idx / kHeadDim;
-        const int d = idx % kHeadDim;
-        const size_t base = (row0 + h) * (size_t)a.nsplit_max;
-        float M = -INFINITY;
-        for (int i = 0; i < nsplit_b; ++i)
-            M = fmaxf(M, __hip_atomic_load(a.part_ml + (base + i) * 2, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT));
-        const float M_use = (M == -INFINITY) ? 0.f : M;
-        float L = 0.f, A = 0.f;
-        for (int i = 0; i < nsplit_b; ++i) {
-            const float mi = __hip_atomic_load(a.part_ml + (base + i) * 2, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-            const float li = __hip_atomic_load(a.part_ml + (base + i) * 2 + 1, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-            const float ai = __hip_atomic_load(a.part_acc + (base + i) * kHeadDim + d, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-            const float w = exp2_fast(mi - M_use);
-            L = fmaf(li, w, L);
-            A = fmaf(ai, w, A);
+    const size_t nsm = (size_t)a.nsplit_max;
+    float Mh[G], Lh[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        const float *ml = a.part_ml + (row0 + h) * nsm * 2;
+        float mx = -INFINITY;
+        for (int i = tid; i < nsplit_b; i += kThreads)
+            mx = fmaxf(mx, coherent_load(ml + 2 * i));
+        Mh[h] = block_max(mx, s_red);
+        const float M_use = (Mh[h] == -INFINITY) ? 0.f : Mh[h];
+        float ls = 0.f;
+        for (int i = tid; i < nsplit_b; i += kThreads) {
+            const float w = merge_weight(coherent_load(ml + 2 * i), M_use);
+            s_w[h][i] = w;
+            ls = fmaf(coherent_load(ml + 2 * i + 1), w, ls);
         }
-        store_out<OUT_F32>(a.out, (row0 + h) * kHeadDim + d, A / L);
-        if (d == 0 && a.lse != nullptr)
-            a.lse[row0 + h] = (M + log2f(L)) * 0.69314718055994530942f;
+        Lh[h] = block_sum(ls, s_red);
+    }
+    __syncthreads();
+
+    // every thread owns 4 dims of one head and a 1/kSets share of the partials
+    constexpr int kChunks = G * kHeadDim / 4;
+    constexpr int kSets = kThreads / kChunks;
+    const int chunk = tid % kChunks;
+    const int set = tid / kChunks;
+    const int h = chunk / (kHeadDim / 4);
+    const int c = chunk % (kHeadDim / 4);
+    const float *acc_h = a.part_acc + (row0 + h) * nsm * kHeadDim + 4 * c;
+    f32x4 A = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int i = set; i < nsplit_b; i += kSets)
+        A += s_w[h][i] * coherent_load4(acc_h + (size_t)i * kHeadDim);
+    s_acc4[set * kChunks + chunk] = A;
+    __syncthreads();
+    if (set == 0) {
+#pragma unroll
+        for (int s = 1; s < kSets; ++s)
+            A += s_acc4[s * kChunks + chunk];
+        float hl = Lh[0];
+#pragma unroll
+        for (int hh = 1; hh < G; ++hh)
+            hl = (hh == h) ? Lh[hh] : hl;
+        const size_t o = (row0 + h) * kHeadDim + 4 * c;
+        store_out<OUT_F32>(a.out, o + 0, A[0] / hl);
+        store_out<OUT_F32>(a.out, o + 1, A[1] / hl);
+        store_out<OUT_F32>(a.out, o + 2, A[2] / hl);
+        store_out<OUT_F32>(a.out, o + 3, A[3] / hl);
+        if (c == 0 && a.lse != nullptr) {
+            float hm = Mh[0];
+#pragma unroll
+            for (int hh = 1; hh < G; ++hh)
+                hm = (hh == h) ? Mh[hh] : hm;
+            a.lse[row0 + h] = (hm + log2f(hl)) * kLn2;
+        }
     }
     if (tid == 0)
-        atomicExch(ticket, 0);
+        __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __global__ void zero_fill_kernel(uint8_t *p, size_t bytes)

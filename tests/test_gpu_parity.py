@@ -185,3 +185,35 @@ def test_graph_capture_replay():
                                              max_context_len=9000)
         torch.cuda.synchronize()
         assert torch.equal(eager_out, out) and torch.equal(eager_lse, lse), "replay differs from eager"
+
+
+def test_alternating_inputs_share_one_workspace():
+    """Partials of one call must never leak into the next: two different inputs
+    of the same shape alternate on one workspace, each checked every time."""
+    case_a = make_case([30000, 9000, 333], seed=21, pool_pages=3000, max_blocks=1875)
+    case_b = make_case([29000, 9000, 1000], seed=22, pool_pages=3000, max_blocks=1875)
+    da, db = DeviceCase(case_a), DeviceCase(case_b)
+    p = hd.make_params(num_seqs=3, num_q_heads=16, num_kv_heads=8, num_pages=3000,
+                       max_blocks_per_seq=case_a.max_blocks, max_context_len=30000, scale=case_a.scale,
+                       partition_tokens=256)
+    ws = torch.zeros(hd.hipdecode_workspace_bytes(p) // 4 + 4, dtype=torch.int32, device="cuda")
+    refs = {}
+    for name, c in (("a", case_a), ("b", case_b)):
+        refs[name] = oracle.run_case(c)
+    first = {}
+    for it in range(12):
+        name, dc = ("a", da) if it % 2 == 0 else ("b", db)
+        log(f"[parity] alternating call {it} ({name})")
+        out, lse = run_hip(dc, partition_tokens=256, max_context_len=30000, workspace=ws)
+        compare(out, lse, *refs[name], what=f"alternating {it}")
+        if name in first:
+            assert torch.equal(out, first[name][0]) and torch.equal(lse, first[name][1])
+        else:
+            first[name] = (out.clone(), lse.clone())
+    assert int(ws[:3 * 8].abs().sum().item()) == 0
+
+
+def test_maximum_split_count():
+    # 65536 tokens at 64-token partitions: 1024 partials per (request, KV head)
+    case = make_case([65536, 100], seed=23)
+    _check(case, "1024 splits", partition_tokens=64)
