@@ -93,6 +93,8 @@ def main(argv=None) -> int:
     ap.add_argument("--rotate", type=int, default=0, help="distinct KV pool copies (0 = auto)")
     ap.add_argument("--graph", action="store_true", help="replay one captured step per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for the traffic counters)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -109,6 +111,16 @@ def main(argv=None) -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+    if args.copy_calibration:
+        n = 1 << 28   # 2**28 float32 = 1 GiB read and 1 GiB written per copy
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read_per_copy": 4 * n,
+                          "bytes_written_per_copy": 4 * n, "copies": 3}), flush=True)
+        return 0
     hd.library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
