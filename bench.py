@@ -90,6 +90,8 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c3", "c4", "c5", "c3b"])
     ap.add_argument("--partition", type=int, default=0, help="split-K partition tokens (0 = planner)")
+    ap.add_argument("--waves", type=int, default=0, help="wavefronts per workgroup, 4 or 16 (0 = planner)")
+    ap.add_argument("--schedule", type=int, default=0, help="1 = split, 2 = stream (0 = planner)")
     ap.add_argument("--rotate", type=int, default=0, help="distinct KV pool copies (0 = auto)")
     ap.add_argument("--graph", action="store_true", help="replay one captured step per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -146,12 +148,15 @@ def main(argv=None) -> int:
     params = hd.make_params(num_seqs=case.B, num_q_heads=case.Hq, num_kv_heads=case.Hkv,
                             num_pages=case.num_pages, max_blocks_per_seq=case.max_blocks,
                             max_context_len=case.max_context_len, scale=case.scale,
-                            partition_tokens=args.partition,
+                            partition_tokens=args.partition, workgroup_waves=args.waves,
+                            schedule=args.schedule,
                             out_dtype=hd.HIPDECODE_F32 if out_bytes == 4 else hd.HIPDECODE_BF16)
     st = hd.hipdecode_check_params(params)
     if st != 0:
         raise hd.HipDecodeError(st, "params")
     part = hd.hipdecode_partition_tokens(params)
+    waves = hd.hipdecode_workgroup_waves(params)
+    schedule = {1: "split", 2: "stream"}[hd.hipdecode_schedule(params)]
     ws = torch.zeros(hd.hipdecode_workspace_bytes(params) // 4 + 4, dtype=torch.int32, device=dev)
     out = torch.empty((case.B, case.Hq, case.D), dtype=out_dtype, device=dev)
     lse = torch.empty((case.B, case.Hq), dtype=torch.float32, device=dev)
@@ -220,6 +225,8 @@ def main(argv=None) -> int:
             "page_size": case.page,
             "layers_per_step": LAYERS,
             "partition_tokens": part,
+            "workgroup_waves": waves,
+            "schedule": schedule,
             "kv_pool_copies": R,
             "mode": "hipgraph" if graph is not None else "eager",
             "out_dtype": case.out_dtype,

@@ -31,7 +31,8 @@
  *                 its first use (hipdecode_workspace_init or any zero fill);
  *                 every completed call leaves its counters at zero again.
  * q, k_pool, v_pool, out and workspace must be 16-byte aligned; all of them are
- * device memory.  Supported shapes: head_dim 128, page size 16, G in {1, 2, 4}.
+ * device memory.  Supported shapes: head_dim 128, page size 16, G in {1, 2, 4}
+ * (16-wavefront workgroups for G <= 2 only).
  *
  * Ownership and ordering.  The caller owns every buffer.  The library
  * allocates nothing, keeps no per-call state, never synchronises the host and
@@ -88,6 +89,8 @@ typedef struct {
     int32_t max_blocks_per_seq;    /* row stride of block_table, in int32 elements */
     int32_t max_context_len;       /* host upper bound of context_lens[]; sizes the grid */
     int32_t partition_tokens;      /* split-K partition: 0 = planner's choice, else a multiple of 64 */
+    int32_t workgroup_waves;       /* wavefronts per workgroup: 0 = planner's choice, else 4 or 16 */
+    int32_t schedule;              /* 0 = planner's choice, 1 = split by partition, 2 = stream */
     int32_t out_dtype;             /* hipdecode_dtype */
     float scale;                   /* applied to q.k, e.g. 1/sqrt(128) */
 } hipdecode_params;
@@ -103,6 +106,18 @@ hipdecode_status hipdecode_check_params(const hipdecode_params *params);
  * planner's choice when partition_tokens is 0); 0 if the parameters are
  * invalid.  Pure host function. */
 int32_t hipdecode_partition_tokens(const hipdecode_params *params);
+
+/* Wavefronts per workgroup that a call with these parameters uses (the
+ * planner's choice when workgroup_waves is 0); 0 if the parameters are
+ * invalid.  Pure host function. */
+int32_t hipdecode_workgroup_waves(const hipdecode_params *params);
+
+/* Work schedule that a call with these parameters uses (1 = split by
+ * partition, 2 = stream); 0 if the parameters are invalid.  Pure host
+ * function.  split: one workgroup per (request, KV head, partition).
+ * stream: a fixed grid of equal slices of all (request, KV head, page) work,
+ * for batches whose context lengths differ widely (at most 1024 requests). */
+int32_t hipdecode_schedule(const hipdecode_params *params);
 
 /* Bytes of workspace a call with these parameters needs; 0 if they are
  * invalid.  Pure host function. */

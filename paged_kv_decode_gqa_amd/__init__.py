@@ -25,11 +25,15 @@ HIPDECODE_ERR_SCALE = 6
 HIPDECODE_ERR_HIP = 7
 HIPDECODE_BF16 = 0
 HIPDECODE_F32 = 1
+HIPDECODE_SCHEDULE_SPLIT = 1
+HIPDECODE_SCHEDULE_STREAM = 2
 
 EXPORTED = (
     "hipdecode_abi_version",
     "hipdecode_check_params",
     "hipdecode_partition_tokens",
+    "hipdecode_workgroup_waves",
+    "hipdecode_schedule",
     "hipdecode_workspace_bytes",
     "hipdecode_workspace_init",
     "hipdecode_paged_attn",
@@ -48,6 +52,8 @@ class hipdecode_params(ctypes.Structure):
         ("max_blocks_per_seq", ctypes.c_int32),
         ("max_context_len", ctypes.c_int32),
         ("partition_tokens", ctypes.c_int32),
+        ("workgroup_waves", ctypes.c_int32),
+        ("schedule", ctypes.c_int32),
         ("out_dtype", ctypes.c_int32),
         ("scale", ctypes.c_float),
     ]
@@ -78,6 +84,10 @@ def library() -> ctypes.CDLL:
     lib.hipdecode_check_params.restype = ctypes.c_int
     lib.hipdecode_partition_tokens.argtypes = [P]
     lib.hipdecode_partition_tokens.restype = ctypes.c_int32
+    lib.hipdecode_workgroup_waves.argtypes = [P]
+    lib.hipdecode_workgroup_waves.restype = ctypes.c_int32
+    lib.hipdecode_schedule.argtypes = [P]
+    lib.hipdecode_schedule.restype = ctypes.c_int32
     lib.hipdecode_workspace_bytes.argtypes = [P]
     lib.hipdecode_workspace_bytes.restype = ctypes.c_size_t
     lib.hipdecode_workspace_init.argtypes = [vp, ctypes.c_size_t, vp]
@@ -92,10 +102,11 @@ def library() -> ctypes.CDLL:
 
 def make_params(*, num_seqs, num_q_heads, num_kv_heads, num_pages, max_blocks_per_seq,
                 max_context_len, scale, head_dim=128, page_size=16, partition_tokens=0,
-                out_dtype=HIPDECODE_BF16) -> hipdecode_params:
+                workgroup_waves=0, schedule=0, out_dtype=HIPDECODE_BF16) -> hipdecode_params:
     return hipdecode_params(int(num_seqs), int(num_q_heads), int(num_kv_heads), int(head_dim),
                             int(page_size), int(num_pages), int(max_blocks_per_seq),
-                            int(max_context_len), int(partition_tokens), int(out_dtype), float(scale))
+                            int(max_context_len), int(partition_tokens), int(workgroup_waves),
+                            int(schedule), int(out_dtype), float(scale))
 
 
 def hipdecode_abi_version() -> int:
@@ -108,6 +119,14 @@ def hipdecode_check_params(params: hipdecode_params | None) -> int:
 
 def hipdecode_partition_tokens(params: hipdecode_params) -> int:
     return int(library().hipdecode_partition_tokens(ctypes.byref(params)))
+
+
+def hipdecode_workgroup_waves(params: hipdecode_params) -> int:
+    return int(library().hipdecode_workgroup_waves(ctypes.byref(params)))
+
+
+def hipdecode_schedule(params: hipdecode_params) -> int:
+    return int(library().hipdecode_schedule(ctypes.byref(params)))
 
 
 def hipdecode_workspace_bytes(params: hipdecode_params) -> int:
@@ -179,7 +198,8 @@ class PreparedCall:
 
 
 def paged_attn(q, k_pool, v_pool, block_table, context_lens, scale, *, max_context_len,
-               out_dtype=None, partition_tokens=0, out=None, lse=None, workspace=None):
+               out_dtype=None, partition_tokens=0, workgroup_waves=0, schedule=0, out=None, lse=None,
+               workspace=None):
     """Allocate outputs (and a zeroed workspace) as needed and run one call.
 
     q: bf16 [B,Hq,128]; k_pool, v_pool: bf16 [P,16,Hkv,128]; block_table: int32
@@ -197,7 +217,7 @@ def paged_attn(q, k_pool, v_pool, block_table, context_lens, scale, *, max_conte
     params = make_params(num_seqs=B, num_q_heads=Hq, num_kv_heads=Hkv, num_pages=P,
                          max_blocks_per_seq=block_table.shape[1], max_context_len=max_context_len,
                          scale=scale, head_dim=D, page_size=page, partition_tokens=partition_tokens,
-                         out_dtype=code)
+                         workgroup_waves=workgroup_waves, schedule=schedule, out_dtype=code)
     st = hipdecode_check_params(params)
     if st != HIPDECODE_OK:
         raise HipDecodeError(st, "hipdecode_check_params")

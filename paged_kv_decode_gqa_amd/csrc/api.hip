@@ -10,7 +10,13 @@
 namespace hipdecode {
 namespace {
 
-constexpr int64_t kTargetWorkgroups = 1024;   // ~4 per CU for the longest request's share
+constexpr int64_t kTargetWorkgroups4 = 1024;   // 4-wave workgroups: 4 resident per CU
+constexpr int64_t kTargetWorkgroups16 = 256;   // 16-wave workgroups: 1 resident per CU
+constexpr int64_t kWideMinPairs = 32;          // at most this many (request, KV head) pairs ...
+constexpr int64_t kWideMinContext = 8192;      // ... with contexts this long use 16-wave workgroups
+constexpr int64_t kSingleSplitMax = 2048;      // contexts up to this long are not split at all
+constexpr int64_t kBalancedPartition = 2048;   // partition when the target would exceed kMaxPartition
+constexpr int64_t kSingleSplitWidePairs = 256; // ... and use 16-wave workgroups up to this many pairs
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -18,9 +24,34 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Partition size: enough splits that B * Hkv * nsplit reaches the workgroup
-// target for the longest context, in multiples of 64 tokens, at least 256
-// tokens so each wavefront folds a few pages, at most 4096.
+// The split schedule is the default: on MI355X it measured faster than the
+// stream schedule both for equal contexts (16 x 28672) and for the ragged
+// 32-request mix, which stream only matches.  Stream runs when asked for.
+int32_t plan_schedule(const hipdecode_params &p)
+{
+    return p.schedule > 0 ? p.schedule : kScheduleSplit;
+}
+
+// Few long requests get 16-wave workgroups: more pages in flight per
+// partition without more partials to merge.  Everything else gets 4.
+int32_t plan_waves(const hipdecode_params &p)
+{
+    if (plan_schedule(p) == kScheduleStream)
+        return 4;
+    if (p.workgroup_waves > 0)
+        return p.workgroup_waves;
+    const int64_t pairs = (int64_t)p.num_seqs * p.num_kv_heads;
+    const int64_t group = p.num_q_heads / p.num_kv_heads;
+    if (group > 2)
+        return 4;
+    if (p.max_context_len <= kSingleSplitMax)
+        return pairs <= kSingleSplitWidePairs ? 16 : 4;
+    return (pairs <= kWideMinPairs && p.max_context_len >= kWideMinContext) ? 16 : 4;
+}
+
+// Partition size: enough splits that B * Hkv * nsplit reaches the resident
+// workgroup count for the longest context, in multiples of 64 tokens, at
+// least 256 tokens, at most 4096, and at most kMaxMergeSplits partials.
 int32_t plan_partition(const hipdecode_params &p)
 {
     if (p.partition_tokens > 0)
@@ -28,7 +59,11 @@ int32_t plan_partition(const hipdecode_params &p)
     const int64_t pairs = (int64_t)p.num_seqs * p.num_kv_heads;
     if (pairs <= 0 || p.max_context_len <= 0)
         return 256;
-    const int64_t want_splits = ceil_div(kTargetWorkgroups, pairs);
+    // short contexts: one partition per request, no cross-workgroup merge
+    if (p.max_context_len <= kSingleSplitMax)
+        return (int32_t)(ceil_div(p.max_context_len, kMinPartition) * kMinPartition);
+    const int64_t target = plan_waves(p) == 16 ? kTargetWorkgroups16 : kTargetWorkgroups4;
+    const int64_t want_splits = ceil_div(target, pairs);
     int64_t part = ceil_div(p.max_context_len, want_splits);
     if (part < 256)
         part = 256;
@@ -37,9 +72,18 @@ int32_t plan_partition(const hipdecode_params &p)
     if (part < floor_part)
         part = floor_part;
     part = ceil_div(part, kMinPartition) * kMinPartition;
+    // a batch that would want partitions past the maximum has work to spare:
+    // smaller partitions then even out requests of very different lengths
     if (part > kMaxPartition)
-        part = kMaxPartition;
+        part = kBalancedPartition;
     return (int32_t)part;
+}
+
+// Resident 4-wave workgroups of the stream kernel: 4 per CU (3 for G = 4,
+// whose register count allows three per SIMD).
+int32_t stream_workgroups(const hipdecode_params &p)
+{
+    return (p.num_q_heads / p.num_kv_heads <= 2 ? 4 : 3) * 256;
 }
 
 int32_t nsplit_max_of(const hipdecode_params &p, int32_t part)
@@ -48,19 +92,25 @@ int32_t nsplit_max_of(const hipdecode_params &p, int32_t part)
     return n < 1 ? 1 : (int32_t)n;
 }
 
-WorkspaceLayout layout_of(const hipdecode_params &p, int32_t nsplit)
+WorkspaceLayout layout_of(const hipdecode_params &p)
 {
     WorkspaceLayout w;
-    const size_t rows = (size_t)p.num_seqs * (size_t)p.num_q_heads;
     w.counters = 0;
     w.part_ml = align256((size_t)p.num_seqs * (size_t)p.num_kv_heads * sizeof(int32_t));
-    if (nsplit <= 1) {
-        w.part_acc = w.part_ml;
-        w.total = w.part_ml;   // a single partition per request needs only the counters
-        return w;
+    size_t partials;
+    if (plan_schedule(p) == kScheduleStream) {
+        partials = (size_t)2 * stream_workgroups(p) * (size_t)(p.num_q_heads / p.num_kv_heads);
+    } else {
+        const int32_t nsplit = nsplit_max_of(p, plan_partition(p));
+        if (nsplit <= 1) {
+            w.part_acc = w.part_ml;
+            w.total = w.part_ml;   // a single partition per request needs only the counters
+            return w;
+        }
+        partials = (size_t)p.num_seqs * (size_t)p.num_q_heads * (size_t)nsplit;
     }
-    w.part_acc = w.part_ml + align256(rows * (size_t)nsplit * 2 * sizeof(float));
-    w.total = w.part_acc + rows * (size_t)nsplit * kHeadDim * sizeof(float);
+    w.part_acc = w.part_ml + align256(partials * 2 * sizeof(float));
+    w.total = w.part_acc + partials * kHeadDim * sizeof(float);
     return w;
 }
 
@@ -92,16 +142,32 @@ hipdecode_status check(const hipdecode_params *pp)
     if (p.partition_tokens != 0 &&
         (p.partition_tokens % kMinPartition != 0 || p.partition_tokens > kMaxPartition))
         return HIPDECODE_ERR_SHAPE;
+    if (p.workgroup_waves != 0 && p.workgroup_waves != 4 && p.workgroup_waves != 16)
+        return HIPDECODE_ERR_UNSUPPORTED;
+    if (p.workgroup_waves == 16 && group > 2)
+        return HIPDECODE_ERR_UNSUPPORTED;
+    if (p.schedule < 0 || p.schedule > kScheduleStream)
+        return HIPDECODE_ERR_UNSUPPORTED;
+    if (p.schedule == kScheduleStream && (p.num_seqs > kMaxStreamSeqs || p.workgroup_waves == 16))
+        return HIPDECODE_ERR_UNSUPPORTED;
     // index arithmetic inside the kernel: rows of q/out and the grid stay in 31 bits
     const int64_t rows = (int64_t)p.num_seqs * p.num_q_heads;
     if (rows * kHeadDim > INT32_MAX)
         return HIPDECODE_ERR_SHAPE;
-    const int32_t nsplit = nsplit_max_of(p, plan_partition(p));
-    if (nsplit > kMaxMergeSplits)
-        return HIPDECODE_ERR_SHAPE;
-    const int64_t grid = (int64_t)p.num_seqs * p.num_kv_heads * nsplit;
-    if (grid > INT32_MAX)
-        return HIPDECODE_ERR_SHAPE;
+    if (plan_schedule(p) == kScheduleStream) {
+        // flattened (request, KV head, page) units stay in 31 bits
+        const int64_t units = (int64_t)p.num_seqs * p.num_kv_heads * ceil_div(p.max_context_len, kPageSize);
+        if (units > INT32_MAX)
+            return HIPDECODE_ERR_SHAPE;
+    }
+    if (plan_schedule(p) == kScheduleSplit) {
+        const int32_t nsplit = nsplit_max_of(p, plan_partition(p));
+        if (nsplit > kMaxMergeSplits)
+            return HIPDECODE_ERR_SHAPE;
+        const int64_t grid = (int64_t)p.num_seqs * p.num_kv_heads * nsplit;
+        if (grid > INT32_MAX)
+            return HIPDECODE_ERR_SHAPE;
+    }
     return HIPDECODE_OK;
 }
 
@@ -124,12 +190,25 @@ HIPDECODE_API int32_t hipdecode_partition_tokens(const hipdecode_params *params)
     return plan_partition(*params);
 }
 
+HIPDECODE_API int32_t hipdecode_workgroup_waves(const hipdecode_params *params)
+{
+    if (check(params) != HIPDECODE_OK)
+        return 0;
+    return plan_waves(*params);
+}
+
+HIPDECODE_API int32_t hipdecode_schedule(const hipdecode_params *params)
+{
+    if (check(params) != HIPDECODE_OK)
+        return 0;
+    return plan_schedule(*params);
+}
+
 HIPDECODE_API size_t hipdecode_workspace_bytes(const hipdecode_params *params)
 {
     if (check(params) != HIPDECODE_OK)
         return 0;
-    const int32_t part = plan_partition(*params);
-    return layout_of(*params, nsplit_max_of(*params, part)).total;
+    return layout_of(*params).total;
 }
 
 HIPDECODE_API hipdecode_status hipdecode_workspace_init(void *workspace, size_t bytes, void *stream)
@@ -172,12 +251,13 @@ HIPDECODE_API hipdecode_status hipdecode_paged_attn(const hipdecode_params *para
 
     const int32_t part = plan_partition(p);
     const int32_t nsplit = nsplit_max_of(p, part);
-    const WorkspaceLayout w = layout_of(p, nsplit);
+    const WorkspaceLayout w = layout_of(p);
     if (workspace_bytes < w.total)
         return HIPDECODE_ERR_WORKSPACE;
 
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     DecodeArgs a;
+    a.num_seqs = p.num_seqs;
     a.q = static_cast<const uint16_t *>(q);
     a.k_pool = static_cast<const uint16_t *>(k_pool);
     a.v_pool = static_cast<const uint16_t *>(v_pool);
@@ -195,10 +275,11 @@ HIPDECODE_API hipdecode_status hipdecode_paged_attn(const hipdecode_params *para
     a.max_context_len = p.max_context_len;
     a.partition_pages = part / kPageSize;
     a.nsplit_max = nsplit;
+    a.stream_workgroups = stream_workgroups(p);
     a.scale_log2 = p.scale * 1.44269504088896340736f;
 
-    const hipError_t e = launch_paged_decode(a, p.num_q_heads / p.num_kv_heads,
-                                             p.out_dtype == HIPDECODE_F32, p.num_seqs,
+    const hipError_t e = launch_paged_decode(a, p.num_q_heads / p.num_kv_heads, plan_waves(p),
+                                             plan_schedule(p), p.out_dtype == HIPDECODE_F32,
                                              static_cast<hipStream_t>(stream));
     return e == hipSuccess ? HIPDECODE_OK : HIPDECODE_ERR_HIP;
 }

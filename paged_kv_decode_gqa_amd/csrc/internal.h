@@ -9,21 +9,24 @@ namespace hipdecode {
 
 constexpr int kHeadDim = 128;   // dims per head; a K or V row is 256 bytes
 constexpr int kPageSize = 16;   // tokens per page
-constexpr int kWaves = 4;       // wavefronts per workgroup
-constexpr int kThreads = 64 * kWaves;
 constexpr int kMinPartition = 64;     // split-K partitions are multiples of this many tokens
-constexpr int kMaxPartition = 4096;   // at most 256 pages: 64 per wavefront, one table entry per lane
+constexpr int kMaxPartition = 4096;   // at most 256 pages, so at most 64 per wavefront: one table entry per lane
 constexpr int kMaxMergeSplits = 1024; // partitions per request the final merge can weigh in LDS
+constexpr int kMaxStreamSeqs = 1024;  // stream schedule: requests whose page counts fit the LDS prefix sum
+constexpr int kScheduleSplit = 1;
+constexpr int kScheduleStream = 2;
 
-// Byte offsets inside the caller's workspace.
+// Byte offsets inside the caller's workspace.  Partials are indexed
+// [B][Hq][nsplit] by the split schedule and [2W][G] by the stream schedule.
 struct WorkspaceLayout {
     size_t counters;   // int32 [B][Hkv]: arrivals per (request, KV head); zero between calls
-    size_t part_ml;    // fp32  [B][Hq][nsplit][2]: (running max, running sum) in log2 units
-    size_t part_acc;   // fp32  [B][Hq][nsplit][128]: unnormalised weighted sums of V
+    size_t part_ml;    // fp32  [partials][2]: (running max, running sum) in log2 units
+    size_t part_acc;   // fp32  [partials][128]: unnormalised weighted sums of V
     size_t total;
 };
 
 struct DecodeArgs {
+    int32_t num_seqs;
     const uint16_t *q;
     const uint16_t *k_pool;
     const uint16_t *v_pool;
@@ -40,11 +43,13 @@ struct DecodeArgs {
     int32_t max_blocks;
     int32_t max_context_len;
     int32_t partition_pages;
-    int32_t nsplit_max;
+    int32_t nsplit_max;          // split schedule: partitions of the longest context
+    int32_t stream_workgroups;   // stream schedule: grid size
     float scale_log2;   // scale * log2(e): scores are kept in base-2 units
 };
 
-hipError_t launch_paged_decode(const DecodeArgs &a, int group, bool out_f32, int num_seqs,
+// waves: 4 or 16 wavefronts per workgroup (split schedule); schedule: kSchedule*
+hipError_t launch_paged_decode(const DecodeArgs &a, int group, int waves, int schedule, bool out_f32,
                                hipStream_t stream);
 hipError_t launch_zero_fill(void *p, size_t bytes, hipStream_t stream);
 

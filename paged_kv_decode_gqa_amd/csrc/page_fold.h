@@ -212,9 +212,14 @@ __device__ __forceinline__ float coherent_load(const float *p)
     return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Four consecutive floats, 8-byte aligned, as two 64-bit coherent loads.
 __device__ __forceinline__ f32x4 coherent_load4(const float *p)
 {
-    return f32x4{coherent_load(p), coherent_load(p + 1), coherent_load(p + 2), coherent_load(p + 3)};
+    uint64_t *q = reinterpret_cast<uint64_t *>(const_cast<float *>(p));
+    const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return f32x4{__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)),
+                 __uint_as_float((uint32_t)hi), __uint_as_float((uint32_t)(hi >> 32))};
 }
 
 // Weight of a stream with running max m when merged under the overall max M

@@ -1,25 +1,32 @@
-// paged_decode.hip -- gfx950 kernel for one decode step of paged GQA attention,
-// split by (request, KV head, partition of the context).
+// paged_decode.hip -- gfx950 kernels for one decode step of paged GQA attention.
 //
-// One workgroup owns one (request b, KV head g, split-K partition) triple and
-// serves all G query heads that read KV head g (the 16-query/8-KV grouping of
-// the audio.cpp "Decoder And Prompt" section), so every K/V byte of the cache
-// is fetched from HBM exactly once per call.  The work is bound by HBM
-// bandwidth: per cached token and query head it is 2x128 multiply-adds against
-// 256 bytes of K and 256 bytes of V shared by the G heads.  Page-level work is
-// in page_fold.h.
+// Every workgroup serves all G query heads that read one KV head (the
+// 16-query/8-KV grouping of the audio.cpp "Decoder And Prompt" section), so
+// each K/V byte of the cache is fetched from HBM once per call.  The work is
+// bound by HBM bandwidth: per cached token and query head it is 2x128
+// multiply-adds against 256 bytes of K and 256 bytes of V shared by the G
+// heads.  Page-level work is in page_fold.h.
 //
-// The four wavefronts take the partition's pages round-robin, each with one
-// page in flight while it folds the previous one; their 16 row-group streams
-// are merged through LDS with the rule
+// Two schedules share everything below the workgroup level.
+//
+//  * split: one workgroup per (request b, KV head g, partition of the
+//    context).  The grid is sized by the host's max_context_len; partitions
+//    past a request's length exit at once.
+//  * stream: a fixed number W of workgroups (the resident count) take equal
+//    contiguous slices of the flattened (request, KV head, page) sequence,
+//    so a batch of very different context lengths still keeps every CU busy
+//    until the end.  Segment boundaries come from a prefix sum of the
+//    context lengths done in the kernel, so the grid does not depend on them.
+//
+// Inside a workgroup the wavefronts take pages round-robin, each with one page
+// in flight while it folds the previous one; their streams are merged with
 //     M = max m_i,  L = sum l_i 2^(m_i - M),  A = sum acc_i 2^(m_i - M).
-// A request whose context spans several partitions writes each partition's
-// (M, L, A) to the workspace; the last workgroup of a (request, KV head) to
-// arrive, found with an atomic ticket, merges the partials with the same rule
-// (all threads loading in parallel), writes out = A/L and
-// lse = ln2 * (M + log2 L), and resets the ticket, so a call is one launch.
-// The partials travel through device-scope atomics (see page_fold.h), not
-// through fences, so no workgroup flushes or invalidates the L2.
+// A (request, KV head) covered by one workgroup writes out = A/L and
+// lse = ln2 * (M + log2 L) directly.  Otherwise each workgroup writes its
+// partial (M, L, A) to the workspace and the last one to arrive, found with an
+// atomic ticket, merges them with the same rule and resets the ticket, so a
+// call is one launch.  Partials travel through device-scope atomics (see
+// page_fold.h), not fences, so no workgroup flushes or invalidates the L2.
 #include "page_fold.h"
 
 namespace hipdecode {
@@ -27,7 +34,7 @@ namespace {
 
 using namespace dev;
 
-constexpr int kRowStreams = kWaves * 4;
+constexpr int kRegPartials = 4;   // final merge: partial sums per thread loaded up front
 
 __device__ __forceinline__ float wave_max(float v)
 {
@@ -45,176 +52,189 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
-// Block-wide reductions over kThreads; `red` is kWaves floats of LDS.
-__device__ __forceinline__ float block_max(float v, float *red)
+// Merge the four row-group streams of a wavefront (lanes l, l^16, l^32, l^48
+// hold the same dims) so that every row-group ends with the wavefront's total.
+template <int G>
+__device__ __forceinline__ void merge_row_groups(Stream<G> &st)
 {
-    v = wave_max(v);
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0)
-        red[threadIdx.x >> 6] = v;
-    __syncthreads();
-    float r = red[0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w)
-        r = fmaxf(r, red[w]);
-    return r;
-}
-
-__device__ __forceinline__ float block_sum(float v, float *red)
-{
-    v = wave_sum(v);
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0)
-        red[threadIdx.x >> 6] = v;
-    __syncthreads();
-    float r = red[0];
+    for (int o = 16; o <= 32; o <<= 1) {
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w)
-        r += red[w];
-    return r;
-}
-
-template <int G, bool OUT_F32>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
-void paged_decode_kernel(DecodeArgs a)
-{
-    __shared__ f32x4 s_acc4[kRowStreams * G * kHeadDim / 4];
-    __shared__ float s_m[kRowStreams][G];
-    __shared__ float s_l[kRowStreams][G];
-    __shared__ float s_w[G][kMaxMergeSplits];
-    __shared__ float s_red[kWaves];
-    __shared__ int s_last;
-    float *s_acc = reinterpret_cast<float *>(s_acc4);   // [kRowStreams][G][kHeadDim]
-
-    // Workgroup -> (b, split, g) with the KV head fastest: consecutive
-    // workgroups read neighbouring head rows of the same pages.
-    const int Hkv = a.num_kv_heads;
-    const int g = blockIdx.x % Hkv;
-    const int rest = blockIdx.x / Hkv;
-    const int split = rest % a.nsplit_max;
-    const int b = rest / a.nsplit_max;
-    const int tid = threadIdx.x;
-
-    int ctx = a.context_lens[b];
-    ctx = ctx < 0 ? 0 : (ctx > a.max_context_len ? a.max_context_len : ctx);
-    const int n_pages = (ctx + kPageSize - 1) / kPageSize;
-    const int nsplit_b = (n_pages + a.partition_pages - 1) / a.partition_pages;
-    const size_t row0 = (size_t)b * a.num_q_heads + (size_t)g * G;   // first query row of the group
-
-    if (ctx == 0) {
-        if (split == 0) {
-            for (int i = tid; i < G * kHeadDim; i += kThreads)
-                store_out<OUT_F32>(a.out, row0 * kHeadDim + i, 0.f);
-            if (a.lse != nullptr && tid < G)
-                a.lse[row0 + tid] = -INFINITY;
+        for (int h = 0; h < G; ++h) {
+            const float m_o = __shfl_xor(st.m[h], o);
+            const float l_o = __shfl_xor(st.l[h], o);
+            const float M = fmaxf(st.m[h], m_o);
+            const float M_use = (M == -INFINITY) ? 0.f : M;
+            const float w_s = merge_weight(st.m[h], M_use);
+            const float w_o = merge_weight(m_o, M_use);
+            st.l[h] = fmaf(st.l[h], w_s, l_o * w_o);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                st.acc[h][e] = fmaf(st.acc[h][e], w_s, __shfl_xor(st.acc[h][e], o) * w_o);
+            st.m[h] = M;
         }
-        return;
     }
-    if (split >= nsplit_b)
-        return;
+}
 
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int row = lane >> 4;
-    const int sub = lane & 15;
+// LDS shared by both kernels.
+template <int G, int WAVES>
+struct Smem {
+    static constexpr int kThreadsWG = 64 * WAVES;
+    static constexpr int kChunks = G * kHeadDim / 4;   // float4 chunks of G heads
+    static constexpr int kSets = kThreadsWG / kChunks;  // final merge: partial subsets
+    static constexpr int kScratch4 =
+        (WAVES * G * kHeadDim / 4 > kThreadsWG) ? WAVES * G * kHeadDim / 4 : kThreadsWG;
+    f32x4 acc4[kScratch4];          // [WAVES][G][kHeadDim] floats, or final-merge scratch
+    float m[WAVES][G];
+    float l[WAVES][G];
+    float w[G][kMaxMergeSplits];    // final merge: partial maxima, then weights
+    float lw[G][kMaxMergeSplits];   // final merge: partial sums
+    float head_m[G];
+    float head_l[G];
+    int last;
+};
 
-    u32x4 qv[G];
+// Per-lane coordinates inside a workgroup.
+struct Lane {
+    int tid, lane, wave, row, sub;
+    __device__ __forceinline__ Lane()
+    {
+        tid = threadIdx.x;
+        lane = tid & 63;
+        wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        row = lane >> 4;
+        sub = lane & 15;
+    }
+};
+
+template <int G>
+__device__ __forceinline__ void load_q(u32x4 (&qv)[G], const DecodeArgs &a, size_t row0, int sub)
+{
 #pragma unroll
     for (int h = 0; h < G; ++h)
         qv[h] = load16(a.q + (row0 + h) * kHeadDim + sub * 8);
+}
 
-    Stream<G> st;
-    st.init();
-
-    const uint32_t tok_bytes = (uint32_t)Hkv * kHeadDim * 2;   // bytes between slots of a page
-    const size_t page_elems = (size_t)kPageSize * Hkv * kHeadDim;
-    const uint32_t lane_off = (uint32_t)g * kHeadDim * 2 + (uint32_t)row * tok_bytes + (uint32_t)sub * 16;
+// Fold pages [p_begin, p_end) (at most 64 per wavefront) of KV head g of a
+// request with ctx tokens and n_pages pages into this wavefront's stream.
+// entry: the block-table entry of page p_begin + wave + WAVES * lane, or
+// anything for lanes past the range.  A partly filled last page of the
+// request is folded by the last wavefront, with masking, after the others.
+template <int G, int WAVES>
+__device__ __forceinline__ void fold_range(Stream<G> &st, const DecodeArgs &a, const u32x4 (&qv)[G],
+                                           const int32_t *trow, int g, int p_begin, int p_end,
+                                           int n_pages, int ctx, int entry, const Lane &ln)
+{
+    const uint32_t tok_bytes = (uint32_t)a.num_kv_heads * kHeadDim * 2;   // bytes between slots
+    const size_t page_elems = (size_t)kPageSize * a.num_kv_heads * kHeadDim;
+    const uint32_t lane_off = (uint32_t)g * kHeadDim * 2 + (uint32_t)ln.row * tok_bytes + (uint32_t)ln.sub * 16;
     const uint32_t tok4 = 4 * tok_bytes;
 
-    // Full pages of this partition, dealt to the wavefronts round-robin; lane
-    // i of a wavefront holds the block-table entry of its i-th page.  A
-    // request's last page may be partly filled: it is folded separately,
-    // with masking, after the loop.
-    const int p_begin = split * a.partition_pages;
-    const int p_end = min(p_begin + a.partition_pages, n_pages);
     const bool tail_partial = (p_end == n_pages) && (ctx % kPageSize != 0);
     const int full_end = tail_partial ? p_end - 1 : p_end;
     const int span = full_end - p_begin;
-    const int npw = span > wave ? (span - wave + kWaves - 1) / kWaves : 0;
-    const int32_t *trow = a.block_table + (size_t)b * a.max_blocks;
-    const int my_entry = lane < npw ? trow[p_begin + wave + kWaves * lane] : -1;
+    const int npw = span > ln.wave ? (span - ln.wave + WAVES - 1) / WAVES : 0;
+    const int my_entry = ln.lane < npw ? entry : -1;
     const unsigned num_pages = (unsigned)a.num_pages;
 
+    // Loads are issued unconditionally so that the compiler's wait counts stay
+    // exact and page i+1 really is in flight while page i is folded: past the
+    // end the last page is fetched again (a cache hit), and a page id outside
+    // the pool is fetched as page 0 (which exists whenever any context is
+    // non-empty) and never folded.
     PageRegs ra, rb;
     auto issue = [&](PageRegs &r, int i) {
-        const int phys = __builtin_amdgcn_readlane(my_entry, i);
-        if ((unsigned)phys < num_pages)
-            load_page(r, a.k_pool + (size_t)phys * page_elems, a.v_pool + (size_t)phys * page_elems,
-                      lane_off, tok4);
+        const int phys = __builtin_amdgcn_readlane(my_entry, min(i, npw - 1));
+        const int safe = (unsigned)phys < num_pages ? phys : 0;
+        load_page(r, a.k_pool + (size_t)safe * page_elems, a.v_pool + (size_t)safe * page_elems, lane_off, tok4);
     };
     auto fold = [&](const PageRegs &r, int i) {
         const int phys = __builtin_amdgcn_readlane(my_entry, i);
-        if ((unsigned)phys < num_pages)   // a page outside the pool is skipped, never read
+        if ((unsigned)phys < num_pages)   // a page outside the pool is never folded
             fold_page<G, false>(st, r, qv, a.scale_log2, 0, 0);
     };
 
-    if (npw > 0)
+    if (npw > 0) {
         issue(ra, 0);
-    for (int i = 0; i < npw; i += 2) {
-        if (i + 1 < npw)
+        int i = 0;
+        for (; i + 1 < npw; i += 2) {
             issue(rb, i + 1);
-        fold(ra, i);
-        if (i + 1 >= npw)
-            break;
-        if (i + 2 < npw)
+            fold(ra, i);
             issue(ra, i + 2);
-        fold(rb, i + 1);
+            fold(rb, i + 1);
+        }
+        if (i < npw)
+            fold(ra, i);
     }
-    if (tail_partial && wave == kWaves - 1) {
+    if (tail_partial && ln.wave == WAVES - 1) {
         const int phys = trow[full_end];
         if ((unsigned)phys < num_pages) {
             load_page(ra, a.k_pool + (size_t)phys * page_elems, a.v_pool + (size_t)phys * page_elems,
                       lane_off, tok4);
-            fold_page<G, true>(st, ra, qv, a.scale_log2, full_end * kPageSize + row, ctx);
+            fold_page<G, true>(st, ra, qv, a.scale_log2, full_end * kPageSize + ln.row, ctx);
         }
     }
+}
 
-    // ---- merge the workgroup's 16 row-group streams through LDS ----
-    const int sid = wave * 4 + row;
+// Row-groups inside each wavefront, then the wavefronts' totals into LDS.
+// The caller syncs the workgroup afterwards.
+template <int G, int WAVES>
+__device__ __forceinline__ void publish_streams(Stream<G> &st, Smem<G, WAVES> &sm, const Lane &ln)
+{
+    merge_row_groups<G>(st);
+    if (ln.row == 0) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        f32x4 *dst = s_acc4 + ((sid * G + h) * kHeadDim + sub * 8) / 4;
-        dst[0] = f32x4{st.acc[h][0], st.acc[h][1], st.acc[h][2], st.acc[h][3]};
-        dst[1] = f32x4{st.acc[h][4], st.acc[h][5], st.acc[h][6], st.acc[h][7]};
-        if (sub == 0) {
-            s_m[sid][h] = st.m[h];
-            s_l[sid][h] = st.l[h];
+        for (int h = 0; h < G; ++h) {
+            f32x4 *dst = sm.acc4 + ((ln.wave * G + h) * kHeadDim + ln.sub * 8) / 4;
+            dst[0] = f32x4{st.acc[h][0], st.acc[h][1], st.acc[h][2], st.acc[h][3]};
+            dst[1] = f32x4{st.acc[h][4], st.acc[h][5], st.acc[h][6], st.acc[h][7]};
+            if (ln.sub == 0) {
+                sm.m[ln.wave][h] = st.m[h];
+                sm.l[ln.wave][h] = st.l[h];
+            }
         }
     }
-    __syncthreads();
+}
 
-    const bool single = (nsplit_b == 1);
-    for (int idx = tid; idx < G * kHeadDim; idx += kThreads) {
+// Combine the workgroup's wavefronts for query head h, dim d: (M, L, A).
+template <int G, int WAVES>
+__device__ __forceinline__ void combine_waves(const Smem<G, WAVES> &sm, int h, int d, float &M, float &L,
+                                              float &A)
+{
+    const float *s_acc = reinterpret_cast<const float *>(sm.acc4);
+    M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w)
+        M = fmaxf(M, sm.m[w][h]);
+    const float M_use = (M == -INFINITY) ? 0.f : M;
+    L = 0.f;
+    A = 0.f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+        const float wt = merge_weight(sm.m[w][h], M_use);
+        L = fmaf(sm.l[w][h], wt, L);
+        A = fmaf(s_acc[(w * G + h) * kHeadDim + d], wt, A);
+    }
+}
+
+// Write the workgroup's result for G query heads: final output when one
+// workgroup covers the (request, KV head), else a partial at partial index
+// part_index(h).  The caller syncs before and after.
+template <int G, int WAVES, bool OUT_F32, class PartIndex>
+__device__ __forceinline__ void emit(const DecodeArgs &a, const Smem<G, WAVES> &sm, size_t row0, bool final,
+                                     PartIndex part_index, const Lane &ln)
+{
+    for (int idx = ln.tid; idx < G * kHeadDim; idx += Smem<G, WAVES>::kThreadsWG) {
         const int h = idx / kHeadDim;
         const int d = idx % kHeadDim;
-        float M = -INFINITY;
-#pragma unroll
-        for (int s = 0; s < kRowStreams; ++s)
-            M = fmaxf(M, s_m[s][h]);
-        const float M_use = (M == -INFINITY) ? 0.f : M;
-        float L = 0.f, A = 0.f;
-#pragma unroll
-        for (int s = 0; s < kRowStreams; ++s) {
-            const float w = merge_weight(s_m[s][h], M_use);
-            L = fmaf(s_l[s][h], w, L);
-            A = fmaf(s_acc[(s * G + h) * kHeadDim + d], w, A);
-        }
-        if (single) {
+        float M, L, A;
+        combine_waves<G, WAVES>(sm, h, d, M, L, A);
+        if (final) {
             store_out<OUT_F32>(a.out, (row0 + h) * kHeadDim + d, A / L);
             if (d == 0 && a.lse != nullptr)
                 a.lse[row0 + h] = (M + log2f(L)) * kLn2;
         } else {
-            const size_t pi = (row0 + h) * (size_t)a.nsplit_max + split;
+            const size_t pi = part_index(h);
             coherent_store(a.part_acc + pi * kHeadDim + d, A);
             if (d == 0) {
                 coherent_store(a.part_ml + pi * 2 + 0, M);
@@ -222,78 +242,304 @@ void paged_decode_kernel(DecodeArgs a)
             }
         }
     }
-    if (single)
-        return;
+}
 
-    // ---- the last partition of (b, g) to finish merges all partials ----
+// After emitting a partial: take the ticket of (request, KV head); true in the
+// last of `count` workgroups to arrive.  Uniform across the workgroup.
+template <int G, int WAVES>
+__device__ __forceinline__ bool arrive(int32_t *ticket, int count, Smem<G, WAVES> &sm, const Lane &ln)
+{
     // every wavefront's partial stores have completed before the ticket moves
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    int32_t *ticket = a.counters + (size_t)b * Hkv + g;
-    if (tid == 0)
-        s_last = (__hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                  nsplit_b - 1);
+    if (ln.tid == 0)
+        sm.last = (__hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == count - 1);
     __syncthreads();
-    if (!s_last)
-        return;
+    return __builtin_amdgcn_readfirstlane(sm.last) != 0;
+}
 
-    const size_t nsm = (size_t)a.nsplit_max;
-    float Mh[G], Lh[G];
+// Merge `count` partials of G query heads (partial i of head h at index
+// part_index(i, h)), write out and lse, and reset the ticket.
+template <int G, int WAVES, bool OUT_F32, class PartIndex>
+__device__ __forceinline__ void merge_partials(const DecodeArgs &a, Smem<G, WAVES> &sm, size_t row0, int count,
+                                               PartIndex part_index, int32_t *ticket, const Lane &ln)
+{
+    using S = Smem<G, WAVES>;
+    // Every thread owns 4 dims of one head and a 1/kSets share of the
+    // partials.  Its first kRegPartials partial sums and the (m, l) of every
+    // partial are loaded in one batch, so the merge waits on memory once.
+    const int chunk = ln.tid % S::kChunks;
+    const int set = ln.tid / S::kChunks;
+    const int h = chunk / (kHeadDim / 4);
+    const int c = chunk % (kHeadDim / 4);
+    f32x4 pre[kRegPartials];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        const float *ml = a.part_ml + (row0 + h) * nsm * 2;
+    for (int r = 0; r < kRegPartials; ++r) {
+        const int i = set + r * S::kSets;
+        pre[r] = i < count ? coherent_load4(a.part_acc + part_index(i, h) * kHeadDim + 4 * c)
+                           : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int idx = ln.tid; idx < G * count; idx += S::kThreadsWG) {
+        const int hh = idx / count;
+        const int i = idx - hh * count;
+        const float *ml = a.part_ml + part_index(i, hh) * 2;
+        sm.w[hh][i] = coherent_load(ml);
+        sm.lw[hh][i] = coherent_load(ml + 1);
+    }
+    __syncthreads();
+    // wavefront hw turns head hw's maxima into weights and sums L
+    if (ln.wave < G) {
+        const int hw = ln.wave;
         float mx = -INFINITY;
-        for (int i = tid; i < nsplit_b; i += kThreads)
-            mx = fmaxf(mx, coherent_load(ml + 2 * i));
-        Mh[h] = block_max(mx, s_red);
-        const float M_use = (Mh[h] == -INFINITY) ? 0.f : Mh[h];
+        for (int i = ln.lane; i < count; i += 64)
+            mx = fmaxf(mx, sm.w[hw][i]);
+        mx = wave_max(mx);
+        const float M_use = (mx == -INFINITY) ? 0.f : mx;
         float ls = 0.f;
-        for (int i = tid; i < nsplit_b; i += kThreads) {
-            const float w = merge_weight(coherent_load(ml + 2 * i), M_use);
-            s_w[h][i] = w;
-            ls = fmaf(coherent_load(ml + 2 * i + 1), w, ls);
+        for (int i = ln.lane; i < count; i += 64) {
+            const float w = merge_weight(sm.w[hw][i], M_use);
+            sm.w[hw][i] = w;
+            ls = fmaf(sm.lw[hw][i], w, ls);
         }
-        Lh[h] = block_sum(ls, s_red);
+        ls = wave_sum(ls);
+        if (ln.lane == 0) {
+            sm.head_m[hw] = mx;
+            sm.head_l[hw] = ls;
+        }
     }
     __syncthreads();
 
-    // every thread owns 4 dims of one head and a 1/kSets share of the partials
-    constexpr int kChunks = G * kHeadDim / 4;
-    constexpr int kSets = kThreads / kChunks;
-    const int chunk = tid % kChunks;
-    const int set = tid / kChunks;
-    const int h = chunk / (kHeadDim / 4);
-    const int c = chunk % (kHeadDim / 4);
-    const float *acc_h = a.part_acc + (row0 + h) * nsm * kHeadDim + 4 * c;
     f32x4 A = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int i = set; i < nsplit_b; i += kSets)
-        A += s_w[h][i] * coherent_load4(acc_h + (size_t)i * kHeadDim);
-    s_acc4[set * kChunks + chunk] = A;
+#pragma unroll
+    for (int r = 0; r < kRegPartials; ++r) {
+        const int i = set + r * S::kSets;
+        if (i < count)
+            A += sm.w[h][i] * pre[r];
+    }
+#pragma unroll 8
+    for (int i = set + kRegPartials * S::kSets; i < count; i += S::kSets)
+        A += sm.w[h][i] * coherent_load4(a.part_acc + part_index(i, h) * kHeadDim + 4 * c);
+    sm.acc4[set * S::kChunks + chunk] = A;
     __syncthreads();
     if (set == 0) {
 #pragma unroll
-        for (int s = 1; s < kSets; ++s)
-            A += s_acc4[s * kChunks + chunk];
-        float hl = Lh[0];
-#pragma unroll
-        for (int hh = 1; hh < G; ++hh)
-            hl = (hh == h) ? Lh[hh] : hl;
+        for (int s = 1; s < S::kSets; ++s)
+            A += sm.acc4[s * S::kChunks + chunk];
+        const float hl = sm.head_l[h];
         const size_t o = (row0 + h) * kHeadDim + 4 * c;
         store_out<OUT_F32>(a.out, o + 0, A[0] / hl);
         store_out<OUT_F32>(a.out, o + 1, A[1] / hl);
         store_out<OUT_F32>(a.out, o + 2, A[2] / hl);
         store_out<OUT_F32>(a.out, o + 3, A[3] / hl);
-        if (c == 0 && a.lse != nullptr) {
-            float hm = Mh[0];
-#pragma unroll
-            for (int hh = 1; hh < G; ++hh)
-                hm = (hh == h) ? Mh[hh] : hm;
-            a.lse[row0 + h] = (hm + log2f(hl)) * kLn2;
-        }
+        if (c == 0 && a.lse != nullptr)
+            a.lse[row0 + h] = (sm.head_m[h] + log2f(hl)) * kLn2;
     }
-    if (tid == 0)
+    if (ln.tid == 0)
         __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <bool OUT_F32>
+__device__ __forceinline__ void write_empty(const DecodeArgs &a, size_t row0, int rows, int tid, int nthreads)
+{
+    for (int i = tid; i < rows * kHeadDim; i += nthreads)
+        store_out<OUT_F32>(a.out, row0 * kHeadDim + i, 0.f);
+    if (a.lse != nullptr)
+        for (int i = tid; i < rows; i += nthreads)
+            a.lse[row0 + i] = -INFINITY;
+}
+
+__device__ __forceinline__ int clamp_ctx(int ctx, int max_ctx)
+{
+    return ctx < 0 ? 0 : (ctx > max_ctx ? max_ctx : ctx);
+}
+
+// ---------------------------------------------------------------------------
+// split schedule: workgroup = (request, split, KV head), KV head fastest so
+// consecutive workgroups read neighbouring head rows of the same pages.
+// ---------------------------------------------------------------------------
+template <int G, int WAVES, bool OUT_F32>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4)))
+void paged_decode_kernel(DecodeArgs a)
+{
+    __shared__ Smem<G, WAVES> sm;
+    const Lane ln;
+    const int Hkv = a.num_kv_heads;
+    const int g = blockIdx.x % Hkv;
+    const int rest = blockIdx.x / Hkv;
+    const int split = rest % a.nsplit_max;
+    const int b = rest / a.nsplit_max;
+
+    // Issued before the context length arrives: lane i of each wavefront
+    // fetches the table entry of its i-th page of this partition, bounded by
+    // the table row (entries past the request's pages are never used).
+    const int32_t *trow = a.block_table + (size_t)b * a.max_blocks;
+    const int p_begin = split * a.partition_pages;
+    const int spec_idx = p_begin + ln.wave + WAVES * ln.lane;
+    const int spec_entry =
+        (spec_idx < a.max_blocks && ln.lane * WAVES < a.partition_pages) ? trow[spec_idx] : -1;
+
+    const int ctx = clamp_ctx(a.context_lens[b], a.max_context_len);
+    const int n_pages = (ctx + kPageSize - 1) / kPageSize;
+    const int nsplit_b = (n_pages + a.partition_pages - 1) / a.partition_pages;
+    const size_t row0 = (size_t)b * a.num_q_heads + (size_t)g * G;   // first query row of the group
+
+    if (ctx == 0) {
+        if (split == 0)
+            write_empty<OUT_F32>(a, row0, G, ln.tid, 64 * WAVES);
+        return;
+    }
+    if (split >= nsplit_b)
+        return;
+
+    u32x4 qv[G];
+    load_q<G>(qv, a, row0, ln.sub);
+    Stream<G> st;
+    st.init();
+    fold_range<G, WAVES>(st, a, qv, trow, g, p_begin, min(p_begin + a.partition_pages, n_pages), n_pages, ctx,
+                         spec_entry, ln);
+    publish_streams<G, WAVES>(st, sm, ln);
+    __syncthreads();
+
+    const size_t nsm = (size_t)a.nsplit_max;
+    const bool single = (nsplit_b == 1);
+    emit<G, WAVES, OUT_F32>(a, sm, row0, single, [&](int h) { return (row0 + h) * nsm + split; }, ln);
+    if (single)
+        return;
+    int32_t *ticket = a.counters + (size_t)b * Hkv + g;
+    if (!arrive<G, WAVES>(ticket, nsplit_b, sm, ln))
+        return;
+    merge_partials<G, WAVES, OUT_F32>(a, sm, row0, nsplit_b,
+                                      [&](int i, int h) { return (row0 + h) * nsm + i; }, ticket, ln);
+}
+
+// ---------------------------------------------------------------------------
+// stream schedule: gridDim.x workgroups, each an equal contiguous slice of the
+// flattened (request, KV head, page) sequence.  Partials live in two slots per
+// workgroup: slot 2w for the (request, KV head) its slice starts in, slot
+// 2w+1 for the one it ends in; pairs wholly inside a slice finish directly.
+// ---------------------------------------------------------------------------
+// Slices of `total` units over W workgroups: the first `rem` slices hold
+// base + 1 units, the others base (base = total / W >= 1).
+struct Slices {
+    int base, rem;
+    __device__ __forceinline__ int start(int w) const { return w * base + min(w, rem); }
+    __device__ __forceinline__ int owner(int x) const   // the workgroup whose slice holds unit x
+    {
+        const int big = rem * (base + 1);
+        return x < big ? x / (base + 1) : rem + (x - big) / base;
+    }
+};
+
+template <int G, bool OUT_F32>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 2 ? 4 : 3)))
+void paged_decode_stream_kernel(DecodeArgs a)
+{
+    constexpr int WAVES = 4;
+    __shared__ Smem<G, WAVES> sm;
+    __shared__ int s_prefix[kMaxStreamSeqs + 1];   // pages of the requests before b
+    const Lane ln;
+    const int B = a.num_seqs;
+    const int Hkv = a.num_kv_heads;
+
+    // per-request page counts, prefix-summed by wavefront 0
+    if (ln.wave == 0) {
+        int carry = 0;
+        for (int c0 = 0; c0 < B; c0 += 64) {
+            const int i = c0 + ln.lane;
+            int v = 0;
+            if (i < B)
+                v = (clamp_ctx(a.context_lens[i], a.max_context_len) + kPageSize - 1) / kPageSize;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int t = __shfl_up(v, o);
+                if (ln.lane >= o)
+                    v += t;
+            }
+            if (i < B)
+                s_prefix[i + 1] = carry + v;
+            carry += __shfl(v, 63);
+        }
+        if (ln.lane == 0)
+            s_prefix[0] = 0;
+    }
+    __syncthreads();
+
+    // LDS values are the same in every lane: keep them in scalar registers
+    auto prefix = [&](int i) { return __builtin_amdgcn_readfirstlane(s_prefix[i]); };
+
+    // requests with no context: zero output, written by one workgroup each
+    for (int bb = blockIdx.x; bb < B; bb += gridDim.x)
+        if (prefix(bb + 1) == prefix(bb))
+            write_empty<OUT_F32>(a, (size_t)bb * a.num_q_heads, a.num_q_heads, ln.tid, 256);
+
+    const int total = prefix(B) * Hkv;   // below 2^31: checked on the host
+    const int W = total < (int)gridDim.x ? total : (int)gridDim.x;
+    const int w = blockIdx.x;
+    if (w >= W)
+        return;
+    const Slices sl{total / W, total % W};
+    const int x1 = sl.start(w + 1);
+
+    int x = sl.start(w);
+    for (int seg = 0; x < x1; ++seg) {
+        // the request whose units hold x: the last b with Hkv * prefix[b] <= x
+        int lo = 0, hi = B - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (prefix(mid) * Hkv <= x)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        const int b = lo;
+        const int nb = prefix(b + 1) - prefix(b);
+        const int base_b = prefix(b) * Hkv;
+        const int g = (x - base_b) / nb;
+        const int p = x - base_b - g * nb;
+        const int bg_start = base_b + g * nb;
+        const int bg_end = bg_start + nb;
+        const int seg_end = bg_end < x1 ? bg_end : x1;
+        const int p_hi = p + (seg_end - x);
+        const int w_first = sl.owner(bg_start);
+        const int count = sl.owner(bg_end - 1) - w_first + 1;
+        const int ctx = clamp_ctx(a.context_lens[b], a.max_context_len);
+        const size_t row0 = (size_t)b * a.num_q_heads + (size_t)g * G;
+        const int32_t *trow = a.block_table + (size_t)b * a.max_blocks;
+
+        u32x4 qv[G];
+        load_q<G>(qv, a, row0, ln.sub);
+        Stream<G> st;
+        st.init();
+        for (int c0 = p; c0 < p_hi; c0 += 64 * WAVES) {   // at most 64 pages per wavefront at a time
+            const int c1 = min(c0 + 64 * WAVES, p_hi);
+            const int idx = c0 + ln.wave + WAVES * ln.lane;
+            const int entry = idx < c1 ? trow[idx] : -1;
+            fold_range<G, WAVES>(st, a, qv, trow, g, c0, c1, nb, ctx, entry, ln);
+        }
+        __syncthreads();   // the previous segment's readers of sm are done
+        publish_streams<G, WAVES>(st, sm, ln);
+        __syncthreads();
+
+        const int slot = 2 * w + (seg == 0 ? 0 : 1);
+        emit<G, WAVES, OUT_F32>(a, sm, row0, count == 1, [&](int h) { return (size_t)slot * G + h; }, ln);
+        if (count > 1) {
+            int32_t *ticket = a.counters + (size_t)b * Hkv + g;
+            if (arrive<G, WAVES>(ticket, count, sm, ln)) {
+                // the first workgroup holds this pair in its second slot unless
+                // its slice starts exactly where the pair starts
+                const int first_slot = 2 * w_first + (bg_start > sl.start(w_first) ? 1 : 0);
+                merge_partials<G, WAVES, OUT_F32>(
+                    a, sm, row0, count,
+                    [&](int i, int h) {
+                        const int s = i == 0 ? first_slot : 2 * (w_first + i);
+                        return (size_t)s * G + h;
+                    },
+                    ticket, ln);
+            }
+        }
+        __syncthreads();
+        x = seg_end;
+    }
 }
 
 __global__ void zero_fill_kernel(uint8_t *p, size_t bytes)
@@ -307,28 +553,46 @@ __global__ void zero_fill_kernel(uint8_t *p, size_t bytes)
         p[n16 * 16 + threadIdx.x] = 0;
 }
 
-template <int G>
-hipError_t launch_g(const DecodeArgs &a, bool out_f32, unsigned grid, hipStream_t stream)
+template <int G, int WAVES>
+hipError_t launch_split(const DecodeArgs &a, bool out_f32, unsigned grid, hipStream_t stream)
 {
     if (out_f32)
-        hipLaunchKernelGGL((paged_decode_kernel<G, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((paged_decode_kernel<G, WAVES, true>), dim3(grid), dim3(64 * WAVES), 0, stream, a);
     else
-        hipLaunchKernelGGL((paged_decode_kernel<G, false>), dim3(grid), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((paged_decode_kernel<G, WAVES, false>), dim3(grid), dim3(64 * WAVES), 0, stream, a);
     return hipGetLastError();
+}
+
+template <int G>
+hipError_t launch_g(const DecodeArgs &a, int waves, int schedule, bool out_f32, hipStream_t stream)
+{
+    if (schedule == kScheduleStream) {
+        const unsigned grid = (unsigned)a.stream_workgroups;
+        if (out_f32)
+            hipLaunchKernelGGL((paged_decode_stream_kernel<G, true>), dim3(grid), dim3(256), 0, stream, a);
+        else
+            hipLaunchKernelGGL((paged_decode_stream_kernel<G, false>), dim3(grid), dim3(256), 0, stream, a);
+        return hipGetLastError();
+    }
+    const unsigned grid = (unsigned)((size_t)a.num_seqs * a.nsplit_max * a.num_kv_heads);
+    if constexpr (G <= 2) {   // G = 4 at 16 wavefronts would not fit 128 VGPRs without spilling
+        if (waves == 16)
+            return launch_split<G, 16>(a, out_f32, grid, stream);
+    }
+    return waves == 4 ? launch_split<G, 4>(a, out_f32, grid, stream) : hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_paged_decode(const DecodeArgs &a, int group, bool out_f32, int num_seqs,
+hipError_t launch_paged_decode(const DecodeArgs &a, int group, int waves, int schedule, bool out_f32,
                                hipStream_t stream)
 {
-    const size_t grid = (size_t)num_seqs * (size_t)a.nsplit_max * (size_t)a.num_kv_heads;
-    if (grid == 0)
+    if (a.num_seqs == 0)
         return hipSuccess;
     switch (group) {
-    case 1: return launch_g<1>(a, out_f32, (unsigned)grid, stream);
-    case 2: return launch_g<2>(a, out_f32, (unsigned)grid, stream);
-    case 4: return launch_g<4>(a, out_f32, (unsigned)grid, stream);
+    case 1: return launch_g<1>(a, waves, schedule, out_f32, stream);
+    case 2: return launch_g<2>(a, waves, schedule, out_f32, stream);
+    case 4: return launch_g<4>(a, waves, schedule, out_f32, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -33,12 +33,13 @@ class DeviceCase:
         self.out_dtype = torch.float32 if case.out_dtype == "f32" else torch.bfloat16
 
 
-def run_hip(dc: DeviceCase, *, partition_tokens=0, max_context_len=None, workspace=None, out_dtype=None):
+def run_hip(dc: DeviceCase, *, partition_tokens=0, workgroup_waves=0, schedule=0, max_context_len=None,
+            workspace=None, out_dtype=None):
     c = dc.case
     mcl = c.max_context_len if max_context_len is None else max_context_len
     out, lse = hd.paged_attn(dc.q, dc.k, dc.v, dc.table, dc.ctx, c.scale, max_context_len=mcl,
                              out_dtype=out_dtype or dc.out_dtype, partition_tokens=partition_tokens,
-                             workspace=workspace)
+                             workgroup_waves=workgroup_waves, schedule=schedule, workspace=workspace)
     torch.cuda.synchronize()
     return out, lse
 

@@ -43,8 +43,8 @@ def test_abi_version():
 
 
 def test_struct_layout_matches_header():
-    # 10 int32 fields then a float, no padding
-    assert ctypes.sizeof(hd.hipdecode_params) == 44
+    # 12 int32 fields then a float, no padding
+    assert ctypes.sizeof(hd.hipdecode_params) == 52
 
 
 def test_status_strings():
@@ -64,6 +64,13 @@ GOOD = [
     dict(out_dtype=hd.HIPDECODE_F32),
     dict(scale=-0.5),
     dict(scale=0.0),
+    dict(workgroup_waves=4),
+    dict(workgroup_waves=16),
+    dict(num_q_heads=16, num_kv_heads=4, workgroup_waves=4),
+    dict(schedule=1),
+    dict(schedule=2),
+    dict(schedule=2, num_seqs=1),
+    dict(schedule=2, num_seqs=1024, max_context_len=4096, max_blocks_per_seq=256),
 ]
 
 BAD = [
@@ -86,6 +93,13 @@ BAD = [
     (dict(partition_tokens=8192), hd.HIPDECODE_ERR_SHAPE),
     (dict(partition_tokens=-64), hd.HIPDECODE_ERR_SHAPE),
     (dict(max_blocks_per_seq=-1, max_context_len=0), hd.HIPDECODE_ERR_SHAPE),
+    (dict(workgroup_waves=8), hd.HIPDECODE_ERR_UNSUPPORTED),
+    (dict(workgroup_waves=-4), hd.HIPDECODE_ERR_UNSUPPORTED),
+    (dict(num_q_heads=16, num_kv_heads=4, workgroup_waves=16), hd.HIPDECODE_ERR_UNSUPPORTED),
+    (dict(schedule=3), hd.HIPDECODE_ERR_UNSUPPORTED),
+    (dict(schedule=-1), hd.HIPDECODE_ERR_UNSUPPORTED),
+    (dict(schedule=2, num_seqs=1025, max_context_len=4096, max_blocks_per_seq=256), hd.HIPDECODE_ERR_UNSUPPORTED),
+    (dict(schedule=2, workgroup_waves=16), hd.HIPDECODE_ERR_UNSUPPORTED),
 ]
 
 
@@ -102,6 +116,7 @@ def test_check_params_rejects(kw, status):
     assert hd.hipdecode_check_params(p) == status
     assert hd.hipdecode_workspace_bytes(p) == 0
     assert hd.hipdecode_partition_tokens(p) == 0
+    assert hd.hipdecode_workgroup_waves(p) == 0
 
 
 def test_null_params():
@@ -131,9 +146,36 @@ def test_call_rejects_before_any_launch():
         == hd.HIPDECODE_OK
 
 
+def test_planner_wave_choice():
+    # few long requests: 16-wave workgroups, one per CU
+    p1 = base(num_seqs=1, num_pages=2048)
+    assert hd.hipdecode_workgroup_waves(p1) == 16
+    assert 8 * -(-28672 // hd.hipdecode_partition_tokens(p1)) <= 256
+    # many long requests, or G = 4: 4-wave workgroups
+    assert hd.hipdecode_workgroup_waves(base()) == 4
+    assert hd.hipdecode_workgroup_waves(base(num_seqs=1, num_q_heads=16, num_kv_heads=4)) == 4
+    assert hd.hipdecode_workgroup_waves(base(workgroup_waves=4, num_seqs=1)) == 4
+    # short contexts: one partition per request, 16 waves unless the batch is large
+    short = base(num_seqs=16, max_context_len=420, max_blocks_per_seq=27, num_pages=512)
+    assert hd.hipdecode_partition_tokens(short) == 448
+    assert hd.hipdecode_workgroup_waves(short) == 16
+    assert hd.hipdecode_workgroup_waves(base(num_seqs=64, max_context_len=420, max_blocks_per_seq=27)) == 4
+
+
+def test_planner_schedule_choice():
+    # split unless the stream schedule is asked for
+    assert hd.hipdecode_schedule(base()) == hd.HIPDECODE_SCHEDULE_SPLIT
+    assert hd.hipdecode_schedule(base(num_seqs=32, max_context_len=67500, max_blocks_per_seq=4219)) == 1
+    assert hd.hipdecode_schedule(base(num_seqs=1, num_pages=2048)) == hd.HIPDECODE_SCHEDULE_SPLIT
+    assert hd.hipdecode_schedule(base(schedule=2)) == hd.HIPDECODE_SCHEDULE_STREAM
+    assert hd.hipdecode_schedule(base(schedule=1)) == 1
+    # the stream kernel always runs 4-wave workgroups
+    assert hd.hipdecode_workgroup_waves(base(schedule=2, num_seqs=1)) == 4
+
+
 def test_planner_and_workspace_sizes():
-    # long meetings at B=16: 128 (request, KV head) pairs
-    p = base()
+    # split at B=16 x 28672: 128 (request, KV head) pairs, ~1024 workgroups
+    p = base(schedule=1)
     part = hd.hipdecode_partition_tokens(p)
     nsplit = -(-28672 // part)
     assert 256 <= part <= 4096 and part % 64 == 0
@@ -141,8 +183,12 @@ def test_planner_and_workspace_sizes():
     rows = 16 * 16
     expect = 512 + ((rows * nsplit * 8 + 255) // 256) * 256 + rows * nsplit * 128 * 4
     assert hd.hipdecode_workspace_bytes(p) == expect
-    # B=1 at 28672: splits so that 8 * nsplit >= 1024 workgroups
-    p1 = base(num_seqs=1, num_pages=2048)
+    # stream: counters plus two partial slots per workgroup (1024 workgroups, G = 2)
+    ps = base(schedule=2)
+    slots = 2 * 1024 * 2
+    assert hd.hipdecode_workspace_bytes(ps) == 512 + ((slots * 8 + 255) // 256) * 256 + slots * 128 * 4
+    # B=1 at 28672 with 4-wave workgroups: splits so that 8 * nsplit >= ~1024 workgroups
+    p1 = base(num_seqs=1, num_pages=2048, workgroup_waves=4)
     part1 = hd.hipdecode_partition_tokens(p1)
     assert 8 * (-(-28672 // part1)) >= 1024 * 0.85
     # one partition per request: only the counters

@@ -41,21 +41,56 @@ def test_workload_parity(name):
     _check(case, name)
 
 
+@pytest.mark.parametrize("name,waves", [("c3", 4), ("c3b", 4), ("c2", 16)])
+def test_workload_parity_other_waves(name, waves):
+    case = make_config(name)
+    _check(case, f"{name} at {waves} wavefronts", workgroup_waves=waves)
+
+
+@pytest.mark.parametrize("name,schedule", [("c4", 2), ("c5", 2), ("c3", 2), ("c2", 2), ("c1", 2)])
+def test_workload_parity_other_schedule(name, schedule):
+    case = make_config(name)
+    _check(case, f"{name} on schedule {schedule}", schedule=schedule)
+
+
+STREAM_CASES = {
+    "edge lengths poisoned": dict(ctx=[0, 1, 15, 16, 17, 63, 64, 65, 4095, 4096, 4097, 0], poison=True),
+    "one request": dict(ctx=[20000]),
+    "all empty": dict(ctx=[0, 0, 0]),
+    "many mixed": dict(ctx=[int(x) for x in np.random.default_rng(5).integers(0, 6000, size=100)]),
+    "one long many short": dict(ctx=[50000] + [17] * 40 + [3000] * 3),
+    "fp32 out": dict(ctx=[7000, 123, 2048, 9999], out_dtype="f32"),
+    "G=1": dict(ctx=[5000, 700, 12000], Hq=8, Hkv=8),
+    "G=4": dict(ctx=[5000, 700, 12000], Hq=16, Hkv=4),
+}
+
+
+@pytest.mark.parametrize("name", sorted(STREAM_CASES))
+def test_stream_schedule(name):
+    kw = dict(STREAM_CASES[name])
+    ctx = kw.pop("ctx")
+    case = make_case(ctx, seed=31, **kw)
+    _check(case, f"stream: {name}", schedule=2)
+
+
+@pytest.mark.parametrize("waves", [4, 16])
 @pytest.mark.parametrize("partition", [0, 64, 256, 4096])
-def test_edge_lengths_poisoned(partition):
+def test_edge_lengths_poisoned(partition, waves):
     ctx = [0, 1, 15, 16, 17, 63, 64, 65, 4095, 4096, 4097, 0]
     case = make_case(ctx, seed=11, poison=True, pool_pages=sum((n + 15) // 16 for n in ctx) + 7)
-    _check(case, f"edge lengths, partition {partition}", partition_tokens=partition)
+    _check(case, f"edge lengths, partition {partition}, {waves} waves", partition_tokens=partition,
+           workgroup_waves=waves)
 
 
-def test_split_count_invariance():
+@pytest.mark.parametrize("waves", [4, 16])
+def test_split_count_invariance(waves):
     case = make_case([200, 1000, 3333, 8191, 17], seed=12, poison=True)
     dc = DeviceCase(case)
     ref_out, ref_lse = oracle.run_case(case)
     outs = []
     for part in (64, 128, 256, 512, 1024, 2048, 4096, 0):
-        log(f"[parity] split invariance, partition {part}")
-        out, lse = run_hip(dc, partition_tokens=part)
+        log(f"[parity] split invariance, partition {part}, {waves} waves")
+        out, lse = run_hip(dc, partition_tokens=part, workgroup_waves=waves)
         compare(out, lse, ref_out, ref_lse, what=f"partition {part}")
         outs.append(out.float().cpu().numpy())
     spread = max(float(np.abs(o - outs[0]).max()) for o in outs)
@@ -94,10 +129,10 @@ def test_shared_prefix_pages():
     _check(case, "aliased prefix pages")
 
 
-@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 4), (32, 16)])
-def test_group_sizes(hq, hkv):
+@pytest.mark.parametrize("hq,hkv,waves", [(8, 8, 4), (8, 8, 16), (16, 4, 4), (32, 16, 4), (32, 16, 16)])
+def test_group_sizes(hq, hkv, waves):
     case = make_case([777, 3000, 1], seed=16, Hq=hq, Hkv=hkv)
-    _check(case, f"Hq={hq} Hkv={hkv}")
+    _check(case, f"Hq={hq} Hkv={hkv} waves={waves}", workgroup_waves=waves)
 
 
 def test_fp32_output_long():
