@@ -38,7 +38,7 @@ ROTATE_MIN_BYTES = 1.5e9
 KERNEL_SOURCES = ["paged_kv_decode_gqa_amd/csrc/paged_decode.hip",
                   "paged_kv_decode_gqa_amd/csrc/api.hip",
                   "paged_kv_decode_gqa_amd/csrc/internal.h"]
-KERNEL_NAME = "paged_decode_kernel"
+KERNEL_NAMES = {"split": "paged_decode_kernel", "stream": "paged_decode_stream_kernel"}
 
 
 def kernel_source_hash() -> str:
@@ -61,10 +61,10 @@ def algorithmic_bytes(case, out_bytes: int) -> int:
                + 4 * blocks + 4 * case.B)
 
 
-def read_traffic(workload: str):
+def read_traffic(kernel: str, workload: str):
     """HBM bytes per launch from a committed rocprofv3 counter summary, if it
     was taken on the kernel as it is now."""
-    path = os.path.join(ROOT, "profiles", f"{KERNEL_NAME}_{workload}_traffic.txt")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -236,7 +236,7 @@ def main(argv=None) -> int:
         "wall_s_timed": round(wall, 4),
         "roofline": {
             "bound": "hbm",
-            "kernel": KERNEL_NAME,
+            "kernel": KERNEL_NAMES[schedule],
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
@@ -247,7 +247,7 @@ def main(argv=None) -> int:
         },
         "cpu_baseline": None,
     }
-    traffic = read_traffic(args.workload)
+    traffic = read_traffic(KERNEL_NAMES[schedule], args.workload)
     if traffic is not None:
         result["roofline"]["traffic"] = round(traffic)
 

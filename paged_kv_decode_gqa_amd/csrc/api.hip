@@ -10,13 +10,11 @@
 namespace hipdecode {
 namespace {
 
-constexpr int64_t kTargetWorkgroups4 = 1024;   // 4-wave workgroups: 4 resident per CU
-constexpr int64_t kTargetWorkgroups16 = 256;   // 16-wave workgroups: 1 resident per CU
-constexpr int64_t kWideMinPairs = 32;          // at most this many (request, KV head) pairs ...
-constexpr int64_t kWideMinContext = 8192;      // ... with contexts this long use 16-wave workgroups
-constexpr int64_t kSingleSplitMax = 2048;      // contexts up to this long are not split at all
-constexpr int64_t kBalancedPartition = 2048;   // partition when the target would exceed kMaxPartition
-constexpr int64_t kSingleSplitWidePairs = 256; // ... and use 16-wave workgroups up to this many pairs
+constexpr int64_t kTargetWorkgroupsMany = 1024;   // 4-wave workgroups resident at once (4 per CU)
+constexpr int64_t kTargetWorkgroupsFew = 256;     // one per CU, for a few long requests
+constexpr int64_t kFewPairs = 32;                 // (request, KV head) pairs counted as few
+constexpr int64_t kSingleSplitMax = 2048;         // contexts up to this long are not split at all
+constexpr int64_t kBalancedPartition = 2048;      // partition when the target would exceed kMaxPartition
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -24,34 +22,29 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// The split schedule is the default: on MI355X it measured faster than the
-// stream schedule both for equal contexts (16 x 28672) and for the ragged
-// 32-request mix, which stream only matches.  Stream runs when asked for.
+// The split schedule is the default.  On MI355X it measured 290 vs 309 us
+// against the stream schedule for 16 equal 28672-token requests and within
+// 1% of it for the ragged 32-request mix; stream runs when asked for.
 int32_t plan_schedule(const hipdecode_params &p)
 {
     return p.schedule > 0 ? p.schedule : kScheduleSplit;
 }
 
-// Few long requests get 16-wave workgroups: more pages in flight per
-// partition without more partials to merge.  Everything else gets 4.
+// 4-wave workgroups unless 16 are asked for (the stream kernel is 4-wave only).
 int32_t plan_waves(const hipdecode_params &p)
 {
     if (plan_schedule(p) == kScheduleStream)
         return 4;
-    if (p.workgroup_waves > 0)
-        return p.workgroup_waves;
-    const int64_t pairs = (int64_t)p.num_seqs * p.num_kv_heads;
-    const int64_t group = p.num_q_heads / p.num_kv_heads;
-    if (group > 2)
-        return 4;
-    if (p.max_context_len <= kSingleSplitMax)
-        return pairs <= kSingleSplitWidePairs ? 16 : 4;
-    return (pairs <= kWideMinPairs && p.max_context_len >= kWideMinContext) ? 16 : 4;
+    return p.workgroup_waves > 0 ? p.workgroup_waves : 4;
 }
 
-// Partition size: enough splits that B * Hkv * nsplit reaches the resident
-// workgroup count for the longest context, in multiples of 64 tokens, at
-// least 256 tokens, at most 4096, and at most kMaxMergeSplits partials.
+// Partition size, in multiples of 64 tokens, at most 4096 and at most
+// kMaxMergeSplits partials per request.  Short contexts are not split.  A few
+// long requests get about one workgroup per CU (fewer, larger partitions
+// merge faster, and a CU holding two workgroups would finish last); larger
+// batches get about four per CU.  A batch that would want partitions past the
+// maximum has work to spare and gets smaller ones, which even out requests of
+// very different lengths.
 int32_t plan_partition(const hipdecode_params &p)
 {
     if (p.partition_tokens > 0)
@@ -59,31 +52,25 @@ int32_t plan_partition(const hipdecode_params &p)
     const int64_t pairs = (int64_t)p.num_seqs * p.num_kv_heads;
     if (pairs <= 0 || p.max_context_len <= 0)
         return 256;
-    // short contexts: one partition per request, no cross-workgroup merge
     if (p.max_context_len <= kSingleSplitMax)
         return (int32_t)(ceil_div(p.max_context_len, kMinPartition) * kMinPartition);
-    const int64_t target = plan_waves(p) == 16 ? kTargetWorkgroups16 : kTargetWorkgroups4;
-    const int64_t want_splits = ceil_div(target, pairs);
+    const int64_t target = pairs <= kFewPairs ? kTargetWorkgroupsFew : kTargetWorkgroupsMany;
+    const int64_t want_splits = target / pairs > 0 ? target / pairs : 1;
     int64_t part = ceil_div(p.max_context_len, want_splits);
-    if (part < 256)
-        part = 256;
-    // the final merge weighs at most kMaxMergeSplits partials per request
     const int64_t floor_part = ceil_div(p.max_context_len, kMaxMergeSplits);
     if (part < floor_part)
         part = floor_part;
     part = ceil_div(part, kMinPartition) * kMinPartition;
-    // a batch that would want partitions past the maximum has work to spare:
-    // smaller partitions then even out requests of very different lengths
     if (part > kMaxPartition)
         part = kBalancedPartition;
     return (int32_t)part;
 }
 
-// Resident 4-wave workgroups of the stream kernel: 4 per CU (3 for G = 4,
-// whose register count allows three per SIMD).
+// Resident 4-wave workgroups of the stream kernel, which its register count
+// sets: 3 per CU for G <= 2, 2 for G = 4.
 int32_t stream_workgroups(const hipdecode_params &p)
 {
-    return (p.num_q_heads / p.num_kv_heads <= 2 ? 4 : 3) * 256;
+    return (p.num_q_heads / p.num_kv_heads <= 2 ? 3 : 2) * 256;
 }
 
 int32_t nsplit_max_of(const hipdecode_params &p, int32_t part)
@@ -99,7 +86,9 @@ WorkspaceLayout layout_of(const hipdecode_params &p)
     w.part_ml = align256((size_t)p.num_seqs * (size_t)p.num_kv_heads * sizeof(int32_t));
     size_t partials;
     if (plan_schedule(p) == kScheduleStream) {
-        partials = (size_t)2 * stream_workgroups(p) * (size_t)(p.num_q_heads / p.num_kv_heads);
+        // two per tile; tiles <= W + B * Hkv (a tile is a full block, or a request's last)
+        partials = (size_t)2 * ((size_t)stream_workgroups(p) + (size_t)p.num_seqs * p.num_kv_heads) *
+                   (size_t)(p.num_q_heads / p.num_kv_heads);
     } else {
         const int32_t nsplit = nsplit_max_of(p, plan_partition(p));
         if (nsplit <= 1) {
@@ -148,7 +137,10 @@ hipdecode_status check(const hipdecode_params *pp)
         return HIPDECODE_ERR_UNSUPPORTED;
     if (p.schedule < 0 || p.schedule > kScheduleStream)
         return HIPDECODE_ERR_UNSUPPORTED;
-    if (p.schedule == kScheduleStream && (p.num_seqs > kMaxStreamSeqs || p.workgroup_waves == 16))
+    if (p.schedule == kScheduleStream &&
+        (p.num_seqs > kMaxStreamSeqs || p.workgroup_waves == 16 ||
+         // a (request, KV head) merges two partials per block, at most W/Hkv + 1 blocks
+         2 * (stream_workgroups(p) / p.num_kv_heads + 1) > kMaxMergeSplits))
         return HIPDECODE_ERR_UNSUPPORTED;
     // index arithmetic inside the kernel: rows of q/out and the grid stay in 31 bits
     const int64_t rows = (int64_t)p.num_seqs * p.num_q_heads;

@@ -247,15 +247,30 @@ __device__ __forceinline__ void emit(const DecodeArgs &a, const Smem<G, WAVES> &
 // After emitting a partial: take the ticket of (request, KV head); true in the
 // last of `count` workgroups to arrive.  Uniform across the workgroup.
 template <int G, int WAVES>
-__device__ __forceinline__ bool arrive(int32_t *ticket, int count, Smem<G, WAVES> &sm, const Lane &ln)
+__device__ __forceinline__ bool arrive(int32_t *ticket, int count, Smem<G, WAVES> &sm, const Lane &ln,
+                                       int inc = 1)
 {
     // every wavefront's partial stores have completed before the ticket moves
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (ln.tid == 0)
-        sm.last = (__hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == count - 1);
+        sm.last = (__hip_atomic_fetch_add(ticket, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + inc == count);
     __syncthreads();
     return __builtin_amdgcn_readfirstlane(sm.last) != 0;
+}
+
+// An empty partial (no tokens): weight 0 in any merge.
+template <int G, int WAVES>
+__device__ __forceinline__ void emit_empty(const DecodeArgs &a, size_t part_base, const Lane &ln)
+{
+    for (int idx = ln.tid; idx < G * kHeadDim; idx += Smem<G, WAVES>::kThreadsWG) {
+        const size_t pi = part_base + idx / kHeadDim;
+        coherent_store(a.part_acc + pi * kHeadDim + idx % kHeadDim, 0.f);
+        if (idx % kHeadDim == 0) {
+            coherent_store(a.part_ml + pi * 2 + 0, -INFINITY);
+            coherent_store(a.part_ml + pi * 2 + 1, 0.f);
+        }
+    }
 }
 
 // Merge `count` partials of G query heads (partial i of head h at index
@@ -413,98 +428,119 @@ void paged_decode_kernel(DecodeArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// stream schedule: gridDim.x workgroups, each an equal contiguous slice of the
-// flattened (request, KV head, page) sequence.  Partials live in two slots per
-// workgroup: slot 2w for the (request, KV head) its slice starts in, slot
-// 2w+1 for the one it ends in; pairs wholly inside a slice finish directly.
+// stream schedule: W = gridDim.x workgroups take equal contiguous slices of
+// all work units, one unit being one page of one KV head of one request.  The
+// units are ordered request, then block j of S pages, then KV head, then page,
+// with S = ceil(total / W): a tile (request b, block j, KV head g) is at most
+// as long as a slice, so consecutive workgroups read the same pages of
+// neighbouring heads, and every tile is cut into at most two pieces.  Tile t
+// owns partial slots 2t (its first piece) and 2t+1 (its second piece, or an
+// empty partial when one workgroup holds the whole tile), so a (request, KV
+// head) with J blocks always merges exactly 2J partials.
 // ---------------------------------------------------------------------------
 // Slices of `total` units over W workgroups: the first `rem` slices hold
 // base + 1 units, the others base (base = total / W >= 1).
 struct Slices {
     int base, rem;
     __device__ __forceinline__ int start(int w) const { return w * base + min(w, rem); }
-    __device__ __forceinline__ int owner(int x) const   // the workgroup whose slice holds unit x
-    {
-        const int big = rem * (base + 1);
-        return x < big ? x / (base + 1) : rem + (x - big) / base;
-    }
 };
 
+// Exclusive prefix sum by one wavefront of f(i), i < n, into out[0..n].
+template <class F>
+__device__ __forceinline__ void wave_prefix(int *out, int n, F f, int lane)
+{
+    int carry = 0;
+    for (int c0 = 0; c0 < n; c0 += 64) {
+        const int i = c0 + lane;
+        int v = i < n ? f(i) : 0;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int t = __shfl_up(v, o);
+            if (lane >= o)
+                v += t;
+        }
+        if (i < n)
+            out[i + 1] = carry + v;
+        carry += __shfl(v, 63);
+    }
+    if (lane == 0)
+        out[0] = 0;
+}
+
 template <int G, bool OUT_F32>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 2 ? 4 : 3)))
-void paged_decode_stream_kernel(DecodeArgs a)
+__global__ __launch_bounds__(256) void paged_decode_stream_kernel(DecodeArgs a)
 {
     constexpr int WAVES = 4;
     __shared__ Smem<G, WAVES> sm;
-    __shared__ int s_prefix[kMaxStreamSeqs + 1];   // pages of the requests before b
+    __shared__ int s_pages[kMaxStreamSeqs + 1];    // pages of the requests before b
+    __shared__ int s_blocks[kMaxStreamSeqs + 1];   // blocks of the requests before b
+    __shared__ int s_tile_pages;
     const Lane ln;
     const int B = a.num_seqs;
     const int Hkv = a.num_kv_heads;
+    const int Wg = (int)gridDim.x;
 
-    // per-request page counts, prefix-summed by wavefront 0
+    // per-request page counts, then (once the tile size is known) block counts
     if (ln.wave == 0) {
-        int carry = 0;
-        for (int c0 = 0; c0 < B; c0 += 64) {
-            const int i = c0 + ln.lane;
-            int v = 0;
-            if (i < B)
-                v = (clamp_ctx(a.context_lens[i], a.max_context_len) + kPageSize - 1) / kPageSize;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const int t = __shfl_up(v, o);
-                if (ln.lane >= o)
-                    v += t;
-            }
-            if (i < B)
-                s_prefix[i + 1] = carry + v;
-            carry += __shfl(v, 63);
-        }
+        wave_prefix(s_pages, B, [&](int i) {
+            return (clamp_ctx(a.context_lens[i], a.max_context_len) + kPageSize - 1) / kPageSize;
+        }, ln.lane);
+        const int tot = __shfl(s_pages[B], 0) * Hkv;
+        const int Wt = tot < Wg ? tot : Wg;
+        const int S = Wt > 0 ? (tot + Wt - 1) / Wt : 1;
+        wave_prefix(s_blocks, B, [&](int i) { return (s_pages[i + 1] - s_pages[i] + S - 1) / S; }, ln.lane);
         if (ln.lane == 0)
-            s_prefix[0] = 0;
+            s_tile_pages = S;
     }
     __syncthreads();
 
     // LDS values are the same in every lane: keep them in scalar registers
-    auto prefix = [&](int i) { return __builtin_amdgcn_readfirstlane(s_prefix[i]); };
+    auto pages_before = [&](int i) { return __builtin_amdgcn_readfirstlane(s_pages[i]); };
+    auto blocks_before = [&](int i) { return __builtin_amdgcn_readfirstlane(s_blocks[i]); };
 
     // requests with no context: zero output, written by one workgroup each
-    for (int bb = blockIdx.x; bb < B; bb += gridDim.x)
-        if (prefix(bb + 1) == prefix(bb))
+    for (int bb = blockIdx.x; bb < B; bb += Wg)
+        if (pages_before(bb + 1) == pages_before(bb))
             write_empty<OUT_F32>(a, (size_t)bb * a.num_q_heads, a.num_q_heads, ln.tid, 256);
 
-    const int total = prefix(B) * Hkv;   // below 2^31: checked on the host
-    const int W = total < (int)gridDim.x ? total : (int)gridDim.x;
+    const int total = pages_before(B) * Hkv;   // below 2^31: checked on the host
+    const int W = total < Wg ? total : Wg;
     const int w = blockIdx.x;
     if (w >= W)
         return;
+    const int S = __builtin_amdgcn_readfirstlane(s_tile_pages);
     const Slices sl{total / W, total % W};
     const int x1 = sl.start(w + 1);
 
-    int x = sl.start(w);
-    for (int seg = 0; x < x1; ++seg) {
-        // the request whose units hold x: the last b with Hkv * prefix[b] <= x
+    for (int x = sl.start(w); x < x1;) {
+        // the request whose units hold x: the last b with Hkv * pages_before(b) <= x
         int lo = 0, hi = B - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
-            if (prefix(mid) * Hkv <= x)
+            if (pages_before(mid) * Hkv <= x)
                 lo = mid;
             else
                 hi = mid - 1;
         }
         const int b = lo;
-        const int nb = prefix(b + 1) - prefix(b);
-        const int base_b = prefix(b) * Hkv;
-        const int g = (x - base_b) / nb;
-        const int p = x - base_b - g * nb;
-        const int bg_start = base_b + g * nb;
-        const int bg_end = bg_start + nb;
-        const int seg_end = bg_end < x1 ? bg_end : x1;
+        const int nb = pages_before(b + 1) - pages_before(b);
+        const int J = (nb + S - 1) / S;
+        const int off = x - pages_before(b) * Hkv;
+        const int j = min(off / (Hkv * S), J - 1);
+        const int len = min(S, nb - j * S);               // pages of block j
+        const int off_j = off - j * Hkv * S;
+        const int g = off_j / len;
+        const int pin = off_j - g * len;                   // page inside the tile
+        const int tile_end = x - pin + len;
+        const int seg_end = tile_end < x1 ? tile_end : x1;
+        const bool first_piece = (pin == 0);
+        const bool whole = first_piece && seg_end == tile_end;
+        const int p = j * S + pin;
         const int p_hi = p + (seg_end - x);
-        const int w_first = sl.owner(bg_start);
-        const int count = sl.owner(bg_end - 1) - w_first + 1;
         const int ctx = clamp_ctx(a.context_lens[b], a.max_context_len);
         const size_t row0 = (size_t)b * a.num_q_heads + (size_t)g * G;
         const int32_t *trow = a.block_table + (size_t)b * a.max_blocks;
+        const int tile0 = blocks_before(b) * Hkv + g;     // tile of block 0; block j adds j * Hkv
 
         u32x4 qv[G];
         load_q<G>(qv, a, row0, ln.sub);
@@ -516,24 +552,23 @@ void paged_decode_stream_kernel(DecodeArgs a)
             const int entry = idx < c1 ? trow[idx] : -1;
             fold_range<G, WAVES>(st, a, qv, trow, g, c0, c1, nb, ctx, entry, ln);
         }
-        __syncthreads();   // the previous segment's readers of sm are done
+        __syncthreads();   // the previous piece's readers of sm are done
         publish_streams<G, WAVES>(st, sm, ln);
         __syncthreads();
 
-        const int slot = 2 * w + (seg == 0 ? 0 : 1);
-        emit<G, WAVES, OUT_F32>(a, sm, row0, count == 1, [&](int h) { return (size_t)slot * G + h; }, ln);
-        if (count > 1) {
+        if (J == 1 && whole) {
+            emit<G, WAVES, OUT_F32>(a, sm, row0, true, [&](int) { return (size_t)0; }, ln);
+        } else {
+            const int tile = tile0 + j * Hkv;
+            const size_t slot = (size_t)2 * tile + (first_piece ? 0 : 1);
+            emit<G, WAVES, OUT_F32>(a, sm, row0, false, [&](int h) { return slot * G + h; }, ln);
+            if (whole)
+                emit_empty<G, WAVES>(a, (slot + 1) * G, ln);
             int32_t *ticket = a.counters + (size_t)b * Hkv + g;
-            if (arrive<G, WAVES>(ticket, count, sm, ln)) {
-                // the first workgroup holds this pair in its second slot unless
-                // its slice starts exactly where the pair starts
-                const int first_slot = 2 * w_first + (bg_start > sl.start(w_first) ? 1 : 0);
+            if (arrive<G, WAVES>(ticket, 2 * J, sm, ln, whole ? 2 : 1)) {
                 merge_partials<G, WAVES, OUT_F32>(
-                    a, sm, row0, count,
-                    [&](int i, int h) {
-                        const int s = i == 0 ? first_slot : 2 * (w_first + i);
-                        return (size_t)s * G + h;
-                    },
+                    a, sm, row0, 2 * J,
+                    [&](int i, int h) { return ((size_t)2 * (tile0 + (i >> 1) * Hkv) + (i & 1)) * G + h; },
                     ticket, ln);
             }
         }

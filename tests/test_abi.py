@@ -100,6 +100,7 @@ BAD = [
     (dict(schedule=-1), hd.HIPDECODE_ERR_UNSUPPORTED),
     (dict(schedule=2, num_seqs=1025, max_context_len=4096, max_blocks_per_seq=256), hd.HIPDECODE_ERR_UNSUPPORTED),
     (dict(schedule=2, workgroup_waves=16), hd.HIPDECODE_ERR_UNSUPPORTED),
+    (dict(schedule=2, num_q_heads=2, num_kv_heads=1), hd.HIPDECODE_ERR_UNSUPPORTED),
 ]
 
 
@@ -147,30 +148,33 @@ def test_call_rejects_before_any_launch():
 
 
 def test_planner_wave_choice():
-    # few long requests: 16-wave workgroups, one per CU
-    p1 = base(num_seqs=1, num_pages=2048)
-    assert hd.hipdecode_workgroup_waves(p1) == 16
-    assert 8 * -(-28672 // hd.hipdecode_partition_tokens(p1)) <= 256
-    # many long requests, or G = 4: 4-wave workgroups
+    # 4-wave workgroups unless 16 are asked for
     assert hd.hipdecode_workgroup_waves(base()) == 4
-    assert hd.hipdecode_workgroup_waves(base(num_seqs=1, num_q_heads=16, num_kv_heads=4)) == 4
-    assert hd.hipdecode_workgroup_waves(base(workgroup_waves=4, num_seqs=1)) == 4
-    # short contexts: one partition per request, 16 waves unless the batch is large
+    assert hd.hipdecode_workgroup_waves(base(num_seqs=1, num_pages=2048)) == 4
+    assert hd.hipdecode_workgroup_waves(base(num_seqs=1, max_context_len=512)) == 4
+    assert hd.hipdecode_workgroup_waves(base(workgroup_waves=16, num_seqs=1)) == 16
+    assert hd.hipdecode_workgroup_waves(base(schedule=2, workgroup_waves=0)) == 4
+
+
+def test_planner_partitions():
+    # one long request: one workgroup per CU (8 KV heads x 32 partitions)
+    assert hd.hipdecode_partition_tokens(base(num_seqs=1, num_pages=2048)) == 896
+    assert hd.hipdecode_partition_tokens(base(num_seqs=1, max_context_len=65536, max_blocks_per_seq=4096)) == 2048
+    # sixteen long requests: ~four per CU
+    assert hd.hipdecode_partition_tokens(base()) == 3584
+    # a batch wanting partitions past the maximum gets balanced ones
+    assert hd.hipdecode_partition_tokens(base(num_seqs=32, max_context_len=67500, max_blocks_per_seq=4219)) == 2048
+    # short contexts: one partition
     short = base(num_seqs=16, max_context_len=420, max_blocks_per_seq=27, num_pages=512)
     assert hd.hipdecode_partition_tokens(short) == 448
-    assert hd.hipdecode_workgroup_waves(short) == 16
-    assert hd.hipdecode_workgroup_waves(base(num_seqs=64, max_context_len=420, max_blocks_per_seq=27)) == 4
 
 
 def test_planner_schedule_choice():
     # split unless the stream schedule is asked for
     assert hd.hipdecode_schedule(base()) == hd.HIPDECODE_SCHEDULE_SPLIT
     assert hd.hipdecode_schedule(base(num_seqs=32, max_context_len=67500, max_blocks_per_seq=4219)) == 1
-    assert hd.hipdecode_schedule(base(num_seqs=1, num_pages=2048)) == hd.HIPDECODE_SCHEDULE_SPLIT
     assert hd.hipdecode_schedule(base(schedule=2)) == hd.HIPDECODE_SCHEDULE_STREAM
     assert hd.hipdecode_schedule(base(schedule=1)) == 1
-    # the stream kernel always runs 4-wave workgroups
-    assert hd.hipdecode_workgroup_waves(base(schedule=2, num_seqs=1)) == 4
 
 
 def test_planner_and_workspace_sizes():
@@ -183,14 +187,14 @@ def test_planner_and_workspace_sizes():
     rows = 16 * 16
     expect = 512 + ((rows * nsplit * 8 + 255) // 256) * 256 + rows * nsplit * 128 * 4
     assert hd.hipdecode_workspace_bytes(p) == expect
-    # stream: counters plus two partial slots per workgroup (1024 workgroups, G = 2)
+    # stream: counters plus two partial slots per tile, tiles <= W + B * Hkv (768 workgroups, G = 2)
     ps = base(schedule=2)
-    slots = 2 * 1024 * 2
+    slots = 2 * (768 + 16 * 8) * 2
     assert hd.hipdecode_workspace_bytes(ps) == 512 + ((slots * 8 + 255) // 256) * 256 + slots * 128 * 4
-    # B=1 at 28672 with 4-wave workgroups: splits so that 8 * nsplit >= ~1024 workgroups
-    p1 = base(num_seqs=1, num_pages=2048, workgroup_waves=4)
+    # B=1 at 28672: 8 KV heads x 32 partitions = one workgroup per CU
+    p1 = base(num_seqs=1, num_pages=2048)
     part1 = hd.hipdecode_partition_tokens(p1)
-    assert 8 * (-(-28672 // part1)) >= 1024 * 0.85
+    assert 8 * (-(-28672 // part1)) == 256
     # one partition per request: only the counters
     p2 = base(num_seqs=1, max_context_len=200, num_pages=64, max_blocks_per_seq=13)
     assert hd.hipdecode_workspace_bytes(p2) == 256
