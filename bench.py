@@ -37,7 +37,8 @@ LAYERS = 28
 ROTATE_MIN_BYTES = 1.5e9
 KERNEL_SOURCES = ["paged_kv_decode_gqa_amd/csrc/paged_decode.hip",
                   "paged_kv_decode_gqa_amd/csrc/api.hip",
-                  "paged_kv_decode_gqa_amd/csrc/internal.h"]
+                  "paged_kv_decode_gqa_amd/csrc/internal.h",
+                  "paged_kv_decode_gqa_amd/csrc/page_fold.h"]
 KERNEL_NAMES = {"split": "paged_decode_kernel", "stream": "paged_decode_stream_kernel"}
 
 

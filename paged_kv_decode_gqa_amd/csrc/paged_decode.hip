@@ -137,14 +137,14 @@ __device__ __forceinline__ void fold_range(Stream<G> &st, const DecodeArgs &a, c
     const int my_entry = ln.lane < npw ? entry : -1;
     const unsigned num_pages = (unsigned)a.num_pages;
 
-    // Loads are issued unconditionally so that the compiler's wait counts stay
-    // exact and page i+1 really is in flight while page i is folded: past the
-    // end the last page is fetched again (a cache hit), and a page id outside
-    // the pool is fetched as page 0 (which exists whenever any context is
-    // non-empty) and never folded.
+    // The steady-state loop issues its loads unconditionally so that the
+    // compiler's wait counts stay exact and page i+1 really is in flight while
+    // page i is folded; the last one or two pages are peeled off after it.  A
+    // page id outside the pool is fetched as page 0 (which exists whenever
+    // any context is non-empty) and never folded.
     PageRegs ra, rb;
     auto issue = [&](PageRegs &r, int i) {
-        const int phys = __builtin_amdgcn_readlane(my_entry, min(i, npw - 1));
+        const int phys = __builtin_amdgcn_readlane(my_entry, i);
         const int safe = (unsigned)phys < num_pages ? phys : 0;
         load_page(r, a.k_pool + (size_t)safe * page_elems, a.v_pool + (size_t)safe * page_elems, lane_off, tok4);
     };
@@ -157,14 +157,19 @@ __device__ __forceinline__ void fold_range(Stream<G> &st, const DecodeArgs &a, c
     if (npw > 0) {
         issue(ra, 0);
         int i = 0;
-        for (; i + 1 < npw; i += 2) {
+        for (; i + 2 < npw; i += 2) {
             issue(rb, i + 1);
             fold(ra, i);
             issue(ra, i + 2);
             fold(rb, i + 1);
         }
-        if (i < npw)
+        if (i + 1 < npw) {
+            issue(rb, i + 1);
             fold(ra, i);
+            fold(rb, i + 1);
+        } else {
+            fold(ra, i);
+        }
     }
     if (tail_partial && ln.wave == WAVES - 1) {
         const int phys = trow[full_end];
