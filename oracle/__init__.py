@@ -5,9 +5,13 @@ CPU-baseline leg of ``bench.py`` may import this package.  The HIP library and
 its Python binding never do; a product path that reached this code would not be
 a GPU result.
 
-The arithmetic lives in ``paged_attn_oracle.c``: the plain definition
-out = softmax(scale * q K^T) V and lse = ln(sum exp(scale * q K^T)) over the
-tokens a request's block table names, in fp64.
+The arithmetic lives in C:
+
+- ``paged_attn_oracle.c``: the plain definition out = softmax(scale * q K^T) V
+  and lse = ln(sum exp(scale * q K^T)) over the tokens a request's block table
+  names, in fp64;
+- ``kv_append_oracle.c``: writing new tokens' K and V into their pages, with
+  optional RoPE on K and q, rotated in fp64 and rounded once to bf16.
 """
 from __future__ import annotations
 
@@ -58,6 +62,15 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.oracle_paged_attn_pairs.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
+    lib.oracle_round_bf16.argtypes = [ctypes.c_double]
+    lib.oracle_round_bf16.restype = ctypes.c_uint16
+    lib.oracle_rope_f64.argtypes = [p, ctypes.c_int32, ctypes.c_double, ctypes.c_double]
+    lib.oracle_rope_f64.restype = None
+    lib.oracle_kv_append_validate.argtypes = [ctypes.POINTER(OracleShape), ctypes.c_int32, p, p, p]
+    lib.oracle_kv_append_validate.restype = ctypes.c_int
+    lib.oracle_kv_append.argtypes = [ctypes.POINTER(OracleShape), ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_double, p, p, p, p, p, p, p, p]
+    lib.oracle_kv_append.restype = ctypes.c_int
     _LIB_CACHE[path] = lib
     return lib
 
@@ -123,3 +136,78 @@ def validate(q, k_pool, v_pool, block_table, context_lens, *, lib: ctypes.CDLL |
 
 def max_threads(lib: ctypes.CDLL | None = None) -> int:
     return int((lib or load()).oracle_max_threads())
+
+
+def round_bf16(x, *, lib: ctypes.CDLL | None = None) -> np.ndarray:
+    """Nearest-even bf16 bit patterns (uint16) of the float64 values ``x``."""
+    lib = lib or load()
+    flat = np.asarray(x, dtype=np.float64).ravel()
+    out = np.fromiter((lib.oracle_round_bf16(float(v)) for v in flat), dtype=np.uint16, count=flat.size)
+    return out.reshape(np.shape(x))
+
+
+def rope_f64(x, pos, theta, *, lib: ctypes.CDLL | None = None) -> np.ndarray:
+    """RoPE of float64 head vectors ``x[..., D]`` at position ``pos`` (a copy)."""
+    lib = lib or load()
+    y = np.array(x, dtype=np.float64, copy=True)
+    rows = y.reshape(-1, y.shape[-1])
+    for r in rows:
+        lib.oracle_rope_f64(r.ctypes.data, r.shape[0], float(pos), float(theta))
+    return y
+
+
+def _append_prep(k_new, v_new, block_table, context_lens, k_pool, new_start, q, num_q_heads):
+    k_new = np.ascontiguousarray(k_new, dtype=np.uint16)
+    v_new = np.ascontiguousarray(v_new, dtype=np.uint16)
+    block_table = np.ascontiguousarray(block_table, dtype=np.int32)
+    context_lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    if k_new.ndim != 3 or k_new.shape != v_new.shape or k_pool.ndim != 4:
+        raise OracleError("k_new/v_new must be [T,Hkv,D] and equal; pools [P,page,Hkv,D]")
+    T, Hkv, D = k_new.shape
+    P, page, Hkv_p, D_p = k_pool.shape
+    if (Hkv_p, D_p) != (Hkv, D) or block_table.ndim != 2 or context_lens.ndim != 1 \
+            or block_table.shape[0] != context_lens.shape[0]:
+        raise OracleError("inconsistent shapes")
+    B = context_lens.shape[0]
+    if q is not None:
+        if q.ndim != 3 or q.shape[0] != T or q.shape[2] != D:
+            raise OracleError("q must be [T,Hq,D]")
+        num_q_heads = q.shape[1]
+    shape = OracleShape(B, num_q_heads or Hkv, Hkv, D, page, P, block_table.shape[1])
+    ns = None if new_start is None else np.ascontiguousarray(new_start, dtype=np.int32)
+    if ns is not None and ns.shape != (B + 1,):
+        raise OracleError("new_start must have num_seqs + 1 entries")
+    return shape, T, k_new, v_new, block_table, context_lens, ns
+
+
+def kv_append(k_new, v_new, block_table, context_lens, k_pool, v_pool, *, new_start=None, q=None,
+              rope=False, theta=1e6, lib: ctypes.CDLL | None = None):
+    """Append new tokens' K/V (bf16 bits) to copies of the pools.
+
+    Returns ``(k_pool, v_pool, q)``: the updated copies, and q rotated (a copy)
+    or ``None``.  ``new_start`` [B+1] gives each request's rows of ``k_new``;
+    ``None`` means one row per request with a non-empty context.
+    """
+    lib = lib or load()
+    k_out = np.array(k_pool, dtype=np.uint16, copy=True, order="C")
+    v_out = np.array(v_pool, dtype=np.uint16, copy=True, order="C")
+    q_out = None if q is None else np.array(q, dtype=np.uint16, copy=True, order="C")
+    shape, T, k_new, v_new, table, ctx, ns = _append_prep(k_new, v_new, block_table, context_lens, k_out,
+                                                          new_start, q_out, None)
+    rc = lib.oracle_kv_append(ctypes.byref(shape), T, 1 if rope else 0, float(theta),
+                              None if q_out is None else q_out.ctypes.data, k_new.ctypes.data,
+                              v_new.ctypes.data, None if ns is None else ns.ctypes.data,
+                              table.ctypes.data, ctx.ctypes.data, k_out.ctypes.data, v_out.ctypes.data)
+    if rc != 0:
+        raise OracleError(f"oracle_kv_append returned {rc}")
+    return k_out, v_out, q_out
+
+
+def kv_append_validate(k_new, block_table, context_lens, k_pool, *, new_start=None,
+                       lib: ctypes.CDLL | None = None) -> int:
+    lib = lib or load()
+    k_new = np.asarray(k_new)
+    shape, T, _, _, table, ctx, ns = _append_prep(k_new, k_new, block_table, context_lens, np.asarray(k_pool),
+                                                  new_start, None, None)
+    return int(lib.oracle_kv_append_validate(ctypes.byref(shape), T, None if ns is None else ns.ctypes.data,
+                                             table.ctypes.data, ctx.ctypes.data))

@@ -14,28 +14,32 @@ import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "paged_attn_oracle.c")
+APPEND_SRC = os.path.join(HERE, "kv_append_oracle.c")
+SOURCES = [SRC, APPEND_SRC]
 LIB = os.path.join(HERE, "liboracle.so")
 CFLAGS = ["-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra"]
 
 
-def _compile(src: str, out: str, include_dir: str) -> None:
-    cmd = ["gcc", *CFLAGS, f"-I{include_dir}", "-o", out + ".tmp", src, "-lm"]
+def _compile(srcs: list[str], out: str, include_dir: str) -> None:
+    cmd = ["gcc", *CFLAGS, f"-I{include_dir}", "-o", out + ".tmp", *srcs, "-lm"]
     subprocess.run(cmd, check=True, capture_output=True, text=True)
     os.replace(out + ".tmp", out)
 
 
 def build(out: str = LIB) -> str:
     """Compile the oracle; returns the path of the shared library."""
-    _compile(SRC, out, HERE)
+    _compile(SOURCES, out, HERE)
     return out
 
 
-def build_variant(substitutions: list[tuple[str, str]], out_dir: str | None = None) -> str:
-    """Compile a copy of the oracle with each ``(old, new)`` text replaced once.
+def build_variant(substitutions: list[tuple[str, str]], out_dir: str | None = None,
+                  source: str = SRC) -> str:
+    """Compile a copy of the oracle with each ``(old, new)`` text replaced once
+    in ``source`` (one of ``SOURCES``); the other sources are built unchanged.
 
     Raises ``ValueError`` if some ``old`` text is not found exactly once.
     """
-    with open(SRC) as f:
+    with open(source) as f:
         text = f.read()
     for old, new in substitutions:
         if text.count(old) != 1:
@@ -46,7 +50,7 @@ def build_variant(substitutions: list[tuple[str, str]], out_dir: str | None = No
     with open(src, "w") as f:
         f.write(text)
     out = os.path.join(d, "libvariant.so")
-    _compile(src, out, HERE)
+    _compile([src if s == source else s for s in SOURCES], out, HERE)
     return out
 
 

@@ -40,6 +40,34 @@ MUTANTS = {
 }
 
 
+# Slips in the append oracle: the RoPE pairing, sign, frequency, base or
+# position; the rounding's precision, direction or subnormal range; a slot off
+# by one; V rotated; q left unrotated; stale rows.
+APPEND_MUTANTS = {
+    "rope_sign": [("x[i + half] = second * c + first * s;", "x[i + half] = second * c - first * s;")],
+    "rope_adjacent_pairs": [("const double first = x[i];\n        const double second = x[i + half];",
+                             "const double first = x[i];\n        const double second = x[i ^ 1];")],
+    "rope_frequency_exponent": [("pow(theta, -2.0 * (double)i / (double)head_dim)",
+                                 "pow(theta, -(double)i / (double)head_dim)")],
+    "rope_default_base": [("pow(theta, -2.0", "pow(10000.0, -2.0")],
+    "rope_angle_sign": [("const double angle = pos * freq;", "const double angle = -pos * freq;")],
+    "rope_at_context_length": [("dim, rope, (double)pos, theta, scratch);\n                memcpy",
+                                "dim, rope, (double)c, theta, scratch);\n                memcpy")],
+    "round_truncates": [("r = ldexp(nearbyint(ldexp(x, -step)), step);", "r = ldexp(trunc(ldexp(x, -step)), step);")],
+    "round_nine_bits": [("int step = e - 8;", "int step = e - 9;")],
+    "round_no_subnormals": [("if (step < -133)\n            step = -133;", "if (step < -126)\n            step = -126;")],
+    "slot_off_by_one": [("const size_t slot = (size_t)page * s->page_size + pos % s->page_size;",
+                         "const size_t slot = (size_t)page * s->page_size + (pos + 1) % s->page_size;")],
+    "position_off_by_one": [("const int32_t pos = c - n + j;", "const int32_t pos = c - n + j - 1 + (c - n + j == 0);")],
+    "v_rotated": [("memcpy(v_pool + slot * kv_row + (size_t)g * dim, v_new + row * kv_row + (size_t)g * dim,\n"
+                   "                       (size_t)dim * sizeof *v_pool);",
+                   "rotate_head(v_new + row * kv_row + (size_t)g * dim, v_pool + slot * kv_row + (size_t)g * dim,\n"
+                   "                            dim, rope, (double)pos, theta, scratch);")],
+    "q_not_rotated": [("if (q && rope)", "if (q && !rope)")],
+    "row_ignores_start": [("const size_t row = (size_t)start + j;", "const size_t row = (size_t)b + j;")],
+}
+
+
 def test_unmutated_copy_passes(tmp_path):
     lib = obuild.build_variant([], out_dir=str(tmp_path))
     r = subprocess.run([sys.executable, "-m", "tests.oracle_pins", "--lib", lib],
@@ -51,5 +79,20 @@ def test_unmutated_copy_passes(tmp_path):
 def test_mutant_is_caught(name, tmp_path):
     lib = obuild.build_variant(MUTANTS[name], out_dir=str(tmp_path))
     r = subprocess.run([sys.executable, "-m", "tests.oracle_pins", "--lib", lib],
+                       cwd=ROOT, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout}"
+
+
+def test_unmutated_append_copy_passes(tmp_path):
+    lib = obuild.build_variant([], out_dir=str(tmp_path), source=obuild.APPEND_SRC)
+    r = subprocess.run([sys.executable, "-m", "tests.oracle_append_pins", "--lib", lib],
+                       cwd=ROOT, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stdout + r.stderr
+
+
+@pytest.mark.parametrize("name", sorted(APPEND_MUTANTS))
+def test_append_mutant_is_caught(name, tmp_path):
+    lib = obuild.build_variant(APPEND_MUTANTS[name], out_dir=str(tmp_path), source=obuild.APPEND_SRC)
+    r = subprocess.run([sys.executable, "-m", "tests.oracle_append_pins", "--lib", lib],
                        cwd=ROOT, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout}"
