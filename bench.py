@@ -15,6 +15,11 @@ roofline.achieved = algorithmic bytes per call / average call duration,
 cpu_baseline = the fp64 oracle, unmodified, on this host's cores, over one
           layer's worth of (request, head) pairs, scaled to tokens/s.
 
+``--op append`` measures the KV-cache append instead (``hipdecode_kv_append``
+with RoPE on K and q): a step is 28 calls, one per layer, each writing the new
+tokens of workload a1 (one token for each of 16 requests) or a2 (one
+4096-token prefill chunk) into its own copy of the pools.
+
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -35,16 +40,21 @@ METRIC = "decode attn tokens/s and achieved HBM GB/s (% of peak) at 28k/64k ctx"
 PEAK_HBM_GBS = 8000.0
 LAYERS = 28
 ROTATE_MIN_BYTES = 1.5e9
-KERNEL_SOURCES = ["paged_kv_decode_gqa_amd/csrc/paged_decode.hip",
+DECODE_SOURCES = ["paged_kv_decode_gqa_amd/csrc/paged_decode.hip",
                   "paged_kv_decode_gqa_amd/csrc/api.hip",
                   "paged_kv_decode_gqa_amd/csrc/internal.h",
                   "paged_kv_decode_gqa_amd/csrc/page_fold.h"]
+APPEND_SOURCES = ["paged_kv_decode_gqa_amd/csrc/kv_append.hip",
+                  "paged_kv_decode_gqa_amd/csrc/internal.h"]
 KERNEL_NAMES = {"split": "paged_decode_kernel", "stream": "paged_decode_stream_kernel"}
+KERNEL_SOURCES = {"paged_decode_kernel": DECODE_SOURCES, "paged_decode_stream_kernel": DECODE_SOURCES,
+                  "kv_append_kernel": APPEND_SOURCES}
+APPEND_METRIC = "kv-cache append new tokens/s (RoPE on K and q) and achieved HBM GB/s"
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kernel: str = "paged_decode_kernel") -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -74,7 +84,7 @@ def read_traffic(kernel: str, workload: str):
         if line and not line.startswith("#") and "=" in line:
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256") != kernel_source_hash():
+    if kv.get("kernel_source_sha256") != kernel_source_hash(kernel):
         return None
     try:
         fetch = float(kv["fetch_kib_per_dispatch"]) * float(kv.get("copy_scale_fetch", 1.0))
@@ -84,12 +94,25 @@ def read_traffic(kernel: str, workload: str):
     return (fetch + write) * 1024.0
 
 
+def append_algorithmic_bytes(case, inputs) -> int:
+    """Bytes an append must move: each new token's K and V rows read and
+    written, its q rows read and written, one table entry per token, the
+    lengths and the row offsets."""
+    T = int(inputs.new_start[-1]) if inputs.new_start is not None else int((case.context_lens > 0).sum())
+    kv = 2 * case.Hkv * case.D * 2
+    qb = case.Hq * case.D * 2 if inputs.q is not None else 0
+    offsets = 4 * (case.B + 1) if inputs.new_start is not None else 0
+    return int(T * (2 * kv + 2 * qb + 4) + 4 * case.B + offsets)
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c4", choices=["c1", "c2", "c3", "c4", "c5", "c3b"])
+    ap.add_argument("--op", default="decode", choices=["decode", "append"])
+    ap.add_argument("--workload", default=None,
+                    help="decode: c1 c2 c3 c4 c5 c3b (default c4); append: a1 a2 (default a2)")
     ap.add_argument("--partition", type=int, default=0, help="split-K partition tokens (0 = planner)")
     ap.add_argument("--waves", type=int, default=0, help="wavefronts per workgroup, 4 or 16 (0 = planner)")
     ap.add_argument("--schedule", type=int, default=0, help="1 = split, 2 = stream (0 = planner)")
@@ -127,6 +150,12 @@ def main(argv=None) -> int:
     hd.library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.op == "append":
+        return run_append(args, dev)
+    args.workload = args.workload or "c4"
+    if args.workload not in ("c1", "c2", "c3", "c4", "c5", "c3b"):
+        print(f"unknown decode workload {args.workload}", file=sys.stderr)
+        return 2
 
     t0 = time.time()
     case = make_config(args.workload)
@@ -271,6 +300,145 @@ def main(argv=None) -> int:
             "sample": f"fp64 oracle over all {case.B * case.Hq} (request, head) pairs of one layer call, "
                       f"{reps} run(s), {t_layer:.3f} s per layer, scaled to {LAYERS} layers per token",
             "parity_max_abs_err": float(np.abs(o_gpu - ref_out).max()),
+        }
+    result["setup_s"] = round(t_gen, 2)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def run_append(args, dev) -> int:
+    import numpy as np
+    import torch
+
+    import paged_kv_decode_gqa_amd as hd
+    from workloads import APPEND_CONFIGS, make_append_config
+
+    name = args.workload or "a2"
+    if name not in APPEND_CONFIGS:
+        print(f"unknown append workload {name}", file=sys.stderr)
+        return 2
+    t0 = time.time()
+    case, inputs = make_append_config(name)
+    alg_bytes = append_algorithmic_bytes(case, inputs)
+    # distinct copies (inputs, table and pool each) so the calls stream from HBM
+    R = args.rotate or max(2, min(LAYERS, math.ceil(ROTATE_MIN_BYTES / max(1, alg_bytes))))
+    copies = [(case, inputs)] + [make_append_config(name, copy=i) for i in range(1, R)]
+    t_gen = time.time() - t0
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def i32(a):
+        return None if a is None else torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    dev_copies = []
+    for c, inp in copies:
+        dev_copies.append(dict(q=bf(inp.q), k_new=bf(inp.k_new), v_new=bf(inp.v_new), new_start=i32(inp.new_start),
+                               table=i32(c.block_table), ctx=i32(c.context_lens), k=bf(c.k_pool), v=bf(c.v_pool)))
+    params = hd.make_append_params(num_seqs=case.B, num_q_heads=case.Hq, num_kv_heads=case.Hkv,
+                                   num_pages=case.num_pages, max_blocks_per_seq=case.max_blocks,
+                                   num_rows=inputs.rows, max_new_tokens=inputs.max_new_tokens,
+                                   rope=hd.HIPDECODE_ROPE_HALF, rope_theta=inputs.theta)
+    st = hd.hipdecode_check_append_params(params)
+    if st != 0:
+        raise hd.HipDecodeError(st, "append params")
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def one_step():
+        for layer in range(LAYERS):
+            d = dev_copies[layer % R]
+            hd.hipdecode_kv_append(params, d["q"], d["k_new"], d["v_new"], d["new_start"], d["table"], d["ctx"],
+                                   d["k"], d["v"])
+
+    graph = None
+    if args.graph:
+        one_step()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            one_step()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+    run = graph.replay if graph is not None else one_step
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        run()
+    ev1.record(stream)
+    ev1.synchronize()
+    wall = time.perf_counter() - w0
+    ms = ev0.elapsed_time(ev1)
+    call_s = ms * 1e-3 / (args.steps * LAYERS)
+    T = int(inputs.new_start[-1]) if inputs.new_start is not None else case.B
+    achieved = alg_bytes / call_s / 1e9
+    result = {
+        "metric": APPEND_METRIC,
+        "value": round(T / call_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 rows and pools; no dataset)",
+        "config": {
+            "workload": case.name,
+            "batch": case.B,
+            "new_tokens_per_call": T,
+            "max_context": int(case.context_lens.max()),
+            "num_q_heads": case.Hq,
+            "num_kv_heads": case.Hkv,
+            "head_dim": case.D,
+            "page_size": case.page,
+            "rope_theta": inputs.theta,
+            "layers_per_step": LAYERS,
+            "copies": R,
+            "mode": "hipgraph" if graph is not None else "eager",
+        },
+        "us_per_layer": round(call_s * 1e6, 3),
+        "wall_s_timed": round(wall, 4),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "kv_append_kernel",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": alg_bytes,
+            "avg_launch_us": round(call_s * 1e6, 3),
+        },
+        "cpu_baseline": None,
+    }
+    traffic = read_traffic("kv_append_kernel", name)
+    if traffic is not None:
+        result["roofline"]["traffic"] = round(traffic)
+    if not args.no_cpu_baseline:
+        import oracle
+        reps, t_cpu = 0, 0.0
+        while reps < 50 and (t_cpu < 10.0 or reps == 0):
+            c0 = time.perf_counter()
+            oracle.kv_append(inputs.k_new, inputs.v_new, case.block_table, case.context_lens, case.k_pool,
+                             case.v_pool, new_start=inputs.new_start, q=inputs.q, rope=True, theta=inputs.theta)
+            t_cpu += time.perf_counter() - c0
+            reps += 1
+        t_call = t_cpu / reps
+        result["cpu_baseline"] = {
+            "value": round(T / t_call, 1),
+            "unit": "tokens/s",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": f"fp64 oracle append of the same {T} new tokens (copies of the pools included), "
+                      f"{reps} run(s), {t_call * 1e3:.2f} ms per call",
         }
     result["setup_s"] = round(t_gen, 2)
     print(json.dumps(result), flush=True)

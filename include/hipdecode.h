@@ -70,7 +70,7 @@ typedef enum {
     HIPDECODE_ERR_UNSUPPORTED = 3, /* valid but not built: head_dim, page size, group, dtype */
     HIPDECODE_ERR_ALIGN = 4,       /* a buffer is not 16-byte aligned */
     HIPDECODE_ERR_WORKSPACE = 5,   /* workspace smaller than hipdecode_workspace_bytes */
-    HIPDECODE_ERR_SCALE = 6,       /* scale is not finite */
+    HIPDECODE_ERR_SCALE = 6,       /* scale is not finite, or rope_theta not finite and > 0 */
     HIPDECODE_ERR_HIP = 7          /* the HIP runtime refused the launch */
 } hipdecode_status;
 
@@ -139,6 +139,87 @@ hipdecode_status hipdecode_paged_attn(const hipdecode_params *params,
                                       void *workspace,
                                       size_t workspace_bytes,
                                       void *stream);
+
+/* ------------------------------------------------------------------------
+ * KV-cache append.
+ *
+ * Before a decode step attends, each request's cache is extended by the token
+ * it has just produced; prefill writes a chunk of prompt tokens the same way
+ * (MOSS-TD article, "ASR model basics" and "Chunked prefill for long audio";
+ * paged cache: FunASR vLLM guide, "Why vLLM?").  The Qwen3 decoder rotates
+ * queries and keys by RoPE with theta 1e6 (audio.cpp "Fun-ASR-Nano Native
+ * Runtime Design", "Decoder And Prompt"); the pages give no pairing or
+ * precision, so this library takes the rotate-half pairing and an exact
+ * rotation rounded once.
+ *
+ * For request b with n_b new tokens and context length c_b (which already
+ * counts them), new token j in [0, n_b) is at position p = c_b - n_b + j and
+ * comes from row r = new_start[b] + j of the packed inputs (r = b and n_b = 1,
+ * or n_b = 0 when c_b == 0, if new_start is NULL).  With
+ * page = block_table[b][p / 16] and slot = p % 16:
+ *     K[page][slot][g][:] = R_p(k_new[r][g][:])   for every KV head g
+ *     V[page][slot][g][:] = v_new[r][g][:]        (bit copy)
+ *     q[r][h][:]          = R_p(q[r][h][:])       for every query head h, in place
+ * With rope == HIPDECODE_ROPE_NONE, R_p is a bit copy and q is not touched.
+ * Otherwise, for i in [0, 64) and f_i = rope_theta^(-i/64):
+ *     x'[i]      = x[i] cos(p f_i) - x[i + 64] sin(p f_i)
+ *     x'[i + 64] = x[i + 64] cos(p f_i) + x[i] sin(p f_i)
+ * evaluated in fp64 from the exactly widened bf16 inputs and rounded once to
+ * the nearest bf16, ties to even.
+ *
+ * Layouts (row-major, contiguous):
+ *   q             [num_rows][num_q_heads][128]   bf16, may be NULL
+ *   k_new, v_new  [num_rows][num_kv_heads][128]  bf16
+ *   new_start     [num_seqs + 1]                 int32, may be NULL
+ *   block_table, context_lens, k_pool, v_pool as for hipdecode_paged_attn.
+ * q, k_new, v_new, k_pool and v_pool must be 16-byte aligned; all are device
+ * memory.  Calls are stream-ordered and asynchronous, allocate nothing, and
+ * may be captured into a HIP graph.
+ *
+ * Device-side contract: new_start non-decreasing with new_start[num_seqs] <=
+ * num_rows; n_b <= min(c_b, max_new_tokens); the blocks written name pool
+ * pages; no two new tokens share a slot; k_new, v_new and q do not overlap
+ * the pools.  When it is broken the kernel still neither reads nor writes
+ * outside the buffers the sizes describe: a request with n_b > c_b, n_b >
+ * max_new_tokens or rows outside [0, num_rows) writes nothing, and a token
+ * whose block lies past max_blocks_per_seq or names no pool page is skipped.
+ * Overlapping slots or buffers give unspecified contents.
+ * ------------------------------------------------------------------------ */
+
+typedef enum {
+    HIPDECODE_ROPE_NONE = 0,
+    HIPDECODE_ROPE_HALF = 1        /* rotate-half pairing: i with i + head_dim/2 */
+} hipdecode_rope;
+
+typedef struct {
+    int32_t num_seqs;              /* B >= 0; B == 0 is a no-op */
+    int32_t num_q_heads;           /* Hq, heads of q */
+    int32_t num_kv_heads;          /* Hkv; Hq % Hkv == 0 */
+    int32_t head_dim;              /* must be 128 */
+    int32_t page_size;             /* must be 16 */
+    int32_t num_pages;             /* P, rows of each pool */
+    int32_t max_blocks_per_seq;    /* row stride of block_table, in int32 elements */
+    int32_t num_rows;              /* rows of k_new, v_new and q; >= num_seqs if new_start is NULL */
+    int32_t max_new_tokens;        /* host upper bound of any n_b; sizes the grid (1 if new_start is NULL) */
+    int32_t rope;                  /* hipdecode_rope */
+    double rope_theta;             /* RoPE base, e.g. 1e6; finite and > 0 when rope is on */
+} hipdecode_append_params;
+
+/* Pure host check of an append parameter block: HIPDECODE_OK or the first
+ * problem found. */
+hipdecode_status hipdecode_check_append_params(const hipdecode_append_params *params);
+
+/* Appends new tokens' keys and values to the paged cache (see above). */
+hipdecode_status hipdecode_kv_append(const hipdecode_append_params *params,
+                                     void *q,
+                                     const void *k_new,
+                                     const void *v_new,
+                                     const int32_t *new_start,
+                                     const int32_t *block_table,
+                                     const int32_t *context_lens,
+                                     void *k_pool,
+                                     void *v_pool,
+                                     void *stream);
 
 /* Static English text for a status code; never NULL. */
 const char *hipdecode_status_string(hipdecode_status status);

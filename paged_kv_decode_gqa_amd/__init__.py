@@ -1,7 +1,7 @@
 """Python binding of ``libhipdecode.so`` (the C ABI in ``include/hipdecode.h``).
 
-Argument marshalling only: every step of the attention runs in the library's
-HIP kernels.  The functions carry the C names; tensors are PyTorch device
+Argument marshalling only: every step of the attention and of the KV-cache
+append runs in the library's HIP kernels.  The functions carry the C names; tensors are PyTorch device
 tensors and are passed as raw pointers on the current HIP stream.
 
 If the library has not been built, importing works but every call raises
@@ -27,6 +27,8 @@ HIPDECODE_BF16 = 0
 HIPDECODE_F32 = 1
 HIPDECODE_SCHEDULE_SPLIT = 1
 HIPDECODE_SCHEDULE_STREAM = 2
+HIPDECODE_ROPE_NONE = 0
+HIPDECODE_ROPE_HALF = 1
 
 EXPORTED = (
     "hipdecode_abi_version",
@@ -37,6 +39,8 @@ EXPORTED = (
     "hipdecode_workspace_bytes",
     "hipdecode_workspace_init",
     "hipdecode_paged_attn",
+    "hipdecode_check_append_params",
+    "hipdecode_kv_append",
     "hipdecode_status_string",
 )
 
@@ -56,6 +60,22 @@ class hipdecode_params(ctypes.Structure):
         ("schedule", ctypes.c_int32),
         ("out_dtype", ctypes.c_int32),
         ("scale", ctypes.c_float),
+    ]
+
+
+class hipdecode_append_params(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("num_rows", ctypes.c_int32),
+        ("max_new_tokens", ctypes.c_int32),
+        ("rope", ctypes.c_int32),
+        ("rope_theta", ctypes.c_double),
     ]
 
 
@@ -94,6 +114,11 @@ def library() -> ctypes.CDLL:
     lib.hipdecode_workspace_init.restype = ctypes.c_int
     lib.hipdecode_paged_attn.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.hipdecode_paged_attn.restype = ctypes.c_int
+    PA = ctypes.POINTER(hipdecode_append_params)
+    lib.hipdecode_check_append_params.argtypes = [PA]
+    lib.hipdecode_check_append_params.restype = ctypes.c_int
+    lib.hipdecode_kv_append.argtypes = [PA, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.hipdecode_kv_append.restype = ctypes.c_int
     lib.hipdecode_status_string.argtypes = [ctypes.c_int]
     lib.hipdecode_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -107,6 +132,14 @@ def make_params(*, num_seqs, num_q_heads, num_kv_heads, num_pages, max_blocks_pe
                             int(page_size), int(num_pages), int(max_blocks_per_seq),
                             int(max_context_len), int(partition_tokens), int(workgroup_waves),
                             int(schedule), int(out_dtype), float(scale))
+
+
+def make_append_params(*, num_seqs, num_q_heads, num_kv_heads, num_pages, max_blocks_per_seq, num_rows,
+                       max_new_tokens=1, rope=HIPDECODE_ROPE_NONE, rope_theta=1e6, head_dim=128,
+                       page_size=16) -> hipdecode_append_params:
+    return hipdecode_append_params(int(num_seqs), int(num_q_heads), int(num_kv_heads), int(head_dim),
+                                   int(page_size), int(num_pages), int(max_blocks_per_seq), int(num_rows),
+                                   int(max_new_tokens), int(rope), float(rope_theta))
 
 
 def hipdecode_abi_version() -> int:
@@ -230,3 +263,62 @@ def paged_attn(q, k_pool, v_pool, block_table, context_lens, scale, *, max_conte
         workspace = torch.zeros(max(nbytes, 16) // 4 + 4, dtype=torch.int32, device=q.device)
     hipdecode_paged_attn(params, q, k_pool, v_pool, block_table, context_lens, out, lse, workspace)
     return out, lse
+
+
+def hipdecode_check_append_params(params: hipdecode_append_params | None) -> int:
+    return int(library().hipdecode_check_append_params(ctypes.byref(params) if params is not None else None))
+
+
+def hipdecode_kv_append(params: hipdecode_append_params, q, k_new, v_new, new_start, block_table,
+                        context_lens, k_pool, v_pool, stream=None) -> None:
+    """Enqueue one append on ``stream`` (default: torch's current stream).
+
+    ``q`` and ``new_start`` may be None.  Raises HipDecodeError on a non-OK
+    status."""
+    for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new), ("new_start", new_start),
+                    ("block_table", block_table), ("context_lens", context_lens), ("k_pool", k_pool),
+                    ("v_pool", v_pool)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    st = library().hipdecode_kv_append(ctypes.byref(params), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(new_start),
+                                       _ptr(block_table), _ptr(context_lens), _ptr(k_pool), _ptr(v_pool),
+                                       _stream_handle(stream))
+    if st != HIPDECODE_OK:
+        raise HipDecodeError(st, "hipdecode_kv_append")
+
+
+def kv_append(k_new, v_new, block_table, context_lens, k_pool, v_pool, *, q=None, new_start=None,
+              max_new_tokens=None, rope_theta=None):
+    """Write new tokens' K/V into the pools in place (rotating K and ``q`` by
+    RoPE when ``rope_theta`` is given).
+
+    k_new, v_new: bf16 [T,Hkv,128]; q: bf16 [T,Hq,128] or None; new_start:
+    int32 [B+1] or None (one row per request); block_table, context_lens and
+    the pools as for ``paged_attn``.  ``max_new_tokens`` bounds any request's
+    new tokens when ``new_start`` is given (default: T)."""
+    import torch
+    for name, t in (("k_new", k_new), ("v_new", v_new), ("k_pool", k_pool), ("v_pool", v_pool), ("q", q)):
+        if t is not None and t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bfloat16")
+    for name, t in (("block_table", block_table), ("context_lens", context_lens), ("new_start", new_start)):
+        if t is not None and t.dtype != torch.int32:
+            raise ValueError(f"{name} must be int32")
+    T, Hkv, D = k_new.shape
+    P, page, Hkv_p, D_p = k_pool.shape
+    if (Hkv_p, D_p) != (Hkv, D) or v_new.shape != k_new.shape or v_pool.shape != k_pool.shape:
+        raise ValueError("inconsistent K/V shapes")
+    if q is not None and (q.dim() != 3 or q.shape[0] != T or q.shape[2] != D):
+        raise ValueError("q must be [T, Hq, head_dim]")
+    Hq = q.shape[1] if q is not None else Hkv
+    B = context_lens.shape[0]
+    if new_start is not None and new_start.shape != (B + 1,):
+        raise ValueError("new_start must have num_seqs + 1 entries")
+    if max_new_tokens is None:
+        max_new_tokens = T if new_start is not None else 1
+    params = make_append_params(num_seqs=B, num_q_heads=Hq, num_kv_heads=Hkv, num_pages=P,
+                                max_blocks_per_seq=block_table.shape[1], num_rows=T,
+                                max_new_tokens=max_new_tokens,
+                                rope=HIPDECODE_ROPE_NONE if rope_theta is None else HIPDECODE_ROPE_HALF,
+                                rope_theta=1e6 if rope_theta is None else rope_theta,
+                                head_dim=D, page_size=page)
+    hipdecode_kv_append(params, q, k_new, v_new, new_start, block_table, context_lens, k_pool, v_pool)

@@ -5,8 +5,6 @@
 
 #include <math.h>
 
-#define HIPDECODE_API extern "C" __attribute__((visibility("default")))
-
 namespace hipdecode {
 namespace {
 
@@ -285,7 +283,7 @@ HIPDECODE_API const char *hipdecode_status_string(hipdecode_status status)
     case HIPDECODE_ERR_UNSUPPORTED: return "unsupported head_dim, page size, group size or dtype";
     case HIPDECODE_ERR_ALIGN: return "a buffer is not suitably aligned";
     case HIPDECODE_ERR_WORKSPACE: return "workspace smaller than hipdecode_workspace_bytes()";
-    case HIPDECODE_ERR_SCALE: return "scale is not finite";
+    case HIPDECODE_ERR_SCALE: return "scale is not finite, or rope_theta is not finite and positive";
     case HIPDECODE_ERR_HIP: return "the HIP runtime refused the launch";
     }
     return "unknown status";

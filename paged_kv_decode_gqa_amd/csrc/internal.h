@@ -5,6 +5,9 @@
 #include <stddef.h>
 #include <stdint.h>
 
+// Exported entry points of the C ABI; everything else has hidden visibility.
+#define HIPDECODE_API extern "C" __attribute__((visibility("default")))
+
 namespace hipdecode {
 
 constexpr int kHeadDim = 128;   // dims per head; a K or V row is 256 bytes

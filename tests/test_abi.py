@@ -210,3 +210,93 @@ def test_product_path_does_not_reach_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.lower(), f"{f} mentions the oracle"
+
+
+# --------------------------------------------------------------------------
+# KV-cache append
+# --------------------------------------------------------------------------
+def abase(**kw):
+    p = dict(num_seqs=16, num_q_heads=16, num_kv_heads=8, num_pages=28672, max_blocks_per_seq=1792,
+             num_rows=16, max_new_tokens=1, rope=hd.HIPDECODE_ROPE_HALF, rope_theta=1e6)
+    p.update(kw)
+    return hd.make_append_params(**p)
+
+
+def test_append_struct_layout_matches_header():
+    # 10 int32 fields then a double at offset 40
+    assert ctypes.sizeof(hd.hipdecode_append_params) == 48
+    assert hd.hipdecode_append_params.rope_theta.offset == 40
+
+
+APPEND_GOOD = [
+    {},
+    dict(num_seqs=0),
+    dict(num_rows=0),
+    dict(rope=hd.HIPDECODE_ROPE_NONE, rope_theta=float("nan")),   # theta unused without RoPE
+    dict(num_q_heads=8, num_kv_heads=8),
+    dict(num_q_heads=32, num_kv_heads=8),
+    dict(num_seqs=1, num_rows=4096, max_new_tokens=4096),
+    dict(rope_theta=10000.0),
+    dict(max_new_tokens=0),
+]
+
+APPEND_BAD = [
+    (dict(num_seqs=-1), hd.HIPDECODE_ERR_SHAPE),
+    (dict(num_q_heads=0), hd.HIPDECODE_ERR_SHAPE),
+    (dict(num_kv_heads=0), hd.HIPDECODE_ERR_SHAPE),
+    (dict(num_q_heads=12, num_kv_heads=8), hd.HIPDECODE_ERR_SHAPE),
+    (dict(num_pages=0), hd.HIPDECODE_ERR_SHAPE),
+    (dict(num_rows=-1), hd.HIPDECODE_ERR_SHAPE),
+    (dict(max_new_tokens=-1), hd.HIPDECODE_ERR_SHAPE),
+    (dict(max_blocks_per_seq=-1), hd.HIPDECODE_ERR_SHAPE),
+    (dict(head_dim=64), hd.HIPDECODE_ERR_UNSUPPORTED),
+    (dict(page_size=32), hd.HIPDECODE_ERR_UNSUPPORTED),
+    (dict(rope=2), hd.HIPDECODE_ERR_UNSUPPORTED),
+    (dict(rope_theta=float("nan")), hd.HIPDECODE_ERR_SCALE),
+    (dict(rope_theta=float("inf")), hd.HIPDECODE_ERR_SCALE),
+    (dict(rope_theta=0.0), hd.HIPDECODE_ERR_SCALE),
+    (dict(rope_theta=-1e6), hd.HIPDECODE_ERR_SCALE),
+    (dict(num_seqs=1 << 20, max_new_tokens=1 << 12), hd.HIPDECODE_ERR_SHAPE),
+]
+
+
+@pytest.mark.parametrize("kw", APPEND_GOOD, ids=lambda k: ",".join(f"{a}={b}" for a, b in k.items()) or "base")
+def test_check_append_params_accepts(kw):
+    assert hd.hipdecode_check_append_params(abase(**kw)) == hd.HIPDECODE_OK
+
+
+@pytest.mark.parametrize("kw,status", APPEND_BAD, ids=lambda x: str(x))
+def test_check_append_params_rejects(kw, status):
+    assert hd.hipdecode_check_append_params(abase(**kw)) == status
+
+
+def test_append_null_params():
+    assert hd.hipdecode_check_append_params(None) == hd.HIPDECODE_ERR_NULL
+
+
+def test_append_rejects_before_any_launch():
+    lib = hd.library()
+    p = abase()
+    fake = ctypes.c_void_p(1 << 20)          # never dereferenced: rejected on the host
+    odd = ctypes.c_void_p((1 << 20) + 2)
+    call = lib.hipdecode_kv_append
+    # NULL k_new
+    assert call(ctypes.byref(p), fake, None, fake, None, fake, fake, fake, fake, None) == hd.HIPDECODE_ERR_NULL
+    # NULL pool
+    assert call(ctypes.byref(p), fake, fake, fake, None, fake, fake, None, fake, None) == hd.HIPDECODE_ERR_NULL
+    # misaligned q, k_new, pool, table
+    assert call(ctypes.byref(p), odd, fake, fake, None, fake, fake, fake, fake, None) == hd.HIPDECODE_ERR_ALIGN
+    assert call(ctypes.byref(p), fake, odd, fake, None, fake, fake, fake, fake, None) == hd.HIPDECODE_ERR_ALIGN
+    assert call(ctypes.byref(p), fake, fake, fake, None, fake, fake, fake, odd, None) == hd.HIPDECODE_ERR_ALIGN
+    assert call(ctypes.byref(p), fake, fake, fake, None, ctypes.c_void_p((1 << 20) + 2), fake, fake, fake,
+                None) == hd.HIPDECODE_ERR_ALIGN
+    # one row per request needs num_rows >= num_seqs
+    few = abase(num_rows=15)
+    assert call(ctypes.byref(few), fake, fake, fake, None, fake, fake, fake, fake, None) == hd.HIPDECODE_ERR_SHAPE
+    # bad params before pointers; empty work needs no pointers
+    assert call(ctypes.byref(abase(head_dim=64)), None, None, None, None, None, None, None, None, None) \
+        == hd.HIPDECODE_ERR_UNSUPPORTED
+    for empty in (abase(num_seqs=0), abase(num_rows=0, num_seqs=0)):
+        assert call(ctypes.byref(empty), None, None, None, None, None, None, None, None, None) == hd.HIPDECODE_OK
+    zero_new = abase(max_new_tokens=0)
+    assert call(ctypes.byref(zero_new), None, None, None, fake, None, None, None, None, None) == hd.HIPDECODE_OK

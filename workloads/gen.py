@@ -314,3 +314,101 @@ def make_config(name: str, *, seed: int | None = None, threads: int | None = Non
     s = default_seed if seed is None else int(seed)
     rng_meta = np.random.default_rng([s, 0])
     return fn(rng_meta, s, threads)
+
+
+# --------------------------------------------------------------------------
+# KV-cache append: new tokens' K/V (and q) rows
+# --------------------------------------------------------------------------
+# Streams of an append: 4 = k_new, 5 = v_new, 6 = q rows, 7 = the compact
+# pool's page permutation.  RoPE theta 1e6 is the Qwen3 decoder's (audio.cpp
+# "Fun-ASR-Nano Native Runtime Design", "Decoder And Prompt").
+ROPE_THETA = 1e6
+
+
+@dataclasses.dataclass
+class AppendInputs:
+    """New rows for an append into some case's pool: row r of k_new/v_new/q."""
+    k_new: np.ndarray              # uint16 bf16 bits [T, Hkv, D]
+    v_new: np.ndarray              # uint16 bf16 bits [T, Hkv, D]
+    q: np.ndarray | None           # uint16 bf16 bits [T, Hq, D]
+    new_start: np.ndarray | None   # int32 [B + 1]; None: one row per request
+    max_new_tokens: int
+    theta: float = ROPE_THETA
+
+    @property
+    def rows(self) -> int:
+        return int(self.k_new.shape[0])
+
+
+def make_append_inputs(case: Case, new_lens=None, *, seed: int = 0, with_q: bool = True,
+                       extra_rows: int = 0, theta: float = ROPE_THETA) -> AppendInputs:
+    """Rows for appending to ``case``: ``new_lens[b]`` tokens for request b
+    (the last ones of its context), or one per request when ``new_lens`` is
+    None.  ``extra_rows`` spare rows that no request names are added at the end."""
+    B, Hkv, D, Hq = case.B, case.Hkv, case.D, case.Hq
+    if new_lens is None:
+        T = B
+        new_start = None
+        max_new = 1
+    else:
+        n = np.asarray(new_lens, dtype=np.int64).reshape(B)
+        if np.any(n < 0) or np.any(n > case.context_lens):
+            raise ValueError("new_lens must lie in [0, context_lens]")
+        new_start = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+        T = int(new_start[-1])
+        max_new = int(n.max()) if B else 0
+    T += int(extra_rows)
+
+    def draw(stream, heads):
+        x = np.random.default_rng([seed, stream]).standard_normal((T, heads, D), dtype=np.float32)
+        return f32_to_bf16_bits(x)
+
+    return AppendInputs(k_new=draw(4, Hkv), v_new=draw(5, Hkv), q=draw(6, Hq) if with_q else None,
+                        new_start=new_start, max_new_tokens=max_new, theta=theta)
+
+
+def make_append_case(ctx_lens, new_lens=None, *, seed: int = 0, Hq: int = HQ, Hkv: int = HKV,
+                     D: int = HEAD_DIM, page: int = PAGE, extra_pages: int = 0,
+                     name: str = "append") -> tuple[Case, AppendInputs]:
+    """A compact case for appends alone: the pool holds only the pages the new
+    tokens land in (plus ``extra_pages``), shuffled; table entries of earlier
+    blocks are -1, since an append reads only the blocks it writes."""
+    ctx = np.asarray([int(c) for c in ctx_lens], dtype=np.int32)
+    B = ctx.shape[0]
+    n = np.ones(B, dtype=np.int64) * (ctx > 0) if new_lens is None else np.asarray(new_lens, dtype=np.int64)
+    first = [(int(c) - int(k)) // page for c, k in zip(ctx, n)]
+    need = [((int(c) + page - 1) // page - f) if k > 0 else 0 for c, k, f in zip(ctx, n, first)]
+    max_blocks = max(1, max(((int(c) + page - 1) // page for c in ctx), default=1))
+    pool_pages = max(1, int(sum(need)) + int(extra_pages))
+    perm = np.random.default_rng([seed, 7]).permutation(pool_pages).astype(np.int32)
+    table = np.full((B, max_blocks), -1, dtype=np.int32)
+    off = 0
+    for b in range(B):
+        table[b, first[b]:first[b] + need[b]] = perm[off:off + need[b]]
+        off += need[b]
+    page_elems = page * Hkv * D
+    k_pool = _normal_pool_bits(seed, 2, pool_pages, page_elems, None).reshape(pool_pages, page, Hkv, D)
+    v_pool = _normal_pool_bits(seed, 3, pool_pages, page_elems, None).reshape(pool_pages, page, Hkv, D)
+    q = f32_to_bf16_bits(np.random.default_rng([seed, 1]).standard_normal((B, Hq, D), dtype=np.float32))
+    case = Case(name=name, q=q, k_pool=k_pool, v_pool=v_pool, block_table=table, context_lens=ctx,
+                scale=SCALE, out_dtype="bf16", seed=seed,
+                notes="compact pool: only the pages the appended tokens land in")
+    inputs = make_append_inputs(case, None if new_lens is None else n, seed=seed)
+    return case, inputs
+
+
+# Named append workloads.  a1: the decode step of the 16 x 28672 batch, one
+# new token per request.  a2: one 4096-token prefill chunk, the last of a
+# 28672-token context (MOSS-TD article, "Chunked prefill for long audio").
+APPEND_CONFIGS = {
+    "a1": (11, [28672] * 16, None),
+    "a2": (12, [28672], [4096]),
+}
+
+
+def make_append_config(name: str, *, copy: int = 0) -> tuple[Case, AppendInputs]:
+    """A named append workload; ``copy`` draws an independent instance."""
+    seed, ctx, new = APPEND_CONFIGS[name]
+    seed = seed * 1000 + int(copy)
+    case, inputs = make_append_case(ctx, new, seed=seed, name=f"{name}_{'decode' if new is None else 'chunk'}")
+    return case, inputs
