@@ -141,11 +141,19 @@ def main(argv=None) -> int:
         n = 1 << 28   # 2**28 float32 = 1 GiB read and 1 GiB written per copy
         src = torch.ones(n, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
         for _ in range(3):
             dst.copy_(src)
-        torch.cuda.synchronize()
+        e1.record()
+        e1.synchronize()
+        ms = e0.elapsed_time(e1) / 3
         print(json.dumps({"calibration": "device copy", "bytes_read_per_copy": 4 * n,
-                          "bytes_written_per_copy": 4 * n, "copies": 3}), flush=True)
+                          "bytes_written_per_copy": 4 * n, "copies": 4,
+                          "read_plus_write_GBps": round(8 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
         return 0
     hd.library()
     dev = torch.device("cuda:0")
@@ -345,11 +353,12 @@ def run_append(args, dev) -> int:
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
+    calls = [hd.PreparedAppend(params, d["q"], d["k_new"], d["v_new"], d["new_start"], d["table"], d["ctx"],
+                               d["k"], d["v"]) for d in dev_copies]
+
     def one_step():
         for layer in range(LAYERS):
-            d = dev_copies[layer % R]
-            hd.hipdecode_kv_append(params, d["q"], d["k_new"], d["v_new"], d["new_start"], d["table"], d["ctx"],
-                                   d["k"], d["v"])
+            calls[layer % R]()
 
     graph = None
     if args.graph:

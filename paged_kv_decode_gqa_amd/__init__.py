@@ -287,6 +287,28 @@ def hipdecode_kv_append(params: hipdecode_append_params, q, k_new, v_new, new_st
         raise HipDecodeError(st, "hipdecode_kv_append")
 
 
+class PreparedAppend:
+    """The marshalled argument list of one ``hipdecode_kv_append`` call,
+    invoked many times on the current stream (or ``stream``) without
+    re-marshalling; the tensors must stay alive and in place."""
+
+    def __init__(self, params, q, k_new, v_new, new_start, block_table, context_lens, k_pool, v_pool):
+        self._keep = (params, q, k_new, v_new, new_start, block_table, context_lens, k_pool, v_pool)
+        for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new), ("new_start", new_start),
+                        ("block_table", block_table), ("context_lens", context_lens), ("k_pool", k_pool),
+                        ("v_pool", v_pool)):
+            if t is not None and not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+        self._args = (ctypes.byref(params), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(new_start),
+                      _ptr(block_table), _ptr(context_lens), _ptr(k_pool), _ptr(v_pool))
+        self._fn = library().hipdecode_kv_append
+
+    def __call__(self, stream=None) -> None:
+        st = self._fn(*self._args, _stream_handle(stream))
+        if st != HIPDECODE_OK:
+            raise HipDecodeError(st, "hipdecode_kv_append")
+
+
 def kv_append(k_new, v_new, block_table, context_lens, k_pool, v_pool, *, q=None, new_start=None,
               max_new_tokens=None, rope_theta=None):
     """Write new tokens' K/V into the pools in place (rotating K and ``q`` by

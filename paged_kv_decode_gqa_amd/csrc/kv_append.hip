@@ -8,12 +8,17 @@
 // vLLM?").  RoPE with theta 1e6 belongs to the Qwen3 decoder (audio.cpp
 // "Fun-ASR-Nano Native Runtime Design", "Decoder And Prompt").
 //
-// One 256-thread workgroup per new token.  The token's 64 rotation angles
-// are evaluated once, in fp64, by the first wavefront and shared through LDS;
-// every thread then takes items of 16 per head: four dimension pairs of a K
-// or q head to rotate, or a 16-byte chunk of V (or of K, without RoPE) to
-// copy.  The work is a few KB per token, so the kernel is bound by HBM for
-// prefill chunks and by launch latency for one decode token per request.
+// Each new token is handled by one wavefront (four tokens per workgroup) or,
+// when there are few tokens, by all four wavefronts of a workgroup; no
+// workgroup barrier is used.  Lane l always works on dimension pairs
+// [4s, 4s+4) with s = l % 16 (and the pair partner i + 64 of each), so it needs
+// only four rotation angles; each wavefront evaluates the token's 64 angles in
+// fp64, lane i the angle of pair i, and shares them through its own slice of
+// LDS.  The input rows are loaded before the block table and the angles are
+// looked at, so those latencies overlap.  A rotated value is computed in fp64
+// and rounded once to bf16 (see round_to_odd_f32).  The work is a few KB per
+// token: HBM-bound for prefill chunks, latency-bound for one decode token per
+// request.
 #include "hipdecode.h"
 #include "internal.h"
 
@@ -22,11 +27,15 @@
 namespace hipdecode {
 namespace {
 
-constexpr int kAppendThreads = 256;
+constexpr int kAppendWaves = 4;                 // wavefronts per workgroup
+constexpr int kAppendThreads = 64 * kAppendWaves;
 constexpr int kHalfDim = kHeadDim / 2;          // rotation pairs per head
 constexpr int kPairsPerItem = 4;
 constexpr int kItemsPerHead = kHalfDim / kPairsPerItem;   // also the 16-byte chunks of one head's row
+constexpr int kRotPre = 6;    // rotation items loaded ahead per wavefront-token: 8 K heads + 16 q heads
+constexpr int kCopyPre = 4;   // 16-byte chunks loaded ahead: V (and K without RoPE) of 8 heads
 constexpr int64_t kMaxGrid = (int64_t)1 << 31;
+constexpr int64_t kFewTokens = 1024;            // up to this many, four wavefronts share each token
 
 struct AppendArgs {
     uint16_t *q;
@@ -43,66 +52,102 @@ struct AppendArgs {
     int32_t max_blocks;
     int32_t num_rows;
     int32_t max_new;
+    int32_t token_groups;   // workgroups per request: ceil(max_new / tokens per workgroup)
     double theta;
 };
 
-__device__ inline double widen_bf16(uint32_t bits16) { return (double)__uint_as_float(bits16 << 16); }
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-// Nearest bf16 of an fp64 value, ties to even, by rounding twice: first to
-// fp32 towards zero with a sticky last bit ("rounding to odd"), then to bf16
-// to nearest even.  fp32 keeps 16 more significand bits than bf16, which is
-// more than the two extra bits rounding to odd needs for the second rounding
-// to equal a direct one (Boldo and Melquiond, "Emulation of FMA and correctly
-// rounded sums: proved algorithms using rounding to odd", IEEE TC 2008).
-__device__ inline uint32_t round_bf16(double x)
+// fp64 -> fp32 rounded to odd: the fp32 number next to x towards zero, with
+// its last bit set when x is not exactly representable.  fp32 keeps 16 more
+// significand bits than bf16 (normal or subnormal alike, the exponent ranges
+// being the same), more than the two that rounding to odd needs for a second
+// rounding, to bf16 nearest even, to equal the direct one (Boldo and
+// Melquiond, "Emulation of FMA and correctly rounded sums: proved algorithms
+// using rounding to odd", IEEE Trans. Computers, 2008).  The hardware
+// conversion rounds to nearest; it is stepped back by one unit in the last
+// place when that went away from zero.
+__device__ inline float round_to_odd_f32(double x)
 {
-    if (x != x)
-        return 0x7FC0u;
-    const float t = __double2float_rz(x);
+    const float t = (float)x;
+    const double back = (double)t;
+    const bool inexact = back != x;
     uint32_t b = __float_as_uint(t);
-    if ((double)t != x)
-        b |= 1u;
-    b += 0x7FFFu + ((b >> 16) & 1u);
-    return b >> 16;
+    b -= (inexact && fabs(back) > fabs(x)) ? 1u : 0u;
+    b |= inexact ? 1u : 0u;
+    return __uint_as_float(b);
 }
 
-__device__ inline void copy16(const uint16_t *src, uint16_t *dst)
+// Nearest-even bf16 bits of x (low half) and y (high half); NaN gives 0x7FC0.
+__device__ inline uint32_t pack_bf16(double x, double y)
 {
-    *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
+    const f32x2_t v = {round_to_odd_f32(x), round_to_odd_f32(y)};
+    uint32_t u = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+    u = x != x ? (u & 0xFFFF0000u) | 0x7FC0u : u;
+    u = y != y ? (u & 0x0000FFFFu) | 0x7FC00000u : u;
+    return u;
 }
 
-// Rotates pairs [4s, 4s+4) of one head: dims 4s.. with dims 64+4s..
-__device__ inline void rotate_item(const uint16_t *src, uint16_t *dst, int s, const double (*cs)[2])
+__device__ inline uint4 load16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
+__device__ inline void store16(uint16_t *p, uint4 v) { *reinterpret_cast<uint4 *>(p) = v; }
+__device__ inline uint2 load8(const uint16_t *p) { return *reinterpret_cast<const uint2 *>(p); }
+__device__ inline void store8(uint16_t *p, uint2 v) { *reinterpret_cast<uint2 *>(p) = v; }
+
+// Rotates four pairs: element e of lo pairs with element e of hi.
+//
+// Fast rounding: t = fp32 nearest of the fp64 value y, then bf16 nearest even
+// of t.  Every bf16 rounding boundary (a midpoint between bf16 neighbours) is
+// an fp32 number and rounding is monotonic, so t lies on the same side of
+// each boundary as y unless t is itself a boundary; the two roundings then
+// agree with the direct one.  Items where some t is a boundary (low 16 bits
+// 0x8000, probability about 2^-16 per value) or NaN take the exact path.
+__device__ inline void rotate4(uint2 lo, uint2 hi, const double2 (&cs)[kPairsPerItem], uint2 &out_lo,
+                               uint2 &out_hi)
 {
-    const uint2 lo = *reinterpret_cast<const uint2 *>(src + kPairsPerItem * s);
-    const uint2 hi = *reinterpret_cast<const uint2 *>(src + kHalfDim + kPairsPerItem * s);
-    const uint32_t a[4] = {lo.x & 0xFFFFu, lo.x >> 16, lo.y & 0xFFFFu, lo.y >> 16};
-    const uint32_t b[4] = {hi.x & 0xFFFFu, hi.x >> 16, hi.y & 0xFFFFu, hi.y >> 16};
-    uint32_t ra[4], rb[4];
+    const uint32_t a[4] = {lo.x << 16, lo.x & 0xFFFF0000u, lo.y << 16, lo.y & 0xFFFF0000u};
+    const uint32_t b[4] = {hi.x << 16, hi.x & 0xFFFF0000u, hi.y << 16, hi.y & 0xFFFF0000u};
+    double y0[4], y1[4];
+    float t0[4], t1[4];
+    bool unsure = false;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const double c = cs[kPairsPerItem * s + e][0];
-        const double sn = cs[kPairsPerItem * s + e][1];
-        const double x0 = widen_bf16(a[e]);
-        const double x1 = widen_bf16(b[e]);
-        ra[e] = round_bf16(x0 * c - x1 * sn);
-        rb[e] = round_bf16(x1 * c + x0 * sn);
+        const double x0 = (double)__uint_as_float(a[e]);
+        const double x1 = (double)__uint_as_float(b[e]);
+        y0[e] = x0 * cs[e].x - x1 * cs[e].y;
+        y1[e] = x1 * cs[e].x + x0 * cs[e].y;
+        t0[e] = (float)y0[e];
+        t1[e] = (float)y1[e];
+        unsure |= (__float_as_uint(t0[e]) & 0xFFFFu) == 0x8000u || t0[e] != t0[e];
+        unsure |= (__float_as_uint(t1[e]) & 0xFFFFu) == 0x8000u || t1[e] != t1[e];
     }
-    *reinterpret_cast<uint2 *>(dst + kPairsPerItem * s) = make_uint2(ra[0] | (ra[1] << 16), ra[2] | (ra[3] << 16));
-    *reinterpret_cast<uint2 *>(dst + kHalfDim + kPairsPerItem * s) =
-        make_uint2(rb[0] | (rb[1] << 16), rb[2] | (rb[3] << 16));
+    if (__builtin_expect(unsure, 0)) {
+        out_lo = make_uint2(pack_bf16(y0[0], y0[1]), pack_bf16(y0[2], y0[3]));
+        out_hi = make_uint2(pack_bf16(y1[0], y1[1]), pack_bf16(y1[2], y1[3]));
+        return;
+    }
+    auto cvt = [](float x, float y) {
+        const f32x2_t v = {x, y};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+    };
+    out_lo = make_uint2(cvt(t0[0], t0[1]), cvt(t0[2], t0[3]));
+    out_hi = make_uint2(cvt(t1[0], t1[1]), cvt(t1[2], t1[3]));
 }
 
-template <bool ROPE, bool HAS_Q>
+// WPT: wavefronts per token, 1 or 4.
+template <bool ROPE, bool HAS_Q, int WPT>
 __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(AppendArgs a)
 {
-    __shared__ double cs[kHalfDim][2];
+    constexpr int kTokensPerGroup = kAppendWaves / WPT;
+    constexpr int kRot = (kRotPre + WPT - 1) / WPT;              // rotation items per lane loaded ahead
+    constexpr int kCopies = ((ROPE ? kCopyPre / 2 : kCopyPre) + WPT - 1) / WPT;
+    __shared__ double2 angles[kAppendWaves][kHalfDim];   // (cos, sin) of each pair, per wavefront
 
-    // Everything up to the rotation table is uniform across the workgroup,
-    // so the early returns leave no thread waiting at the barrier.
-    const int bid = blockIdx.x;
-    const int b = bid / a.max_new;
-    const int j = bid - b * a.max_new;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wt = w % WPT;                               // this wavefront's share of its token
+    const int b = blockIdx.x / a.token_groups;
+    const int j = (blockIdx.x - b * a.token_groups) * kTokensPerGroup + w / WPT;
     const int ctx = a.context_lens[b];
     int start, n;
     if (a.new_start != nullptr) {
@@ -113,55 +158,117 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(AppendArgs a)
         n = ctx > 0 ? 1 : 0;
     }
     // A request that breaks the contract (more new tokens than its context or
-    // the host bound, rows outside the inputs) writes nothing at all.
+    // the host bound, rows outside the inputs) writes nothing at all.  All of
+    // this is uniform across the wavefront, and nothing below waits for the
+    // other wavefronts, so a wavefront may leave on its own.
     if (j >= n || n > ctx || n > a.max_new || start < 0 || (int64_t)start + n > a.num_rows)
         return;
     const int pos = ctx - n + j;
+    const size_t row = (size_t)start + j;
+    const size_t kv_row = (size_t)a.num_kv_heads * kHeadDim;
+    const int kv_items = a.num_kv_heads * kItemsPerHead;
+    const int rot_items = (ROPE ? kv_items : 0) + (HAS_Q ? a.num_q_heads * kItemsPerHead : 0);
+    const int copy_items = (ROPE ? 0 : kv_items) + kv_items;
+    const int s = lane % kItemsPerHead;   // the same for every item of this lane
+
+    // Rotation item it: K head it / 16 (with RoPE), then q heads.  Copy item c:
+    // K 16-byte chunk c (without RoPE), then V chunks.
+    auto rot_src = [&](int it) -> const uint16_t * {
+        if (ROPE && it < kv_items)
+            return a.k_new + row * kv_row + (size_t)(it / kItemsPerHead) * kHeadDim;
+        return a.q + (row * a.num_q_heads + (it - (ROPE ? kv_items : 0)) / kItemsPerHead) * kHeadDim;
+    };
+    auto copy_src = [&](int c) -> const uint16_t * {
+        if (!ROPE && c < kv_items)
+            return a.k_new + row * kv_row + (size_t)c * 8;
+        return a.v_new + row * kv_row + (size_t)(c - (ROPE ? 0 : kv_items)) * 8;
+    };
+
+    // Item k of this lane is lane + 64 * (wt + WPT * k).  Loads are issued for
+    // every preloaded item without branches (indices past the end are clamped
+    // to the last item and their results dropped), copy chunks first, so the
+    // compiler can count them exactly and the angle evaluation below overlaps
+    // them.
+    auto item = [&](int k) { return lane + 64 * (wt + WPT * k); };
+    uint4 cp[kCopies];
+#pragma unroll
+    for (int k = 0; k < kCopies; ++k)
+        cp[k] = load16(copy_src(min(item(k), copy_items - 1)));
+    uint2 lo[kRot], hi[kRot];
+    if (ROPE) {
+#pragma unroll
+        for (int k = 0; k < kRot; ++k) {
+            const uint16_t *src = rot_src(min(item(k), rot_items - 1));
+            lo[k] = load8(src + kPairsPerItem * s);
+            hi[k] = load8(src + kHalfDim + kPairsPerItem * s);
+        }
+    }
+
     const int blk = pos / kPageSize;
     if (blk >= a.max_blocks)
         return;
     const int page = a.block_table[(size_t)b * a.max_blocks + blk];
     if ((unsigned)page >= (unsigned)a.num_pages)
         return;
-    const size_t row = (size_t)start + j;
     const size_t slot = (size_t)page * kPageSize + pos % kPageSize;
-
-    if (ROPE) {
-        if (threadIdx.x < kHalfDim) {
-            const int i = threadIdx.x;
-            const double freq = pow(a.theta, -2.0 * (double)i / (double)kHeadDim);
-            double sn, c;
-            sincos((double)pos * freq, &sn, &c);
-            cs[i][0] = c;
-            cs[i][1] = sn;
-        }
-        __syncthreads();
-    }
-
-    const size_t kv_row = (size_t)a.num_kv_heads * kHeadDim;
-    const uint16_t *kn = a.k_new + row * kv_row;
-    const uint16_t *vn = a.v_new + row * kv_row;
     uint16_t *kd = a.k_pool + slot * kv_row;
     uint16_t *vd = a.v_pool + slot * kv_row;
-    const int n_kv = a.num_kv_heads * kItemsPerHead;
-    const int n_q = HAS_Q ? a.num_q_heads * kItemsPerHead : 0;
-    const int total = 2 * n_kv + n_q;
-    for (int it = threadIdx.x; it < total; it += kAppendThreads) {
-        if (it < n_kv) {
-            if (ROPE) {
-                const int h = it / kItemsPerHead;
-                rotate_item(kn + h * kHeadDim, kd + h * kHeadDim, it % kItemsPerHead, cs);
-            } else {
-                copy16(kn + it * 8, kd + it * 8);
+    auto rot_dst = [&](int it) -> uint16_t * {
+        if (ROPE && it < kv_items)
+            return kd + (it / kItemsPerHead) * kHeadDim;
+        return a.q + (row * a.num_q_heads + (it - (ROPE ? kv_items : 0)) / kItemsPerHead) * kHeadDim;
+    };
+    auto copy_dst = [&](int c) -> uint16_t * {
+        if (!ROPE && c < kv_items)
+            return kd + c * 8;
+        return vd + (c - (ROPE ? 0 : kv_items)) * 8;
+    };
+
+    double2 cs[kPairsPerItem];
+    if (ROPE) {
+        // lane i: the angle of pair i, evaluated in fp64
+        const double freq = pow(a.theta, -2.0 * (double)lane / (double)kHeadDim);
+        double sn, c;
+        sincos((double)pos * freq, &sn, &c);
+        angles[w][lane] = make_double2(c, sn);
+        // LDS operations of one wavefront complete in order; this keeps the
+        // compiler from moving the reads above the write.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int e = 0; e < kPairsPerItem; ++e)
+            cs[e] = angles[w][kPairsPerItem * s + e];
+    }
+
+#pragma unroll
+    for (int k = 0; k < kCopies; ++k) {
+        const int c = item(k);
+        if (c < copy_items)
+            store16(copy_dst(c), cp[k]);
+    }
+    for (int c = item(kCopies); c < copy_items; c += 64 * WPT)
+        store16(copy_dst(c), load16(copy_src(c)));
+
+    if (ROPE) {
+#pragma unroll
+        for (int k = 0; k < kRot; ++k) {
+            const int it = item(k);
+            if (it < rot_items) {
+                uint2 ol, oh;
+                rotate4(lo[k], hi[k], cs, ol, oh);
+                uint16_t *dst = rot_dst(it);
+                store8(dst + kPairsPerItem * s, ol);
+                store8(dst + kHalfDim + kPairsPerItem * s, oh);
             }
-        } else if (it < 2 * n_kv) {
-            const int c = it - n_kv;
-            copy16(vn + c * 8, vd + c * 8);
-        } else if (HAS_Q) {
-            const int c = it - 2 * n_kv;
-            const int h = c / kItemsPerHead;
-            uint16_t *qh = a.q + (row * a.num_q_heads + h) * kHeadDim;
-            rotate_item(qh, qh, c % kItemsPerHead, cs);
+        }
+        for (int it = item(kRot); it < rot_items; it += 64 * WPT) {
+            const uint16_t *src = rot_src(it);
+            uint2 ol, oh;
+            rotate4(load8(src + kPairsPerItem * s), load8(src + kHalfDim + kPairsPerItem * s), cs, ol, oh);
+            uint16_t *dst = rot_dst(it);
+            store8(dst + kPairsPerItem * s, ol);
+            store8(dst + kHalfDim + kPairsPerItem * s, oh);
         }
     }
 }
@@ -185,7 +292,8 @@ hipdecode_status check_append(const hipdecode_append_params *pp)
         return HIPDECODE_ERR_SCALE;
     // rows and heads fit the 32-bit item arithmetic; the grid fits one dimension
     if ((int64_t)p.num_q_heads * kItemsPerHead > (int64_t)1 << 30 ||
-        (int64_t)p.num_seqs * (p.max_new_tokens > 0 ? p.max_new_tokens : 1) >= kMaxGrid)
+        (int64_t)p.num_seqs * (((int64_t)(p.max_new_tokens > 0 ? p.max_new_tokens : 1) + kAppendWaves - 1) /
+                               kAppendWaves) >= kMaxGrid)
         return HIPDECODE_ERR_SHAPE;
     return HIPDECODE_OK;
 }
@@ -242,14 +350,30 @@ HIPDECODE_API hipdecode_status hipdecode_kv_append(const hipdecode_append_params
     a.max_new = max_new;
     a.theta = p.rope_theta;
 
-    const dim3 grid((unsigned)((int64_t)p.num_seqs * max_new));
+    // Few tokens (a decode step): four wavefronts per token, for latency.
+    const bool few = (int64_t)p.num_seqs * max_new <= kFewTokens;
+    const int tokens_per_group = few ? 1 : kAppendWaves;
+    a.token_groups = (max_new + tokens_per_group - 1) / tokens_per_group;
+    const dim3 grid((unsigned)((int64_t)p.num_seqs * a.token_groups));
     const dim3 block(kAppendThreads);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (p.rope == HIPDECODE_ROPE_NONE)
-        hipLaunchKernelGGL((kv_append_kernel<false, false>), grid, block, 0, s, a);
-    else if (q == nullptr)
-        hipLaunchKernelGGL((kv_append_kernel<true, false>), grid, block, 0, s, a);
-    else
-        hipLaunchKernelGGL((kv_append_kernel<true, true>), grid, block, 0, s, a);
+    // the kernel's wavefronts per token must match tokens_per_group above
+    const bool rope = p.rope != HIPDECODE_ROPE_NONE;
+    const bool has_q = rope && q != nullptr;
+    if (few) {
+        if (!rope)
+            hipLaunchKernelGGL((kv_append_kernel<false, false, kAppendWaves>), grid, block, 0, s, a);
+        else if (!has_q)
+            hipLaunchKernelGGL((kv_append_kernel<true, false, kAppendWaves>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((kv_append_kernel<true, true, kAppendWaves>), grid, block, 0, s, a);
+    } else {
+        if (!rope)
+            hipLaunchKernelGGL((kv_append_kernel<false, false, 1>), grid, block, 0, s, a);
+        else if (!has_q)
+            hipLaunchKernelGGL((kv_append_kernel<true, false, 1>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((kv_append_kernel<true, true, 1>), grid, block, 0, s, a);
+    }
     return hipGetLastError() == hipSuccess ? HIPDECODE_OK : HIPDECODE_ERR_HIP;
 }

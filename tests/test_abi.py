@@ -238,6 +238,7 @@ APPEND_GOOD = [
     dict(num_seqs=1, num_rows=4096, max_new_tokens=4096),
     dict(rope_theta=10000.0),
     dict(max_new_tokens=0),
+    dict(num_seqs=1 << 20, max_new_tokens=1 << 12),     # 2^30 workgroups of four tokens
 ]
 
 APPEND_BAD = [
@@ -256,7 +257,7 @@ APPEND_BAD = [
     (dict(rope_theta=float("inf")), hd.HIPDECODE_ERR_SCALE),
     (dict(rope_theta=0.0), hd.HIPDECODE_ERR_SCALE),
     (dict(rope_theta=-1e6), hd.HIPDECODE_ERR_SCALE),
-    (dict(num_seqs=1 << 20, max_new_tokens=1 << 12), hd.HIPDECODE_ERR_SHAPE),
+    (dict(num_seqs=1 << 20, max_new_tokens=1 << 13), hd.HIPDECODE_ERR_SHAPE),   # 2^31 workgroups
 ]
 
 
