@@ -11,7 +11,9 @@ The arithmetic lives in C:
   and lse = ln(sum exp(scale * q K^T)) over the tokens a request's block table
   names, in fp64;
 - ``kv_append_oracle.c``: writing new tokens' K and V into their pages, with
-  optional RoPE on K and q, rotated in fp64 and rounded once to bf16.
+  optional RoPE on K and q, rotated in fp64 and rounded once to bf16;
+- ``prefill_attn_oracle.c``: chunked-prefill attention, each chunk row being
+  the decode definition over the cache up to its own position.
 """
 from __future__ import annotations
 
@@ -71,6 +73,14 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.oracle_kv_append.argtypes = [ctypes.POINTER(OracleShape), ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_double, p, p, p, p, p, p, p, p]
     lib.oracle_kv_append.restype = ctypes.c_int
+    lib.oracle_prefill_validate.argtypes = [ctypes.POINTER(OracleShape), ctypes.c_int32, p, p, p]
+    lib.oracle_prefill_validate.restype = ctypes.c_int
+    lib.oracle_prefill_attn.argtypes = [ctypes.POINTER(OracleShape), ctypes.c_int32, p, p, p, p, p, p,
+                                        ctypes.c_double, p, p]
+    lib.oracle_prefill_attn.restype = ctypes.c_int
+    lib.oracle_prefill_attn_pairs.argtypes = [ctypes.POINTER(OracleShape), ctypes.c_int32, p, p, p, p, p, p,
+                                              ctypes.c_double, p, ctypes.c_int32, p, p]
+    lib.oracle_prefill_attn_pairs.restype = ctypes.c_int
     _LIB_CACHE[path] = lib
     return lib
 
@@ -211,3 +221,63 @@ def kv_append_validate(k_new, block_table, context_lens, k_pool, *, new_start=No
                                                   new_start, None, None)
     return int(lib.oracle_kv_append_validate(ctypes.byref(shape), T, None if ns is None else ns.ctypes.data,
                                              table.ctypes.data, ctx.ctypes.data))
+
+
+def _prefill_prep(q, k_pool, v_pool, block_table, context_lens, new_start):
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    k_pool = np.ascontiguousarray(k_pool, dtype=np.uint16)
+    v_pool = np.ascontiguousarray(v_pool, dtype=np.uint16)
+    block_table = np.ascontiguousarray(block_table, dtype=np.int32)
+    context_lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    new_start = np.ascontiguousarray(new_start, dtype=np.int32)
+    if q.ndim != 3 or k_pool.ndim != 4 or k_pool.shape != v_pool.shape:
+        raise OracleError("q must be [T,Hq,D]; pools must be [P,page,Hkv,D] and equal in shape")
+    T, Hq, D = q.shape
+    P, page, Hkv, Dk = k_pool.shape
+    B = context_lens.shape[0]
+    if Dk != D or block_table.ndim != 2 or block_table.shape[0] != B or new_start.shape != (B + 1,):
+        raise OracleError("inconsistent shapes")
+    shape = OracleShape(B, Hq, Hkv, D, page, P, block_table.shape[1])
+    return shape, T, q, k_pool, v_pool, block_table, context_lens, new_start
+
+
+def prefill_attn(q, k_pool, v_pool, block_table, context_lens, new_start, scale, *,
+                 lib: ctypes.CDLL | None = None):
+    """fp64 (out [T,Hq,D], lse [T,Hq]) of every chunk row; rows no request
+    names are NaN."""
+    lib = lib or load()
+    shape, T, q, k_pool, v_pool, table, ctx, ns = _prefill_prep(q, k_pool, v_pool, block_table, context_lens,
+                                                                new_start)
+    out = np.full((T, shape.num_q_heads, shape.head_dim), np.nan, dtype=np.float64)
+    lse = np.full((T, shape.num_q_heads), np.nan, dtype=np.float64)
+    rc = lib.oracle_prefill_attn(ctypes.byref(shape), T, q.ctypes.data, k_pool.ctypes.data, v_pool.ctypes.data,
+                                 ns.ctypes.data, table.ctypes.data, ctx.ctypes.data, float(scale),
+                                 out.ctypes.data, lse.ctypes.data)
+    if rc != 0:
+        raise OracleError(f"oracle_prefill_attn returned {rc}")
+    return out, lse
+
+
+def prefill_attn_pairs(q, k_pool, v_pool, block_table, context_lens, new_start, scale, pairs, *,
+                       lib: ctypes.CDLL | None = None):
+    """fp64 (out [n,D], lse [n]) for the (row, query head) pairs listed."""
+    lib = lib or load()
+    shape, T, q, k_pool, v_pool, table, ctx, ns = _prefill_prep(q, k_pool, v_pool, block_table, context_lens,
+                                                                new_start)
+    pairs = np.ascontiguousarray(np.asarray(pairs, dtype=np.int32).reshape(-1, 2))
+    n = pairs.shape[0]
+    out = np.zeros((n, shape.head_dim), dtype=np.float64)
+    lse = np.zeros((n,), dtype=np.float64)
+    rc = lib.oracle_prefill_attn_pairs(ctypes.byref(shape), T, q.ctypes.data, k_pool.ctypes.data,
+                                       v_pool.ctypes.data, ns.ctypes.data, table.ctypes.data, ctx.ctypes.data,
+                                       float(scale), pairs.ctypes.data, n, out.ctypes.data, lse.ctypes.data)
+    if rc != 0:
+        raise OracleError(f"oracle_prefill_attn_pairs returned {rc}")
+    return out, lse
+
+
+def prefill_validate(q, k_pool, block_table, context_lens, new_start, *, lib: ctypes.CDLL | None = None) -> int:
+    lib = lib or load()
+    shape, T, _, _, _, table, ctx, ns = _prefill_prep(q, k_pool, k_pool, block_table, context_lens, new_start)
+    return int(lib.oracle_prefill_validate(ctypes.byref(shape), T, ns.ctypes.data, table.ctypes.data,
+                                           ctx.ctypes.data))

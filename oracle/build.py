@@ -15,7 +15,8 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "paged_attn_oracle.c")
 APPEND_SRC = os.path.join(HERE, "kv_append_oracle.c")
-SOURCES = [SRC, APPEND_SRC]
+PREFILL_SRC = os.path.join(HERE, "prefill_attn_oracle.c")
+SOURCES = [SRC, APPEND_SRC, PREFILL_SRC]
 LIB = os.path.join(HERE, "liboracle.so")
 CFLAGS = ["-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra"]
 

@@ -68,6 +68,17 @@ APPEND_MUTANTS = {
 }
 
 
+# Slips in the prefill oracle: the causal cut off by one, positions counted
+# from the chunk start, the query of the request instead of the row, the
+# first request's table row for everyone.
+PREFILL_MUTANTS = {
+    "cut_excludes_own_token": [("const int32_t visible = pos + 1;", "const int32_t visible = pos;")],
+    "positions_from_chunk_start": [("*pos_out = context_lens[b] - n + (r - start);", "*pos_out = r - start;")],
+    "query_of_request": [("q + (size_t)r * s->num_q_heads * s->head_dim", "q + (size_t)b * s->num_q_heads * s->head_dim")],
+    "first_table_row": [("block_table + (size_t)b * s->max_blocks, &visible", "block_table, &visible")],
+}
+
+
 def test_unmutated_copy_passes(tmp_path):
     lib = obuild.build_variant([], out_dir=str(tmp_path))
     r = subprocess.run([sys.executable, "-m", "tests.oracle_pins", "--lib", lib],
@@ -94,5 +105,20 @@ def test_unmutated_append_copy_passes(tmp_path):
 def test_append_mutant_is_caught(name, tmp_path):
     lib = obuild.build_variant(APPEND_MUTANTS[name], out_dir=str(tmp_path), source=obuild.APPEND_SRC)
     r = subprocess.run([sys.executable, "-m", "tests.oracle_append_pins", "--lib", lib],
+                       cwd=ROOT, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout}"
+
+
+def test_unmutated_prefill_copy_passes(tmp_path):
+    lib = obuild.build_variant([], out_dir=str(tmp_path), source=obuild.PREFILL_SRC)
+    r = subprocess.run([sys.executable, "-m", "tests.oracle_prefill_pins", "--lib", lib],
+                       cwd=ROOT, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stdout + r.stderr
+
+
+@pytest.mark.parametrize("name", sorted(PREFILL_MUTANTS))
+def test_prefill_mutant_is_caught(name, tmp_path):
+    lib = obuild.build_variant(PREFILL_MUTANTS[name], out_dir=str(tmp_path), source=obuild.PREFILL_SRC)
+    r = subprocess.run([sys.executable, "-m", "tests.oracle_prefill_pins", "--lib", lib],
                        cwd=ROOT, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout}"
