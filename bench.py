@@ -20,6 +20,10 @@ with RoPE on K and q): a step is 28 calls, one per layer, each writing the new
 tokens of workload a1 (one token for each of 16 requests) or a2 (one
 4096-token prefill chunk) into its own copy of the pools.
 
+``--op prefill`` measures chunked-prefill attention (``hipdecode_prefill_attn``)
+on workload p1 (the last 4096-token chunk of a 28672-token prompt) or p2 (the
+first chunk), against the bf16 dense matrix-core peak.
+
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -46,10 +50,13 @@ DECODE_SOURCES = ["paged_kv_decode_gqa_amd/csrc/paged_decode.hip",
                   "paged_kv_decode_gqa_amd/csrc/page_fold.h"]
 APPEND_SOURCES = ["paged_kv_decode_gqa_amd/csrc/kv_append.hip",
                   "paged_kv_decode_gqa_amd/csrc/internal.h"]
+PREFILL_SOURCES = ["paged_kv_decode_gqa_amd/csrc/prefill_attn.hip", "paged_kv_decode_gqa_amd/csrc/internal.h"]
 KERNEL_NAMES = {"split": "paged_decode_kernel", "stream": "paged_decode_stream_kernel"}
 KERNEL_SOURCES = {"paged_decode_kernel": DECODE_SOURCES, "paged_decode_stream_kernel": DECODE_SOURCES,
-                  "kv_append_kernel": APPEND_SOURCES}
+                  "kv_append_kernel": APPEND_SOURCES, "prefill_attn_kernel": PREFILL_SOURCES}
 APPEND_METRIC = "kv-cache append new tokens/s (RoPE on K and q) and achieved HBM GB/s"
+PREFILL_METRIC = "chunked-prefill attention tokens/s and achieved bf16 TFLOP/s"
+PEAK_BF16_TFLOPS = 2500.0
 
 
 def kernel_source_hash(kernel: str = "paged_decode_kernel") -> str:
@@ -105,14 +112,27 @@ def append_algorithmic_bytes(case, inputs) -> int:
     return int(T * (2 * kv + 2 * qb + 4) + 4 * case.B + offsets)
 
 
+def prefill_algorithmic_flops(case, inputs) -> int:
+    """Matrix flops the method needs: for every chunk row and query head,
+    2 * 128 for q.k and 2 * 128 for p.v per visible key (p + 1 keys)."""
+    total = 0
+    for b in range(case.B):
+        n = int(inputs.new_start[b + 1] - inputs.new_start[b])
+        c = int(case.context_lens[b])
+        first = c - n + 1                     # visible keys of the first row
+        total += (first + c) * n // 2         # sum of p + 1 over the chunk
+    return int(total * case.Hq * case.D * 4)
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--op", default="decode", choices=["decode", "append"])
+    ap.add_argument("--op", default="decode", choices=["decode", "append", "prefill"])
     ap.add_argument("--workload", default=None,
-                    help="decode: c1 c2 c3 c4 c5 c3b (default c4); append: a1 a2 (default a2)")
+                    help="decode: c1 c2 c3 c4 c5 c3b (default c4); append: a1 a2 (default a2); "
+                         "prefill: p1 p2 (default p1)")
     ap.add_argument("--partition", type=int, default=0, help="split-K partition tokens (0 = planner)")
     ap.add_argument("--waves", type=int, default=0, help="wavefronts per workgroup, 4 or 16 (0 = planner)")
     ap.add_argument("--schedule", type=int, default=0, help="1 = split, 2 = stream (0 = planner)")
@@ -160,6 +180,8 @@ def main(argv=None) -> int:
     torch.cuda.set_device(dev)
     if args.op == "append":
         return run_append(args, dev)
+    if args.op == "prefill":
+        return run_prefill(args, dev)
     args.workload = args.workload or "c4"
     if args.workload not in ("c1", "c2", "c3", "c4", "c5", "c3b"):
         print(f"unknown decode workload {args.workload}", file=sys.stderr)
@@ -448,6 +470,145 @@ def run_append(args, dev) -> int:
             "kind": "oracle",
             "sample": f"fp64 oracle append of the same {T} new tokens (copies of the pools included), "
                       f"{reps} run(s), {t_call * 1e3:.2f} ms per call",
+        }
+    result["setup_s"] = round(t_gen, 2)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def run_prefill(args, dev) -> int:
+    import numpy as np
+    import torch
+
+    import paged_kv_decode_gqa_amd as hd
+    from workloads import PREFILL_CONFIGS, make_prefill_config
+
+    name = args.workload or "p1"
+    if name not in PREFILL_CONFIGS:
+        print(f"unknown prefill workload {name}", file=sys.stderr)
+        return 2
+    t0 = time.time()
+    case, inp = make_prefill_config(name)
+    t_gen = time.time() - t0
+    flops = prefill_algorithmic_flops(case, inp)
+    kv_bytes = 2 * case.Hkv * case.D * 2 * case.total_tokens
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    R = args.rotate or max(2, min(LAYERS, math.ceil(ROTATE_MIN_BYTES / max(1, kv_bytes))))
+    k0, v0 = bf(case.k_pool), bf(case.v_pool)
+    pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(R - 1)]
+    q = bf(inp.q)
+    table = torch.from_numpy(case.block_table).to(dev)
+    ctx = torch.from_numpy(case.context_lens).to(dev)
+    ns = torch.from_numpy(inp.new_start).to(dev)
+    out = torch.empty((inp.rows, case.Hq, case.D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((inp.rows, case.Hq), dtype=torch.float32, device=dev)
+    params = hd.make_prefill_params(num_seqs=case.B, num_q_heads=case.Hq, num_kv_heads=case.Hkv,
+                                    num_pages=case.num_pages, max_blocks_per_seq=case.max_blocks,
+                                    num_rows=inp.rows, max_new_tokens=inp.max_new_tokens, scale=case.scale)
+    st = hd.hipdecode_check_prefill_params(params)
+    if st != 0:
+        raise hd.HipDecodeError(st, "prefill params")
+    calls = [hd.PreparedPrefill(params, q, kp, vp, ns, table, ctx, out, lse) for kp, vp in pools]
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def one_step():
+        for layer in range(LAYERS):
+            calls[layer % R]()
+
+    graph = None
+    if args.graph:
+        one_step()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            one_step()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+    run = graph.replay if graph is not None else one_step
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        run()
+    ev1.record(stream)
+    ev1.synchronize()
+    wall = time.perf_counter() - w0
+    ms = ev0.elapsed_time(ev1)
+    call_s = ms * 1e-3 / (args.steps * LAYERS)
+    T = int(inp.new_start[-1])
+    achieved = flops / call_s / 1e12
+    result = {
+        "metric": PREFILL_METRIC,
+        "value": round(T / call_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 q rows and KV pages, shuffled pools; no dataset)",
+        "config": {
+            "workload": case.name,
+            "batch": case.B,
+            "chunk_tokens": T,
+            "context": int(case.context_lens.max()),
+            "num_q_heads": case.Hq,
+            "num_kv_heads": case.Hkv,
+            "head_dim": case.D,
+            "page_size": case.page,
+            "layers_per_step": LAYERS,
+            "kv_pool_copies": R,
+            "mode": "hipgraph" if graph is not None else "eager",
+        },
+        "us_per_layer": round(call_s * 1e6, 3),
+        "wall_s_timed": round(wall, 4),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "prefill_attn_kernel",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "algorithmic_flops_per_launch": flops,
+            "avg_launch_us": round(call_s * 1e6, 3),
+        },
+        "cpu_baseline": None,
+    }
+    traffic = read_traffic("prefill_attn_kernel", name)
+    if traffic is not None:
+        result["roofline"]["traffic"] = round(traffic)
+    if not args.no_cpu_baseline:
+        import oracle
+        rng = np.random.default_rng(0)
+        rows = rng.integers(0, T, size=16)
+        pairs = [(int(r), int(h)) for r in rows for h in range(case.Hq)]
+        reps, t_cpu = 0, 0.0
+        while reps < 50 and (t_cpu < 10.0 or reps == 0):
+            c0 = time.perf_counter()
+            oracle.prefill_attn_pairs(inp.q, case.k_pool, case.v_pool, case.block_table, case.context_lens,
+                                      inp.new_start, case.scale, pairs)
+            t_cpu += time.perf_counter() - c0
+            reps += 1
+        t_rows = t_cpu / reps
+        result["cpu_baseline"] = {
+            "value": round(len(rows) / t_rows, 2),
+            "unit": "tokens/s",
+            "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"fp64 oracle over 16 random chunk rows x all {case.Hq} heads, {reps} run(s), "
+                      f"{t_rows:.3f} s per 16 rows",
         }
     result["setup_s"] = round(t_gen, 2)
     print(json.dumps(result), flush=True)

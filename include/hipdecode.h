@@ -221,6 +221,70 @@ hipdecode_status hipdecode_kv_append(const hipdecode_append_params *params,
                                      void *v_pool,
                                      void *stream);
 
+/* ------------------------------------------------------------------------
+ * Chunked-prefill attention.
+ *
+ * Prefill builds a long prompt's cache in chunks of query tokens (MOSS-TD
+ * article, "Chunked prefill for long audio": 4096-token blocks).  After a
+ * chunk's keys and values have been appended (hipdecode_kv_append, with the
+ * same row offsets), each chunk token attends causally to the cache up to its
+ * own position.  For request b with n_b chunk tokens and context length c_b
+ * (which counts them), chunk token j is at position p = c_b - n_b + j, its
+ * query is row r = new_start[b] + j, and for every query head h (KV head
+ * g = h / (num_q_heads / num_kv_heads)):
+ *     z_t      = scale * dot(q[r][h][:], K[page(b,t)][t % 16][g][:])   for t <= p
+ *     out[r][h] = sum_{t <= p} softmax(z)_t V[page(b,t)][t % 16][g][:]
+ *     lse[r][h] = ln sum_{t <= p} exp(z_t)
+ * which is the decode step of hipdecode_paged_attn for a context of p + 1.
+ * Rows no request names are not written.
+ *
+ * Layouts: q [num_rows][num_q_heads][128] bf16; out the same shape in
+ * out_dtype; lse [num_rows][num_q_heads] fp32, may be NULL; new_start
+ * [num_seqs + 1] int32; the rest as for hipdecode_paged_attn.  q, the pools
+ * and out must be 16-byte aligned.  Supported: head_dim 128, page size 16,
+ * G = num_q_heads / num_kv_heads in {1, 2, 4}.  No workspace; asynchronous on
+ * `stream`, graph-capturable.
+ *
+ * The matrix cores take softmax weights in bf16 (relative rounding 2^-9),
+ * so the output carries an absolute error of up to about 2^-9 times the
+ * largest |V| a row attends to; scores, the running sums and lse are fp32.
+ *
+ * Device-side contract as for the append: new_start non-decreasing, n_b <=
+ * min(c_b, max_new_tokens), rows within num_rows, c_b <= 16 *
+ * max_blocks_per_seq, blocks in the pool.  A request that breaks the first
+ * conditions writes nothing; pages outside the pool read as page 0, so memory
+ * outside the buffers is never touched.
+ * ------------------------------------------------------------------------ */
+
+typedef struct {
+    int32_t num_seqs;              /* B >= 0; B == 0 is a no-op */
+    int32_t num_q_heads;           /* Hq */
+    int32_t num_kv_heads;          /* Hkv; Hq / Hkv in {1, 2, 4} */
+    int32_t head_dim;              /* must be 128 */
+    int32_t page_size;             /* must be 16 */
+    int32_t num_pages;             /* P, rows of each pool */
+    int32_t max_blocks_per_seq;    /* row stride of block_table, >= 1 */
+    int32_t num_rows;              /* rows of q, out and lse */
+    int32_t max_new_tokens;        /* host upper bound of any n_b; sizes the grid */
+    int32_t out_dtype;             /* hipdecode_dtype */
+    float scale;                   /* applied to q.k */
+} hipdecode_prefill_params;
+
+/* Pure host check of a prefill parameter block. */
+hipdecode_status hipdecode_check_prefill_params(const hipdecode_prefill_params *params);
+
+/* Chunked-prefill attention over the paged cache (see above). */
+hipdecode_status hipdecode_prefill_attn(const hipdecode_prefill_params *params,
+                                        const void *q,
+                                        const void *k_pool,
+                                        const void *v_pool,
+                                        const int32_t *new_start,
+                                        const int32_t *block_table,
+                                        const int32_t *context_lens,
+                                        void *out,
+                                        float *lse,
+                                        void *stream);
+
 /* Static English text for a status code; never NULL. */
 const char *hipdecode_status_string(hipdecode_status status);
 

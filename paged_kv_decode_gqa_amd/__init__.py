@@ -1,7 +1,7 @@
 """Python binding of ``libhipdecode.so`` (the C ABI in ``include/hipdecode.h``).
 
-Argument marshalling only: every step of the attention and of the KV-cache
-append runs in the library's HIP kernels.  The functions carry the C names; tensors are PyTorch device
+Argument marshalling only: every step of the decode attention, the KV-cache
+append and the chunked-prefill attention runs in the library's HIP kernels.  The functions carry the C names; tensors are PyTorch device
 tensors and are passed as raw pointers on the current HIP stream.
 
 If the library has not been built, importing works but every call raises
@@ -41,6 +41,8 @@ EXPORTED = (
     "hipdecode_paged_attn",
     "hipdecode_check_append_params",
     "hipdecode_kv_append",
+    "hipdecode_check_prefill_params",
+    "hipdecode_prefill_attn",
     "hipdecode_status_string",
 )
 
@@ -76,6 +78,22 @@ class hipdecode_append_params(ctypes.Structure):
         ("max_new_tokens", ctypes.c_int32),
         ("rope", ctypes.c_int32),
         ("rope_theta", ctypes.c_double),
+    ]
+
+
+class hipdecode_prefill_params(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("num_rows", ctypes.c_int32),
+        ("max_new_tokens", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float),
     ]
 
 
@@ -119,6 +137,11 @@ def library() -> ctypes.CDLL:
     lib.hipdecode_check_append_params.restype = ctypes.c_int
     lib.hipdecode_kv_append.argtypes = [PA, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.hipdecode_kv_append.restype = ctypes.c_int
+    PP = ctypes.POINTER(hipdecode_prefill_params)
+    lib.hipdecode_check_prefill_params.argtypes = [PP]
+    lib.hipdecode_check_prefill_params.restype = ctypes.c_int
+    lib.hipdecode_prefill_attn.argtypes = [PP, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.hipdecode_prefill_attn.restype = ctypes.c_int
     lib.hipdecode_status_string.argtypes = [ctypes.c_int]
     lib.hipdecode_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -140,6 +163,14 @@ def make_append_params(*, num_seqs, num_q_heads, num_kv_heads, num_pages, max_bl
     return hipdecode_append_params(int(num_seqs), int(num_q_heads), int(num_kv_heads), int(head_dim),
                                    int(page_size), int(num_pages), int(max_blocks_per_seq), int(num_rows),
                                    int(max_new_tokens), int(rope), float(rope_theta))
+
+
+def make_prefill_params(*, num_seqs, num_q_heads, num_kv_heads, num_pages, max_blocks_per_seq, num_rows,
+                        max_new_tokens, scale, head_dim=128, page_size=16,
+                        out_dtype=HIPDECODE_BF16) -> hipdecode_prefill_params:
+    return hipdecode_prefill_params(int(num_seqs), int(num_q_heads), int(num_kv_heads), int(head_dim),
+                                    int(page_size), int(num_pages), int(max_blocks_per_seq), int(num_rows),
+                                    int(max_new_tokens), int(out_dtype), float(scale))
 
 
 def hipdecode_abi_version() -> int:
@@ -344,3 +375,72 @@ def kv_append(k_new, v_new, block_table, context_lens, k_pool, v_pool, *, q=None
                                 rope_theta=1e6 if rope_theta is None else rope_theta,
                                 head_dim=D, page_size=page)
     hipdecode_kv_append(params, q, k_new, v_new, new_start, block_table, context_lens, k_pool, v_pool)
+
+
+def hipdecode_check_prefill_params(params: hipdecode_prefill_params | None) -> int:
+    return int(library().hipdecode_check_prefill_params(ctypes.byref(params) if params is not None else None))
+
+
+def hipdecode_prefill_attn(params: hipdecode_prefill_params, q, k_pool, v_pool, new_start, block_table,
+                           context_lens, out, lse, stream=None) -> None:
+    """Enqueue one chunked-prefill attention call; ``lse`` may be None."""
+    for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool), ("new_start", new_start),
+                    ("block_table", block_table), ("context_lens", context_lens), ("out", out), ("lse", lse)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    st = library().hipdecode_prefill_attn(ctypes.byref(params), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                          _ptr(new_start), _ptr(block_table), _ptr(context_lens), _ptr(out),
+                                          _ptr(lse), _stream_handle(stream))
+    if st != HIPDECODE_OK:
+        raise HipDecodeError(st, "hipdecode_prefill_attn")
+
+
+class PreparedPrefill:
+    """The marshalled argument list of one ``hipdecode_prefill_attn`` call,
+    invoked many times without re-marshalling; tensors must stay in place."""
+
+    def __init__(self, params, q, k_pool, v_pool, new_start, block_table, context_lens, out, lse):
+        self._keep = (params, q, k_pool, v_pool, new_start, block_table, context_lens, out, lse)
+        self._args = (ctypes.byref(params), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(new_start),
+                      _ptr(block_table), _ptr(context_lens), _ptr(out), _ptr(lse))
+        self._fn = library().hipdecode_prefill_attn
+
+    def __call__(self, stream=None) -> None:
+        st = self._fn(*self._args, _stream_handle(stream))
+        if st != HIPDECODE_OK:
+            raise HipDecodeError(st, "hipdecode_prefill_attn")
+
+
+def prefill_attn(q, k_pool, v_pool, block_table, context_lens, new_start, scale, *, max_new_tokens=None,
+                 out_dtype=None, out=None, lse=None):
+    """Chunked-prefill attention: q bf16 [T,Hq,128] (row new_start[b] + j is
+    chunk token j of request b); returns (out [T,Hq,128], lse [T,Hq]).  Rows
+    no request names are left as allocated (uninitialised unless ``out`` and
+    ``lse`` are given)."""
+    import torch
+    if q.dtype != torch.bfloat16 or k_pool.dtype != torch.bfloat16 or v_pool.dtype != torch.bfloat16:
+        raise ValueError("q, k_pool and v_pool must be bfloat16")
+    for name, t in (("block_table", block_table), ("context_lens", context_lens), ("new_start", new_start)):
+        if t.dtype != torch.int32:
+            raise ValueError(f"{name} must be int32")
+    T, Hq, D = q.shape
+    P, page, Hkv, Dk = k_pool.shape
+    B = context_lens.shape[0]
+    if new_start.shape != (B + 1,):
+        raise ValueError("new_start must have num_seqs + 1 entries")
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else torch.bfloat16
+    params = make_prefill_params(num_seqs=B, num_q_heads=Hq, num_kv_heads=Hkv, num_pages=P,
+                                 max_blocks_per_seq=block_table.shape[1], num_rows=T,
+                                 max_new_tokens=T if max_new_tokens is None else max_new_tokens, scale=scale,
+                                 head_dim=D, page_size=page,
+                                 out_dtype=HIPDECODE_F32 if out_dtype == torch.float32 else HIPDECODE_BF16)
+    st = hipdecode_check_prefill_params(params)
+    if st != HIPDECODE_OK:
+        raise HipDecodeError(st, "hipdecode_check_prefill_params")
+    if out is None:
+        out = torch.empty((T, Hq, D), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
+    hipdecode_prefill_attn(params, q, k_pool, v_pool, new_start, block_table, context_lens, out, lse)
+    return out, lse

@@ -301,3 +301,74 @@ def test_append_rejects_before_any_launch():
         assert call(ctypes.byref(empty), None, None, None, None, None, None, None, None, None) == hd.HIPDECODE_OK
     zero_new = abase(max_new_tokens=0)
     assert call(ctypes.byref(zero_new), None, None, None, fake, None, None, None, None, None) == hd.HIPDECODE_OK
+
+
+# --------------------------------------------------------------------------
+# chunked-prefill attention
+# --------------------------------------------------------------------------
+def pbase(**kw):
+    p = dict(num_seqs=1, num_q_heads=16, num_kv_heads=8, num_pages=1792, max_blocks_per_seq=1792,
+             num_rows=4096, max_new_tokens=4096, scale=1 / math.sqrt(128))
+    p.update(kw)
+    return hd.make_prefill_params(**p)
+
+
+def test_prefill_struct_layout_matches_header():
+    # 10 int32 fields then a float
+    assert ctypes.sizeof(hd.hipdecode_prefill_params) == 44
+
+
+PREFILL_GOOD = [
+    {},
+    dict(num_seqs=0),
+    dict(num_rows=0),
+    dict(max_new_tokens=0),
+    dict(num_q_heads=8, num_kv_heads=8),
+    dict(num_q_heads=16, num_kv_heads=4),
+    dict(out_dtype=hd.HIPDECODE_F32),
+    dict(scale=-1.0),
+]
+
+PREFILL_BAD = [
+    (dict(num_seqs=-1), hd.HIPDECODE_ERR_SHAPE),
+    (dict(num_q_heads=0), hd.HIPDECODE_ERR_SHAPE),
+    (dict(num_q_heads=12, num_kv_heads=8), hd.HIPDECODE_ERR_SHAPE),
+    (dict(num_q_heads=16, num_kv_heads=2), hd.HIPDECODE_ERR_UNSUPPORTED),
+    (dict(head_dim=64), hd.HIPDECODE_ERR_UNSUPPORTED),
+    (dict(page_size=32), hd.HIPDECODE_ERR_UNSUPPORTED),
+    (dict(out_dtype=5), hd.HIPDECODE_ERR_UNSUPPORTED),
+    (dict(num_pages=0), hd.HIPDECODE_ERR_SHAPE),
+    (dict(max_blocks_per_seq=0), hd.HIPDECODE_ERR_SHAPE),
+    (dict(num_rows=-1), hd.HIPDECODE_ERR_SHAPE),
+    (dict(max_new_tokens=-1), hd.HIPDECODE_ERR_SHAPE),
+    (dict(scale=float("nan")), hd.HIPDECODE_ERR_SCALE),
+    (dict(num_seqs=1 << 20, max_new_tokens=1 << 20), hd.HIPDECODE_ERR_SHAPE),
+]
+
+
+@pytest.mark.parametrize("kw", PREFILL_GOOD, ids=lambda k: ",".join(f"{a}={b}" for a, b in k.items()) or "base")
+def test_check_prefill_params_accepts(kw):
+    assert hd.hipdecode_check_prefill_params(pbase(**kw)) == hd.HIPDECODE_OK
+
+
+@pytest.mark.parametrize("kw,status", PREFILL_BAD, ids=lambda x: str(x))
+def test_check_prefill_params_rejects(kw, status):
+    assert hd.hipdecode_check_prefill_params(pbase(**kw)) == status
+
+
+def test_prefill_rejects_before_any_launch():
+    lib = hd.library()
+    p = pbase()
+    fake = ctypes.c_void_p(1 << 20)
+    odd = ctypes.c_void_p((1 << 20) + 2)
+    call = lib.hipdecode_prefill_attn
+    assert hd.hipdecode_check_prefill_params(None) == hd.HIPDECODE_ERR_NULL
+    assert call(ctypes.byref(p), None, fake, fake, fake, fake, fake, fake, fake, None) == hd.HIPDECODE_ERR_NULL
+    assert call(ctypes.byref(p), fake, fake, fake, None, fake, fake, fake, fake, None) == hd.HIPDECODE_ERR_NULL
+    assert call(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None, fake, None) == hd.HIPDECODE_ERR_NULL
+    assert call(ctypes.byref(p), odd, fake, fake, fake, fake, fake, fake, fake, None) == hd.HIPDECODE_ERR_ALIGN
+    assert call(ctypes.byref(p), fake, fake, fake, fake, fake, fake, odd, fake, None) == hd.HIPDECODE_ERR_ALIGN
+    assert call(ctypes.byref(pbase(head_dim=64)), None, None, None, None, None, None, None, None, None) \
+        == hd.HIPDECODE_ERR_UNSUPPORTED
+    assert call(ctypes.byref(pbase(num_seqs=0)), None, None, None, None, None, None, None, None, None) \
+        == hd.HIPDECODE_OK

@@ -1,0 +1,175 @@
+"""GPU parity of chunked-prefill attention against the fp64 oracle, through the
+C ABI.
+
+Tolerances: max |out - oracle| <= 1e-2 (bf16 and fp32 outputs) and
+|lse - oracle| <= 1e-4 * max(1, |oracle|).  The matrix cores take the softmax
+weights in bf16, so unlike the decode kernel the outputs are not at bf16
+rounding level: each weight carries a relative error of up to 2^-9, which
+bounds the output error by about 2^-9 times the largest |V| a row attends to
+(here about 5, so under 1e-2); the tests also report the mean error.
+Rows that no request names must be left exactly as they were.
+"""
+from __future__ import annotations
+
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_decode_gqa_amd as hd
+from tests.gpu_util import DeviceCase, bits_to_bf16, compare, log, run_hip
+from workloads import make_append_inputs, make_case, make_prefill_case, make_prefill_config
+
+pytestmark = pytest.mark.gpu
+
+OUT_ATOL = 1e-2
+LSE_RTOL = 1e-4
+SENTINEL = 7.0
+
+
+def i32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+
+def run_gpu(case, inp, *, out_dtype=torch.bfloat16, dc=None, q=None, max_new=None):
+    dc = dc or DeviceCase(case)
+    q = q if q is not None else bits_to_bf16(inp.q)
+    T = q.shape[0]
+    out = torch.full((T, case.Hq, case.D), SENTINEL, dtype=out_dtype, device="cuda")
+    lse = torch.full((T, case.Hq), SENTINEL, dtype=torch.float32, device="cuda")
+    hd.prefill_attn(q, dc.k, dc.v, dc.table, dc.ctx, i32(inp.new_start), case.scale,
+                    max_new_tokens=max_new or inp.max_new_tokens, out=out, lse=lse)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def named_rows(new_start, T):
+    named = np.zeros(T, dtype=bool)
+    for b in range(len(new_start) - 1):
+        named[new_start[b]:new_start[b + 1]] = True
+    return named
+
+
+def check_rows(o, l, ref_o, ref_l, what):
+    err = np.abs(o - ref_o)
+    assert np.all(np.isfinite(o)), f"{what}: non-finite output"
+    max_err = float(err.max()) if err.size else 0.0
+    assert max_err <= OUT_ATOL, f"{what}: max |out err| {max_err}"
+    lerr = np.abs(l - ref_l) / np.maximum(1.0, np.abs(ref_l))
+    assert np.all(lerr <= LSE_RTOL), f"{what}: lse err {float(lerr.max())}"
+    log(f"[prefill] {what}: max|dout|={max_err:.2e} mean|dout|={float(err.mean()):.2e} "
+        f"max rel dlse={float(lerr.max()):.2e}")
+    return max_err
+
+
+def check_full(case, inp, o, l, what):
+    ref_o, ref_l = oracle.prefill_attn(inp.q, case.k_pool, case.v_pool, case.block_table, case.context_lens,
+                                       inp.new_start, case.scale)
+    named = named_rows(inp.new_start, inp.rows)
+    check_rows(o[named], l[named], ref_o[named], ref_l[named], what)
+    assert np.all(o[~named] == SENTINEL) and np.all(l[~named] == SENTINEL), f"{what}: an unnamed row was written"
+
+
+RAGGED = [(300, 300), (1000, 64), (77, 5), (16, 16), (33, 1), (130, 129), (64, 0)]
+
+
+def test_prefill_ragged_chunks():
+    ctx = [c for c, _ in RAGGED]
+    new = [n for _, n in RAGGED]
+    case, inp = make_prefill_case(ctx, new, seed=41, extra_rows=3)
+    o, l = run_gpu(case, inp)
+    check_full(case, inp, o, l, "ragged chunks")
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 4), (4, 1), (32, 16)])
+def test_prefill_group_shapes(hq, hkv):
+    case, inp = make_prefill_case([200, 70, 513], [200, 33, 129], seed=42, Hq=hq, Hkv=hkv)
+    o, l = run_gpu(case, inp)
+    check_full(case, inp, o, l, f"{hq}/{hkv}")
+
+
+def test_prefill_fp32_out():
+    case, inp = make_prefill_case([450, 97], [160, 97], seed=43)
+    o, l = run_gpu(case, inp, out_dtype=torch.float32)
+    check_full(case, inp, o, l, "fp32 out")
+
+
+def sampled_pairs(inp, Hq, rng, extra=48):
+    T = inp.rows
+    rows = [0, 1, 31, 32, 63, 64, 127, 128, T // 2, T - 2, T - 1]
+    pairs = [(r, h) for r in rows for h in (0, 1, Hq // 2, Hq - 1)]
+    pairs += [(int(rng.integers(T)), int(rng.integers(Hq))) for _ in range(extra)]
+    return pairs
+
+
+@pytest.mark.parametrize("name", ["p1", "p2"])
+def test_prefill_named_workloads_sampled(name):
+    case, inp = make_prefill_config(name)
+    log(f"[prefill] {name}: {case.name} rows={inp.rows}")
+    o, l = run_gpu(case, inp)
+    pairs = sampled_pairs(inp, case.Hq, np.random.default_rng(44))
+    ref_o, ref_l = oracle.prefill_attn_pairs(inp.q, case.k_pool, case.v_pool, case.block_table,
+                                             case.context_lens, inp.new_start, case.scale, pairs)
+    idx = np.array(pairs)
+    check_rows(o[idx[:, 0], idx[:, 1]], l[idx[:, 0], idx[:, 1]], ref_o, ref_l, f"{name} sampled")
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l)), f"{name}: non-finite rows"
+
+
+def test_prefill_last_rows_match_decode_kernel():
+    """The last row of each chunk sees the whole context: the decode kernel on
+    that query must agree."""
+    case, inp = make_prefill_case([3000, 517, 16], [256, 100, 16], seed=45)
+    dc = DeviceCase(case)
+    o, l = run_gpu(case, inp, dc=dc)
+    last = inp.new_start[1:] - 1
+    dc.q = bits_to_bf16(inp.q[last])
+    d_out, d_lse = run_hip(dc)
+    d_o = d_out.float().cpu().numpy()
+    d_l = d_lse.cpu().numpy()
+    assert np.abs(o[last] - d_o).max() <= 2 * OUT_ATOL
+    assert np.all(np.abs(l[last] - d_l) <= 2 * LSE_RTOL * np.maximum(1.0, np.abs(d_l)))
+
+
+def test_prefill_skips_what_breaks_the_contract():
+    case, inp = make_prefill_case([100, 50, 40], [20, 10, 40], seed=46)
+    ctx_bad = case.context_lens.copy()
+    ctx_bad[1] = 5                                   # 10 chunk tokens, context 5
+    broken = replace(case, context_lens=ctx_bad)
+    o, l = run_gpu(broken, inp)
+    ok_rows = np.r_[0:20, 30:70]
+    ref_o, ref_l = oracle.prefill_attn(inp.q, case.k_pool, case.v_pool, case.block_table, case.context_lens,
+                                       inp.new_start, case.scale)
+    check_rows(o[ok_rows], l[ok_rows], ref_o[ok_rows], ref_l[ok_rows], "valid requests")
+    assert np.all(o[20:30] == SENTINEL) and np.all(l[20:30] == SENTINEL), "a broken request wrote rows"
+
+
+def test_chunked_prefill_pipeline_with_append():
+    """A 700-token prompt in chunks of 256, 256 and 188: each chunk's K/V are
+    appended with RoPE (K and the chunk's q rotated), then the chunk attends;
+    every chunk's rows against the oracle doing the same two steps."""
+    total = 700
+    chunks = [256, 256, 188]
+    case = make_case([total], seed=47, pool_pages=50)
+    dc = DeviceCase(case)
+    k_ref, v_ref = case.k_pool.copy(), case.v_pool.copy()
+    done = 0
+    for i, n in enumerate(chunks):
+        done += n
+        ctx = np.array([done], dtype=np.int32)
+        sub = replace(case, context_lens=ctx)
+        rows = make_append_inputs(sub, [n], seed=470 + i)
+        ns = i32(rows.new_start)
+        ctx_d = i32(ctx)
+        q = bits_to_bf16(rows.q)
+        hd.kv_append(bits_to_bf16(rows.k_new), bits_to_bf16(rows.v_new), dc.table, ctx_d, dc.k, dc.v, q=q,
+                     new_start=ns, max_new_tokens=n, rope_theta=rows.theta)
+        out = torch.empty((n, case.Hq, case.D), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((n, case.Hq), dtype=torch.float32, device="cuda")
+        hd.prefill_attn(q, dc.k, dc.v, dc.table, ctx_d, ns, case.scale, max_new_tokens=n, out=out, lse=lse)
+        torch.cuda.synchronize()
+        k_ref, v_ref, q_rot = oracle.kv_append(rows.k_new, rows.v_new, case.block_table, ctx, k_ref, v_ref,
+                                               new_start=rows.new_start, q=rows.q, rope=True, theta=rows.theta)
+        ref_o, ref_l = oracle.prefill_attn(q_rot, k_ref, v_ref, case.block_table, ctx, rows.new_start, case.scale)
+        check_rows(out.float().cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, f"pipeline chunk {i}")

@@ -7,9 +7,11 @@ and the HIP library are fed from here, and neither imports the other.
 from .gen import (  # noqa: F401
     APPEND_CONFIGS,
     CONFIGS,
+    PREFILL_CONFIGS,
     ROPE_THETA,
     AppendInputs,
     Case,
+    PrefillInputs,
     bf16_bits_to_f32,
     f32_to_bf16_bits,
     make_append_case,
@@ -17,4 +19,6 @@ from .gen import (  # noqa: F401
     make_append_inputs,
     make_case,
     make_config,
+    make_prefill_case,
+    make_prefill_config,
 )

@@ -412,3 +412,45 @@ def make_append_config(name: str, *, copy: int = 0) -> tuple[Case, AppendInputs]
     seed = seed * 1000 + int(copy)
     case, inputs = make_append_case(ctx, new, seed=seed, name=f"{name}_{'decode' if new is None else 'chunk'}")
     return case, inputs
+
+
+# --------------------------------------------------------------------------
+# Chunked prefill: query rows of a chunk over a filled cache
+# --------------------------------------------------------------------------
+@dataclasses.dataclass
+class PrefillInputs:
+    """Chunk query rows for a case whose cache already holds the chunk's K/V."""
+    q: np.ndarray               # uint16 bf16 bits [T, Hq, D]
+    new_start: np.ndarray       # int32 [B + 1]
+    max_new_tokens: int
+
+    @property
+    def rows(self) -> int:
+        return int(self.q.shape[0])
+
+
+def make_prefill_case(ctx_lens, new_lens, *, seed: int = 0, Hq: int = HQ, Hkv: int = HKV,
+                      pool_pages: int | None = None, max_blocks: int | None = None, extra_rows: int = 0,
+                      threads: int | None = None, name: str = "prefill") -> tuple[Case, PrefillInputs]:
+    """A full cache (``make_case``) and the query rows of one chunk per
+    request: the last ``new_lens[b]`` tokens of request b's context.  The
+    rows come from the append generator's q stream."""
+    case = make_case(ctx_lens, seed=seed, Hq=Hq, Hkv=Hkv, pool_pages=pool_pages, max_blocks=max_blocks,
+                     threads=threads, name=name)
+    rows = make_append_inputs(case, new_lens, seed=seed, extra_rows=extra_rows)
+    return case, PrefillInputs(q=rows.q, new_start=rows.new_start, max_new_tokens=rows.max_new_tokens)
+
+
+# Named prefill workloads (MOSS-TD article, "Chunked prefill for long audio":
+# 4096-token query blocks).  p1: the last chunk of a 28672-token prompt, the
+# heaviest; p2: the first chunk, a causal triangle.
+PREFILL_CONFIGS = {
+    "p1": (21, [28672], [4096]),
+    "p2": (22, [4096], [4096]),
+}
+
+
+def make_prefill_config(name: str, *, threads: int | None = None) -> tuple[Case, PrefillInputs]:
+    seed, ctx, new = PREFILL_CONFIGS[name]
+    label = {"p1": "p1_last_chunk_of_28672", "p2": "p2_first_chunk_4096"}[name]
+    return make_prefill_case(ctx, new, seed=seed, threads=threads, name=label)
