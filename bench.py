@@ -24,6 +24,11 @@ tokens of workload a1 (one token for each of 16 requests) or a2 (one
 on workload p1 (the last 4096-token chunk of a 28672-token prompt) or p2 (the
 first chunk), against the bf16 dense matrix-core peak.
 
+``--op step`` measures the graph-replayed decode step (``hipdecode_step_runner``:
+per layer, append with RoPE and attention, one captured graph per batch
+bucket) on the launch-bound shapes s1 (one request at 512 tokens) and s2 (16
+requests of 200-420 tokens), against the same 2 x 28 launches issued eagerly.
+
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -129,10 +134,10 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--op", default="decode", choices=["decode", "append", "prefill"])
+    ap.add_argument("--op", default="decode", choices=["decode", "append", "prefill", "step"])
     ap.add_argument("--workload", default=None,
                     help="decode: c1 c2 c3 c4 c5 c3b (default c4); append: a1 a2 (default a2); "
-                         "prefill: p1 p2 (default p1)")
+                         "prefill: p1 p2 (default p1); step: s1 s2 (default s2)")
     ap.add_argument("--partition", type=int, default=0, help="split-K partition tokens (0 = planner)")
     ap.add_argument("--waves", type=int, default=0, help="wavefronts per workgroup, 4 or 16 (0 = planner)")
     ap.add_argument("--schedule", type=int, default=0, help="1 = split, 2 = stream (0 = planner)")
@@ -182,6 +187,8 @@ def main(argv=None) -> int:
         return run_append(args, dev)
     if args.op == "prefill":
         return run_prefill(args, dev)
+    if args.op == "step":
+        return run_step(args, dev)
     args.workload = args.workload or "c4"
     if args.workload not in ("c1", "c2", "c3", "c4", "c5", "c3b"):
         print(f"unknown decode workload {args.workload}", file=sys.stderr)
@@ -472,6 +479,128 @@ def run_append(args, dev) -> int:
                       f"{reps} run(s), {t_call * 1e3:.2f} ms per call",
         }
     result["setup_s"] = round(t_gen, 2)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+STEP_WORKLOADS = {"s1": "c1", "s2": "c2"}   # decode shapes whose steps are launch-bound
+STEP_METRIC = "decode-step tokens/s, graph-replayed append + attention over 28 layers"
+
+
+def run_step(args, dev) -> int:
+    import numpy as np
+    import torch
+
+    import paged_kv_decode_gqa_amd as hd
+    from workloads import ROPE_THETA, make_append_inputs, make_config
+
+    name = args.workload or "s2"
+    if name not in STEP_WORKLOADS:
+        print(f"unknown step workload {name}", file=sys.stderr)
+        return 2
+    t0 = time.time()
+    case = make_config(STEP_WORKLOADS[name])
+    rows = make_append_inputs(case, None, seed=99)
+    t_gen = time.time() - t0
+    B = case.B
+    bucket = hd.hipdecode_step_bucket(B, B)
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def pad(t, n):
+        out = torch.zeros((n,) + tuple(t.shape[1:]), dtype=t.dtype, device=dev)
+        out[: t.shape[0]].copy_(t)
+        return out
+
+    k0, v0 = bf(case.k_pool), bf(case.v_pool)
+    q0, kn, vn = bf(rows.q), bf(rows.k_new), bf(rows.v_new)
+    layers = []
+    for _ in range(LAYERS):          # every layer its own pools and rows
+        layers.append(dict(k_pool=k0.clone(), v_pool=v0.clone(), q=pad(q0, bucket), k_new=pad(kn, bucket),
+                           v_new=pad(vn, bucket),
+                           out=torch.empty((bucket, case.Hq, case.D), dtype=torch.bfloat16, device=dev),
+                           lse=torch.empty((bucket, case.Hq), dtype=torch.float32, device=dev)))
+    table = pad(torch.from_numpy(case.block_table).to(dev), bucket)
+    ctx_dev = pad(torch.from_numpy(case.context_lens).to(dev), bucket)
+    ctx_host = case.context_lens.copy()
+    runner = hd.StepRunner(layers, table, ctx_dev, max_seqs=B, num_pages=case.num_pages,
+                           max_context_len=case.max_context_len, scale=case.scale, rope_theta=ROPE_THETA)
+    # the same launches, issued eagerly
+    aparams = hd.make_append_params(num_seqs=bucket, num_q_heads=case.Hq, num_kv_heads=case.Hkv,
+                                    num_pages=case.num_pages, max_blocks_per_seq=case.max_blocks, num_rows=bucket,
+                                    rope=hd.HIPDECODE_ROPE_HALF, rope_theta=ROPE_THETA)
+    params = hd.make_params(num_seqs=bucket, num_q_heads=case.Hq, num_kv_heads=case.Hkv, num_pages=case.num_pages,
+                            max_blocks_per_seq=case.max_blocks, max_context_len=case.max_context_len,
+                            scale=case.scale)
+    ws = torch.zeros(hd.hipdecode_workspace_bytes(params) // 4 + 4, dtype=torch.int32, device=dev)
+    eager = []
+    for d in layers:
+        eager.append(hd.PreparedAppend(aparams, d["q"], d["k_new"], d["v_new"], None, table, ctx_dev, d["k_pool"],
+                                       d["v_pool"]))
+        eager.append(hd.PreparedCall(params, d["q"], d["k_pool"], d["v_pool"], table, ctx_dev, d["out"], d["lse"], ws))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    def eager_step():
+        for c in eager:
+            c()
+
+    ms_eager = timed(eager_step)
+    ms_graph = timed(lambda: runner.step(ctx_host))
+    runner.close()
+    kv_bytes = 2 * case.Hkv * case.D * 2 * case.total_tokens * LAYERS
+    achieved = kv_bytes / (ms_graph * 1e-3) / 1e9
+    result = {
+        "metric": STEP_METRIC,
+        "value": round(B / (ms_graph * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_graph, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 rows and KV pages; no dataset)",
+        "config": {
+            "workload": f"{name}_{case.name}",
+            "batch": B,
+            "bucket": bucket,
+            "layers_per_step": LAYERS,
+            "context_tokens_total": case.total_tokens,
+            "rope_theta": ROPE_THETA,
+            "mode": "hip graph per bucket (step runner)",
+        },
+        "eager_ms_per_step": round(ms_eager, 4),
+        "speedup_vs_eager": round(ms_eager / ms_graph, 3),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "paged_decode_kernel + kv_append_kernel",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_step": kv_bytes,
+        },
+        "cpu_baseline": None,
+        "setup_s": round(t_gen, 2),
+    }
     print(json.dumps(result), flush=True)
     return 0
 

@@ -285,6 +285,87 @@ hipdecode_status hipdecode_prefill_attn(const hipdecode_prefill_params *params,
                                         float *lse,
                                         void *stream);
 
+/* ------------------------------------------------------------------------
+ * Graph-replayed decode step.
+ *
+ * Decode runs as captured graphs replayed with the batch padded to fixed
+ * bucket sizes, and the host prepares the next step while the GPU still runs
+ * the current one (MOSS-TD article, "Autoregressive decoding": decode is
+ * replayed as graphs with padded batch buckets, and asynchronous lookahead
+ * scheduling never waits on the GPU).  A runner holds one HIP graph per
+ * bucket -- 1, 2, 4, ... up to the first power of two >= max_seqs -- each
+ * capturing, for layer l = 0 .. num_layers-1 in order,
+ *     hipdecode_kv_append  (one new token per request; RoPE when rope_theta > 0)
+ *     hipdecode_paged_attn
+ * over `bucket` rows of the caller's buffers.  A step for num_seqs requests
+ * writes their context lengths, and zeros up to the bucket, through a pinned
+ * double buffer to `context_lens` with one asynchronous copy, then launches
+ * the bucket's graph (captured on first use).  Padding rows have context
+ * length 0: they append nothing and their out is 0 and lse -inf.  The host
+ * blocks only when the staging half it needs still feeds a copy issued two
+ * steps earlier that has not completed.
+ *
+ * Buffers (the caller owns them; the runner keeps the pointers): per layer l,
+ * k_pool[l], v_pool[l] as for hipdecode_paged_attn; q[l] [max_bucket][Hq][128]
+ * bf16, rotated in place by the append; k_new[l], v_new[l]
+ * [max_bucket][Hkv][128] bf16; out[l] [max_bucket][Hq][128] in out_dtype;
+ * lse[l] [max_bucket][Hq] fp32 (lse itself may be NULL: no LSE);
+ * block_table [max_bucket][max_blocks_per_seq] and context_lens [max_bucket]
+ * int32, device memory.  The caller updates q, k_new, v_new and block_table
+ * between steps with work ordered on the same stream.  The runner allocates
+ * its attention workspace, two pinned staging buffers, two events, a capture
+ * stream and the graphs, and frees them in hipdecode_step_runner_destroy.
+ * A runner is used from one thread, its steps on one stream.
+ * ------------------------------------------------------------------------ */
+
+typedef struct hipdecode_step_runner hipdecode_step_runner;
+
+typedef struct {
+    int32_t num_layers;            /* L >= 1 */
+    int32_t max_seqs;              /* largest batch of a step, >= 1 */
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;              /* 128 */
+    int32_t page_size;             /* 16 */
+    int32_t num_pages;             /* rows of each layer's pools */
+    int32_t max_blocks_per_seq;
+    int32_t max_context_len;       /* bound of every step's context lengths */
+    int32_t out_dtype;             /* hipdecode_dtype */
+    float scale;
+    double rope_theta;             /* > 0: RoPE on K and q; 0: none */
+} hipdecode_step_config;
+
+typedef struct {
+    void *const *k_pool;           /* host arrays of num_layers device pointers */
+    void *const *v_pool;
+    void *const *q;
+    const void *const *k_new;
+    const void *const *v_new;
+    void *const *out;
+    float *const *lse;             /* may be NULL */
+    int32_t *block_table;          /* device */
+    int32_t *context_lens;         /* device */
+} hipdecode_step_buffers;
+
+/* Rows of the bucket a step of num_seqs requests runs in (pure host); 0 if
+ * num_seqs is not in [1, max_seqs]. */
+int32_t hipdecode_step_bucket(int32_t max_seqs, int32_t num_seqs);
+
+/* Checks the configuration and buffers, sizes and zero-fills the workspace;
+ * graphs are captured on first use.  *runner is NULL on failure. */
+hipdecode_status hipdecode_step_runner_create(const hipdecode_step_config *config,
+                                              const hipdecode_step_buffers *buffers,
+                                              hipdecode_step_runner **runner);
+
+/* One decode step for num_seqs requests (0 is a no-op) with host context
+ * lengths context_lens_host[0 .. num_seqs), enqueued on `stream`. */
+hipdecode_status hipdecode_step_runner_step(hipdecode_step_runner *runner, int32_t num_seqs,
+                                            const int32_t *context_lens_host, void *stream);
+
+/* Synchronizes the device (steps may still run on the caller's streams),
+ * then frees what the runner allocated. */
+hipdecode_status hipdecode_step_runner_destroy(hipdecode_step_runner *runner);
+
 /* Static English text for a status code; never NULL. */
 const char *hipdecode_status_string(hipdecode_status status);
 

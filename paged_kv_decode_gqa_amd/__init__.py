@@ -43,6 +43,10 @@ EXPORTED = (
     "hipdecode_kv_append",
     "hipdecode_check_prefill_params",
     "hipdecode_prefill_attn",
+    "hipdecode_step_bucket",
+    "hipdecode_step_runner_create",
+    "hipdecode_step_runner_step",
+    "hipdecode_step_runner_destroy",
     "hipdecode_status_string",
 )
 
@@ -97,6 +101,37 @@ class hipdecode_prefill_params(ctypes.Structure):
     ]
 
 
+class hipdecode_step_config(ctypes.Structure):
+    _fields_ = [
+        ("num_layers", ctypes.c_int32),
+        ("max_seqs", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("max_context_len", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("rope_theta", ctypes.c_double),
+    ]
+
+
+class hipdecode_step_buffers(ctypes.Structure):
+    _fields_ = [
+        ("k_pool", ctypes.POINTER(ctypes.c_void_p)),
+        ("v_pool", ctypes.POINTER(ctypes.c_void_p)),
+        ("q", ctypes.POINTER(ctypes.c_void_p)),
+        ("k_new", ctypes.POINTER(ctypes.c_void_p)),
+        ("v_new", ctypes.POINTER(ctypes.c_void_p)),
+        ("out", ctypes.POINTER(ctypes.c_void_p)),
+        ("lse", ctypes.POINTER(ctypes.c_void_p)),
+        ("block_table", ctypes.c_void_p),
+        ("context_lens", ctypes.c_void_p),
+    ]
+
+
 class HipDecodeError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -142,6 +177,15 @@ def library() -> ctypes.CDLL:
     lib.hipdecode_check_prefill_params.restype = ctypes.c_int
     lib.hipdecode_prefill_attn.argtypes = [PP, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.hipdecode_prefill_attn.restype = ctypes.c_int
+    lib.hipdecode_step_bucket.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    lib.hipdecode_step_bucket.restype = ctypes.c_int32
+    lib.hipdecode_step_runner_create.argtypes = [ctypes.POINTER(hipdecode_step_config),
+                                                 ctypes.POINTER(hipdecode_step_buffers), ctypes.POINTER(vp)]
+    lib.hipdecode_step_runner_create.restype = ctypes.c_int
+    lib.hipdecode_step_runner_step.argtypes = [vp, ctypes.c_int32, vp, vp]
+    lib.hipdecode_step_runner_step.restype = ctypes.c_int
+    lib.hipdecode_step_runner_destroy.argtypes = [vp]
+    lib.hipdecode_step_runner_destroy.restype = ctypes.c_int
     lib.hipdecode_status_string.argtypes = [ctypes.c_int]
     lib.hipdecode_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -444,3 +488,76 @@ def prefill_attn(q, k_pool, v_pool, block_table, context_lens, new_start, scale,
         lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
     hipdecode_prefill_attn(params, q, k_pool, v_pool, new_start, block_table, context_lens, out, lse)
     return out, lse
+
+
+def hipdecode_step_bucket(max_seqs: int, num_seqs: int) -> int:
+    return int(library().hipdecode_step_bucket(int(max_seqs), int(num_seqs)))
+
+
+class StepRunner:
+    """A ``hipdecode_step_runner``: per-layer append + attention, replayed as
+    one captured graph per batch bucket.
+
+    ``layers`` is a list of dicts of device tensors with keys k_pool, v_pool,
+    q, k_new, v_new, out and (optionally) lse, shaped for ``bucket(max_seqs)``
+    rows; ``block_table`` and ``context_lens`` are device int32 tensors of
+    that many rows.  The tensors must stay alive and in place while the runner
+    exists.  ``step(context_lens)`` takes a host sequence of ints."""
+
+    def __init__(self, layers, block_table, context_lens, *, max_seqs, num_pages, max_context_len, scale,
+                 rope_theta=0.0, out_dtype=HIPDECODE_BF16):
+        import numpy as np
+        first = layers[0]
+        L = len(layers)
+        self._keep = (layers, block_table, context_lens)
+
+        def ptrs(key):
+            if any(layer.get(key) is None for layer in layers):
+                return None
+            for layer in layers:
+                if not layer[key].is_contiguous():
+                    raise ValueError(f"{key} must be contiguous")
+            arr = (ctypes.c_void_p * L)(*[layer[key].data_ptr() for layer in layers])
+            return arr
+
+        self._arrays = {k: ptrs(k) for k in ("k_pool", "v_pool", "q", "k_new", "v_new", "out", "lse")}
+        cast = ctypes.cast
+        P = ctypes.POINTER(ctypes.c_void_p)
+        self.buffers = hipdecode_step_buffers(
+            *[cast(self._arrays[k], P) if self._arrays[k] is not None else None
+              for k in ("k_pool", "v_pool", "q", "k_new", "v_new", "out", "lse")],
+            block_table.data_ptr(), context_lens.data_ptr())
+        self.config = hipdecode_step_config(L, int(max_seqs), first["q"].shape[1], first["k_pool"].shape[2],
+                                            first["q"].shape[2], first["k_pool"].shape[1], int(num_pages),
+                                            block_table.shape[1], int(max_context_len), int(out_dtype),
+                                            float(scale), float(rope_theta))
+        handle = ctypes.c_void_p()
+        st = library().hipdecode_step_runner_create(ctypes.byref(self.config), ctypes.byref(self.buffers),
+                                                    ctypes.byref(handle))
+        if st != HIPDECODE_OK:
+            raise HipDecodeError(st, "hipdecode_step_runner_create")
+        self._handle = handle
+        self._np = np
+
+    def bucket(self, num_seqs: int) -> int:
+        return hipdecode_step_bucket(self.config.max_seqs, num_seqs)
+
+    def step(self, context_lens, stream=None) -> None:
+        ctx = self._np.ascontiguousarray(context_lens, dtype=self._np.int32)
+        st = library().hipdecode_step_runner_step(self._handle, int(ctx.shape[0]), ctx.ctypes.data,
+                                                  _stream_handle(stream))
+        if st != HIPDECODE_OK:
+            raise HipDecodeError(st, "hipdecode_step_runner_step")
+
+    def close(self) -> None:
+        if getattr(self, "_handle", None):
+            st = library().hipdecode_step_runner_destroy(self._handle)
+            self._handle = None
+            if st != HIPDECODE_OK:
+                raise HipDecodeError(st, "hipdecode_step_runner_destroy")
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

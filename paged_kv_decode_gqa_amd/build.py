@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libhipdecode.so")
-SOURCES = ["api.hip", "paged_decode.hip", "kv_append.hip", "prefill_attn.hip"]
+SOURCES = ["api.hip", "paged_decode.hip", "kv_append.hip", "prefill_attn.hip", "step_runner.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -372,3 +372,43 @@ def test_prefill_rejects_before_any_launch():
         == hd.HIPDECODE_ERR_UNSUPPORTED
     assert call(ctypes.byref(pbase(num_seqs=0)), None, None, None, None, None, None, None, None, None) \
         == hd.HIPDECODE_OK
+
+
+# --------------------------------------------------------------------------
+# graph-replayed decode step
+# --------------------------------------------------------------------------
+def test_step_structs_match_header():
+    # 10 int32, a float, then a double at offset 48
+    assert ctypes.sizeof(hd.hipdecode_step_config) == 56
+    assert hd.hipdecode_step_config.rope_theta.offset == 48
+    assert ctypes.sizeof(hd.hipdecode_step_buffers) == 9 * 8
+
+
+@pytest.mark.parametrize("max_seqs,n,want", [
+    (16, 1, 1), (16, 2, 2), (16, 3, 4), (16, 5, 8), (16, 9, 16), (16, 16, 16),
+    (12, 12, 16), (12, 13, 0), (16, 0, 0), (16, -1, 0), (0, 1, 0), (1, 1, 1), (100, 65, 128)])
+def test_step_buckets(max_seqs, n, want):
+    assert hd.hipdecode_step_bucket(max_seqs, n) == want
+
+
+def test_step_runner_rejects_before_allocating():
+    lib = hd.library()
+    out = ctypes.c_void_p(123)
+    cfg = hd.hipdecode_step_config(2, 16, 16, 8, 128, 16, 100, 10, 160, 0, 0.1, 1e6)
+    assert lib.hipdecode_step_runner_create(ctypes.byref(cfg), None, ctypes.byref(out)) == hd.HIPDECODE_ERR_NULL
+    assert out.value is None
+    bufs = hd.hipdecode_step_buffers()
+    bad = hd.hipdecode_step_config(0, 16, 16, 8, 128, 16, 100, 10, 160, 0, 0.1, 1e6)
+    assert lib.hipdecode_step_runner_create(ctypes.byref(bad), ctypes.byref(bufs), ctypes.byref(out)) \
+        == hd.HIPDECODE_ERR_SHAPE
+    bad = hd.hipdecode_step_config(2, 16, 16, 8, 64, 16, 100, 10, 160, 0, 0.1, 1e6)
+    assert lib.hipdecode_step_runner_create(ctypes.byref(bad), ctypes.byref(bufs), ctypes.byref(out)) \
+        == hd.HIPDECODE_ERR_UNSUPPORTED
+    bad = hd.hipdecode_step_config(2, 16, 16, 8, 128, 16, 100, 10, 160, 0, 0.1, float("nan"))
+    assert lib.hipdecode_step_runner_create(ctypes.byref(bad), ctypes.byref(bufs), ctypes.byref(out)) \
+        == hd.HIPDECODE_ERR_SCALE
+    # valid shapes but no buffers
+    assert lib.hipdecode_step_runner_create(ctypes.byref(cfg), ctypes.byref(bufs), ctypes.byref(out)) \
+        == hd.HIPDECODE_ERR_NULL
+    assert lib.hipdecode_step_runner_step(None, 1, None, None) == hd.HIPDECODE_ERR_NULL
+    assert lib.hipdecode_step_runner_destroy(None) == hd.HIPDECODE_ERR_NULL
