@@ -196,8 +196,12 @@ def test_planner_and_workspace_sizes():
     part1 = hd.hipdecode_partition_tokens(p1)
     assert 8 * (-(-28672 // part1)) == 256
     # one partition per request: only the counters
-    p2 = base(num_seqs=1, max_context_len=200, num_pages=64, max_blocks_per_seq=13)
-    assert hd.hipdecode_workspace_bytes(p2) == 256
+    p2 = base(num_seqs=16, max_context_len=200, num_pages=64, max_blocks_per_seq=13)
+    assert hd.hipdecode_partition_tokens(p2) == 256
+    assert hd.hipdecode_workspace_bytes(p2) == 512
+    # one short request is split for latency: 512 tokens in 64-token partitions
+    p3 = base(num_seqs=1, max_context_len=512, num_pages=64, max_blocks_per_seq=32)
+    assert hd.hipdecode_partition_tokens(p3) == 64
     # explicit partition is honoured
     assert hd.hipdecode_partition_tokens(base(partition_tokens=128)) == 128
 
