@@ -25,9 +25,10 @@ on workload p1 (the last 4096-token chunk of a 28672-token prompt) or p2 (the
 first chunk), against the bf16 dense matrix-core peak.
 
 ``--op step`` measures the graph-replayed decode step (``hipdecode_step_runner``:
-per layer, append with RoPE and attention, one captured graph per batch
-bucket) on the launch-bound shapes s1 (one request at 512 tokens) and s2 (16
-requests of 200-420 tokens), against the same 2 x 28 launches issued eagerly.
+per layer, one fused launch of append with RoPE and attention, one captured
+graph per batch bucket) on the latency-bound shapes s1 (one request at 512
+tokens) and s2 (16 requests of 200-420 tokens), against the same fused
+launches issued eagerly and against separate append and attention launches.
 
 Prints one JSON line.
 """
@@ -484,7 +485,7 @@ def run_append(args, dev) -> int:
 
 
 STEP_WORKLOADS = {"s1": "c1", "s2": "c2"}   # decode shapes whose steps are launch-bound
-STEP_METRIC = "decode-step tokens/s, graph-replayed append + attention over 28 layers"
+STEP_METRIC = "decode-step tokens/s, graph-replayed fused append + attention over 28 layers"
 
 
 def run_step(args, dev) -> int:
@@ -534,11 +535,14 @@ def run_step(args, dev) -> int:
                             max_blocks_per_seq=case.max_blocks, max_context_len=case.max_context_len,
                             scale=case.scale)
     ws = torch.zeros(hd.hipdecode_workspace_bytes(params) // 4 + 4, dtype=torch.int32, device=dev)
-    eager = []
+    eager = []           # two launches per layer: append, then attention
+    fused = []           # one fused launch per layer
     for d in layers:
         eager.append(hd.PreparedAppend(aparams, d["q"], d["k_new"], d["v_new"], None, table, ctx_dev, d["k_pool"],
                                        d["v_pool"]))
         eager.append(hd.PreparedCall(params, d["q"], d["k_pool"], d["v_pool"], table, ctx_dev, d["out"], d["lse"], ws))
+        fused.append(hd.PreparedAttnAppend(params, ROPE_THETA, d["q"], d["k_new"], d["v_new"], d["k_pool"],
+                                           d["v_pool"], table, ctx_dev, d["out"], d["lse"], ws))
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
@@ -559,7 +563,12 @@ def run_step(args, dev) -> int:
         for c in eager:
             c()
 
+    def fused_step():
+        for c in fused:
+            c()
+
     ms_eager = timed(eager_step)
+    ms_fused = timed(fused_step)
     ms_graph = timed(lambda: runner.step(ctx_host))
     runner.close()
     kv_bytes = 2 * case.Hkv * case.D * 2 * case.total_tokens * LAYERS
@@ -587,6 +596,7 @@ def run_step(args, dev) -> int:
             "mode": "hip graph per bucket (step runner)",
         },
         "eager_ms_per_step": round(ms_eager, 4),
+        "eager_fused_ms_per_step": round(ms_fused, 4),
         "speedup_vs_eager": round(ms_eager / ms_graph, 3),
         "roofline": {
             "bound": "hbm",

@@ -295,8 +295,8 @@ hipdecode_status hipdecode_prefill_attn(const hipdecode_prefill_params *params,
  * scheduling never waits on the GPU).  A runner holds one HIP graph per
  * bucket -- 1, 2, 4, ... up to the first power of two >= max_seqs -- each
  * capturing, for layer l = 0 .. num_layers-1 in order,
- *     hipdecode_kv_append  (one new token per request; RoPE when rope_theta > 0)
- *     hipdecode_paged_attn
+ *     hipdecode_paged_attn_append  (append one new token per request, RoPE
+ *                                   when rope_theta > 0, and attend)
  * over `bucket` rows of the caller's buffers.  A step for num_seqs requests
  * writes their context lengths, and zeros up to the bucket, through a pinned
  * double buffer to `context_lens` with one asynchronous copy, then launches
@@ -307,7 +307,7 @@ hipdecode_status hipdecode_prefill_attn(const hipdecode_prefill_params *params,
  *
  * Buffers (the caller owns them; the runner keeps the pointers): per layer l,
  * k_pool[l], v_pool[l] as for hipdecode_paged_attn; q[l] [max_bucket][Hq][128]
- * bf16, rotated in place by the append; k_new[l], v_new[l]
+ * bf16 (read, not rotated in place); k_new[l], v_new[l]
  * [max_bucket][Hkv][128] bf16; out[l] [max_bucket][Hq][128] in out_dtype;
  * lse[l] [max_bucket][Hq] fp32 (lse itself may be NULL: no LSE);
  * block_table [max_bucket][max_blocks_per_seq] and context_lens [max_bucket]
@@ -365,6 +365,32 @@ hipdecode_status hipdecode_step_runner_step(hipdecode_step_runner *runner, int32
 /* Synchronizes the device (steps may still run on the caller's streams),
  * then frees what the runner allocated. */
 hipdecode_status hipdecode_step_runner_destroy(hipdecode_step_runner *runner);
+
+/* One decode step of append and attention in a single launch: the same
+ * result as hipdecode_kv_append (one new token per request, new_start NULL;
+ * RoPE on K and q with rope_theta when rope_theta > 0, none when 0) followed
+ * by hipdecode_paged_attn, except that q is read, not rotated in place.  The
+ * workgroup that folds a request's last page takes the new token's K and V
+ * from k_new/v_new [num_seqs][num_kv_heads][128] (bf16, 16-byte aligned),
+ * writes them to their slot and folds them from registers; every workgroup
+ * rotates its query heads itself.  Split schedule only (schedule 0 or 1):
+ * a stream schedule gives HIPDECODE_ERR_UNSUPPORTED; a rope_theta that is
+ * negative or not finite gives HIPDECODE_ERR_SCALE.  Same buffers, workspace
+ * and contract as hipdecode_paged_attn otherwise; the pools are written. */
+hipdecode_status hipdecode_paged_attn_append(const hipdecode_params *params,
+                                             double rope_theta,
+                                             const void *q,
+                                             const void *k_new,
+                                             const void *v_new,
+                                             void *k_pool,
+                                             void *v_pool,
+                                             const int32_t *block_table,
+                                             const int32_t *context_lens,
+                                             void *out,
+                                             float *lse,
+                                             void *workspace,
+                                             size_t workspace_bytes,
+                                             void *stream);
 
 /* Static English text for a status code; never NULL. */
 const char *hipdecode_status_string(hipdecode_status status);

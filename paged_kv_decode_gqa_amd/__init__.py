@@ -39,6 +39,7 @@ EXPORTED = (
     "hipdecode_workspace_bytes",
     "hipdecode_workspace_init",
     "hipdecode_paged_attn",
+    "hipdecode_paged_attn_append",
     "hipdecode_check_append_params",
     "hipdecode_kv_append",
     "hipdecode_check_prefill_params",
@@ -167,6 +168,9 @@ def library() -> ctypes.CDLL:
     lib.hipdecode_workspace_init.restype = ctypes.c_int
     lib.hipdecode_paged_attn.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.hipdecode_paged_attn.restype = ctypes.c_int
+    lib.hipdecode_paged_attn_append.argtypes = [P, ctypes.c_double, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                ctypes.c_size_t, vp]
+    lib.hipdecode_paged_attn_append.restype = ctypes.c_int
     PA = ctypes.POINTER(hipdecode_append_params)
     lib.hipdecode_check_append_params.argtypes = [PA]
     lib.hipdecode_check_append_params.restype = ctypes.c_int
@@ -360,6 +364,25 @@ def hipdecode_kv_append(params: hipdecode_append_params, q, k_new, v_new, new_st
                                        _stream_handle(stream))
     if st != HIPDECODE_OK:
         raise HipDecodeError(st, "hipdecode_kv_append")
+
+
+class PreparedAttnAppend:
+    """The marshalled argument list of one ``hipdecode_paged_attn_append``
+    call, invoked many times without re-marshalling."""
+
+    def __init__(self, params, rope_theta, q, k_new, v_new, k_pool, v_pool, block_table, context_lens, out, lse,
+                 workspace):
+        self._keep = (params, q, k_new, v_new, k_pool, v_pool, block_table, context_lens, out, lse, workspace)
+        ws_bytes = workspace.numel() * workspace.element_size()
+        self._args = (ctypes.byref(params), float(rope_theta), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool),
+                      _ptr(v_pool), _ptr(block_table), _ptr(context_lens), _ptr(out), _ptr(lse), _ptr(workspace),
+                      ws_bytes)
+        self._fn = library().hipdecode_paged_attn_append
+
+    def __call__(self, stream=None) -> None:
+        st = self._fn(*self._args, _stream_handle(stream))
+        if st != HIPDECODE_OK:
+            raise HipDecodeError(st, "hipdecode_paged_attn_append")
 
 
 class PreparedAppend:
@@ -561,3 +584,50 @@ class StepRunner:
             self.close()
         except Exception:
             pass
+
+
+def hipdecode_paged_attn_append(params: hipdecode_params, rope_theta, q, k_new, v_new, k_pool, v_pool, block_table,
+                                context_lens, out, lse, workspace, stream=None) -> None:
+    """Enqueue one fused append + attention call (q is not modified)."""
+    for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new), ("k_pool", k_pool), ("v_pool", v_pool),
+                    ("block_table", block_table), ("context_lens", context_lens), ("out", out), ("lse", lse),
+                    ("workspace", workspace)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = library().hipdecode_paged_attn_append(ctypes.byref(params), float(rope_theta), _ptr(q), _ptr(k_new),
+                                               _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+                                               _ptr(context_lens), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+                                               _stream_handle(stream))
+    if st != HIPDECODE_OK:
+        raise HipDecodeError(st, "hipdecode_paged_attn_append")
+
+
+def paged_attn_append(q, k_new, v_new, k_pool, v_pool, block_table, context_lens, scale, *, max_context_len,
+                      rope_theta=0.0, out_dtype=None, partition_tokens=0, workgroup_waves=0, out=None, lse=None,
+                      workspace=None):
+    """Append each request's new token (k_new/v_new [B,Hkv,128], RoPE when
+    rope_theta > 0) and attend, in one launch; returns (out, lse)."""
+    import torch
+    B, Hq, D = q.shape
+    P, page, Hkv, _ = k_pool.shape
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else torch.bfloat16
+    params = make_params(num_seqs=B, num_q_heads=Hq, num_kv_heads=Hkv, num_pages=P,
+                         max_blocks_per_seq=block_table.shape[1], max_context_len=max_context_len, scale=scale,
+                         head_dim=D, page_size=page, partition_tokens=partition_tokens,
+                         workgroup_waves=workgroup_waves, schedule=HIPDECODE_SCHEDULE_SPLIT,
+                         out_dtype=HIPDECODE_F32 if out_dtype == torch.float32 else HIPDECODE_BF16)
+    st = hipdecode_check_params(params)
+    if st != HIPDECODE_OK:
+        raise HipDecodeError(st, "hipdecode_check_params")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nbytes = hipdecode_workspace_bytes(params)
+        workspace = torch.zeros(max(nbytes, 16) // 4 + 4, dtype=torch.int32, device=q.device)
+    hipdecode_paged_attn_append(params, rope_theta, q, k_new, v_new, k_pool, v_pool, block_table, context_lens, out,
+                                lse, workspace)
+    return out, lse

@@ -217,17 +217,26 @@ HIPDECODE_API hipdecode_status hipdecode_workspace_init(void *workspace, size_t 
                : HIPDECODE_ERR_HIP;
 }
 
-HIPDECODE_API hipdecode_status hipdecode_paged_attn(const hipdecode_params *params, const void *q,
-                                                    const void *k_pool, const void *v_pool,
-                                                    const int32_t *block_table,
-                                                    const int32_t *context_lens, void *out,
-                                                    float *lse, void *workspace,
-                                                    size_t workspace_bytes, void *stream)
+namespace hipdecode {
+namespace {
+
+// The body of both decode entry points; `fused` also appends each request's
+// new token (k_new/v_new, RoPE with rope_theta when > 0) inside the kernel.
+hipdecode_status run_decode(const hipdecode_params *params, const void *q, const void *k_pool, const void *v_pool,
+                            const int32_t *block_table, const int32_t *context_lens, void *out, float *lse,
+                            void *workspace, size_t workspace_bytes, void *stream, bool fused,
+                            const void *k_new, const void *v_new, double rope_theta)
 {
     const hipdecode_status st = check(params);
     if (st != HIPDECODE_OK)
         return st;
     const hipdecode_params &p = *params;
+    if (fused) {
+        if (plan_schedule(p) != kScheduleSplit)
+            return HIPDECODE_ERR_UNSUPPORTED;
+        if (!(rope_theta >= 0.0) || !isfinite(rope_theta))
+            return HIPDECODE_ERR_SCALE;
+    }
     if (p.num_seqs == 0)
         return HIPDECODE_OK;
     if (q == nullptr || out == nullptr || context_lens == nullptr || block_table == nullptr ||
@@ -235,8 +244,11 @@ HIPDECODE_API hipdecode_status hipdecode_paged_attn(const hipdecode_params *para
         return HIPDECODE_ERR_NULL;
     if (p.max_context_len > 0 && (k_pool == nullptr || v_pool == nullptr))
         return HIPDECODE_ERR_NULL;
+    if (fused && p.max_context_len > 0 && (k_new == nullptr || v_new == nullptr))
+        return HIPDECODE_ERR_NULL;
     if (!aligned16(q) || !aligned16(out) || !aligned16(workspace) ||
         (k_pool != nullptr && !aligned16(k_pool)) || (v_pool != nullptr && !aligned16(v_pool)) ||
+        (k_new != nullptr && !aligned16(k_new)) || (v_new != nullptr && !aligned16(v_new)) ||
         (reinterpret_cast<uintptr_t>(lse) & 3u) != 0 ||
         (reinterpret_cast<uintptr_t>(block_table) & 3u) != 0 ||
         (reinterpret_cast<uintptr_t>(context_lens) & 3u) != 0)
@@ -270,11 +282,40 @@ HIPDECODE_API hipdecode_status hipdecode_paged_attn(const hipdecode_params *para
     a.nsplit_max = nsplit;
     a.stream_workgroups = stream_workgroups(p);
     a.scale_log2 = p.scale * 1.44269504088896340736f;
+    a.k_new = static_cast<const uint16_t *>(k_new);
+    a.v_new = static_cast<const uint16_t *>(v_new);
+    a.k_pool_w = fused ? static_cast<uint16_t *>(const_cast<void *>(k_pool)) : nullptr;
+    a.v_pool_w = fused ? static_cast<uint16_t *>(const_cast<void *>(v_pool)) : nullptr;
+    a.rope_theta = fused ? rope_theta : 0.0;
 
-    const hipError_t e = launch_paged_decode(a, p.num_q_heads / p.num_kv_heads, plan_waves(p),
-                                             plan_schedule(p), p.out_dtype == HIPDECODE_F32,
-                                             static_cast<hipStream_t>(stream));
+    const hipError_t e = launch_paged_decode(a, p.num_q_heads / p.num_kv_heads, plan_waves(p), plan_schedule(p),
+                                             p.out_dtype == HIPDECODE_F32, static_cast<hipStream_t>(stream), fused);
     return e == hipSuccess ? HIPDECODE_OK : HIPDECODE_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace hipdecode
+
+HIPDECODE_API hipdecode_status hipdecode_paged_attn(const hipdecode_params *params, const void *q,
+                                                    const void *k_pool, const void *v_pool,
+                                                    const int32_t *block_table,
+                                                    const int32_t *context_lens, void *out,
+                                                    float *lse, void *workspace,
+                                                    size_t workspace_bytes, void *stream)
+{
+    return run_decode(params, q, k_pool, v_pool, block_table, context_lens, out, lse, workspace, workspace_bytes,
+                      stream, false, nullptr, nullptr, 0.0);
+}
+
+HIPDECODE_API hipdecode_status hipdecode_paged_attn_append(const hipdecode_params *params, double rope_theta,
+                                                           const void *q, const void *k_new, const void *v_new,
+                                                           void *k_pool, void *v_pool,
+                                                           const int32_t *block_table,
+                                                           const int32_t *context_lens, void *out, float *lse,
+                                                           void *workspace, size_t workspace_bytes, void *stream)
+{
+    return run_decode(params, q, k_pool, v_pool, block_table, context_lens, out, lse, workspace, workspace_bytes,
+                      stream, true, k_new, v_new, rope_theta);
 }
 
 HIPDECODE_API const char *hipdecode_status_string(hipdecode_status status)

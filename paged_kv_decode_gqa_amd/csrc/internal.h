@@ -49,11 +49,19 @@ struct DecodeArgs {
     int32_t nsplit_max;          // split schedule: partitions of the longest context
     int32_t stream_workgroups;   // stream schedule: grid size
     float scale_log2;   // scale * log2(e): scores are kept in base-2 units
+    // Fused append (hipdecode_paged_attn_append) only: each request's new
+    // token, written to its slot and folded from registers, and RoPE.
+    const uint16_t *k_new;   // [B][Hkv][128]
+    const uint16_t *v_new;   // [B][Hkv][128]
+    uint16_t *k_pool_w;      // the pools, writable
+    uint16_t *v_pool_w;
+    double rope_theta;       // > 0: q and the new key are rotated at position ctx - 1
 };
 
-// waves: 4 or 16 wavefronts per workgroup (split schedule); schedule: kSchedule*
+// waves: 4 or 16 wavefronts per workgroup (split schedule); schedule: kSchedule*;
+// fused: the split kernel that also appends each request's new token
 hipError_t launch_paged_decode(const DecodeArgs &a, int group, int waves, int schedule, bool out_f32,
-                               hipStream_t stream);
+                               hipStream_t stream, bool fused = false);
 hipError_t launch_zero_fill(void *p, size_t bytes, hipStream_t stream);
 
 }  // namespace hipdecode

@@ -21,6 +21,7 @@
 // request.
 #include "hipdecode.h"
 #include "internal.h"
+#include "rope_round.h"
 
 #include <math.h>
 
@@ -56,38 +57,9 @@ struct AppendArgs {
     double theta;
 };
 
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-// fp64 -> fp32 rounded to odd: the fp32 number next to x towards zero, with
-// its last bit set when x is not exactly representable.  fp32 keeps 16 more
-// significand bits than bf16 (normal or subnormal alike, the exponent ranges
-// being the same), more than the two that rounding to odd needs for a second
-// rounding, to bf16 nearest even, to equal the direct one (Boldo and
-// Melquiond, "Emulation of FMA and correctly rounded sums: proved algorithms
-// using rounding to odd", IEEE Trans. Computers, 2008).  The hardware
-// conversion rounds to nearest; it is stepped back by one unit in the last
-// place when that went away from zero.
-__device__ inline float round_to_odd_f32(double x)
-{
-    const float t = (float)x;
-    const double back = (double)t;
-    const bool inexact = back != x;
-    uint32_t b = __float_as_uint(t);
-    b -= (inexact && fabs(back) > fabs(x)) ? 1u : 0u;
-    b |= inexact ? 1u : 0u;
-    return __uint_as_float(b);
-}
-
-// Nearest-even bf16 bits of x (low half) and y (high half); NaN gives 0x7FC0.
-__device__ inline uint32_t pack_bf16(double x, double y)
-{
-    const f32x2_t v = {round_to_odd_f32(x), round_to_odd_f32(y)};
-    uint32_t u = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
-    u = x != x ? (u & 0xFFFF0000u) | 0x7FC0u : u;
-    u = y != y ? (u & 0x0000FFFFu) | 0x7FC00000u : u;
-    return u;
-}
+using rope::bf16x2_t;
+using rope::f32x2_t;
+using rope::pack_bf16;
 
 __device__ inline uint4 load16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
 __device__ inline void store16(uint16_t *p, uint4 v) { *reinterpret_cast<uint4 *>(p) = v; }
@@ -227,10 +199,7 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(AppendArgs a)
     double2 cs[kPairsPerItem];
     if (ROPE) {
         // lane i: the angle of pair i, evaluated in fp64
-        const double freq = pow(a.theta, -2.0 * (double)lane / (double)kHeadDim);
-        double sn, c;
-        sincos((double)pos * freq, &sn, &c);
-        angles[w][lane] = make_double2(c, sn);
+        angles[w][lane] = rope::angle(a.theta, pos, lane);
         // LDS operations of one wavefront complete in order; this keeps the
         // compiler from moving the reads above the write.
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

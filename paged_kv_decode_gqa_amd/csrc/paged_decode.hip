@@ -28,6 +28,7 @@
 // call is one launch.  Partials travel through device-scope atomics (see
 // page_fold.h), not fences, so no workgroup flushes or invalidates the L2.
 #include "page_fold.h"
+#include "rope_round.h"
 
 namespace hipdecode {
 namespace {
@@ -120,17 +121,22 @@ __device__ __forceinline__ void load_q(u32x4 (&qv)[G], const DecodeArgs &a, size
 // entry: the block-table entry of page p_begin + wave + WAVES * lane, or
 // anything for lanes past the range.  A partly filled last page of the
 // request is folded by the last wavefront, with masking, after the others.
-template <int G, int WAVES>
+// FUSED: the request's last page always goes that way, and its new token
+// (slot (ctx - 1) % 16, row b of k_new/v_new) is taken from k_new/v_new --
+// K rotated with `angles` when RoPE is on -- written to the pool and folded
+// from registers; no other workgroup reads that page.
+template <int G, int WAVES, bool FUSED = false>
 __device__ __forceinline__ void fold_range(Stream<G> &st, const DecodeArgs &a, const u32x4 (&qv)[G],
                                            const int32_t *trow, int g, int p_begin, int p_end,
-                                           int n_pages, int ctx, int entry, const Lane &ln)
+                                           int n_pages, int ctx, int entry, const Lane &ln, int b = 0,
+                                           const double2 *angles = nullptr)
 {
     const uint32_t tok_bytes = (uint32_t)a.num_kv_heads * kHeadDim * 2;   // bytes between slots
     const size_t page_elems = (size_t)kPageSize * a.num_kv_heads * kHeadDim;
     const uint32_t lane_off = (uint32_t)g * kHeadDim * 2 + (uint32_t)ln.row * tok_bytes + (uint32_t)ln.sub * 16;
     const uint32_t tok4 = 4 * tok_bytes;
 
-    const bool tail_partial = (p_end == n_pages) && (ctx % kPageSize != 0);
+    const bool tail_partial = (p_end == n_pages) && (FUSED || ctx % kPageSize != 0);
     const int full_end = tail_partial ? p_end - 1 : p_end;
     const int span = full_end - p_begin;
     const int npw = span > ln.wave ? (span - ln.wave + WAVES - 1) / WAVES : 0;
@@ -176,6 +182,32 @@ __device__ __forceinline__ void fold_range(Stream<G> &st, const DecodeArgs &a, c
         if ((unsigned)phys < num_pages) {
             load_page(ra, a.k_pool + (size_t)phys * page_elems, a.v_pool + (size_t)phys * page_elems,
                       lane_off, tok4);
+            if constexpr (FUSED) {
+                const int slot = (ctx - 1) % kPageSize;
+                if (ln.row == (slot & 3)) {   // the 16 lanes holding the new token, in register slot / 4
+                    const size_t nrow = ((size_t)b * a.num_kv_heads + g) * kHeadDim;
+                    u32x4 kn = load16(a.k_new + nrow + ln.sub * 8);
+                    const u32x4 vn = load16(a.v_new + nrow + ln.sub * 8);
+                    if (angles != nullptr) {
+                        const u32x4 kp = load16(a.k_new + nrow + (ln.sub ^ 8) * 8);
+                        const int base = 8 * (ln.sub & 7);
+                        const uint4 r = rope::rotate8(make_uint4(kn.x, kn.y, kn.z, kn.w),
+                                                      make_uint4(kp.x, kp.y, kp.z, kp.w), ln.sub >= 8,
+                                                      [&](int e) { return angles[base + e]; });
+                        kn = u32x4{r.x, r.y, r.z, r.w};
+                    }
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        if (t == (slot >> 2)) {
+                            ra.k[t] = kn;
+                            ra.v[t] = vn;
+                        }
+                    }
+                    const size_t off = (size_t)phys * page_elems * 2 + lane_off + (size_t)(slot >> 2) * tok4;
+                    *reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(a.k_pool_w) + off) = kn;
+                    *reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(a.v_pool_w) + off) = vn;
+                }
+            }
             fold_page<G, true>(st, ra, qv, a.scale_log2, full_end * kPageSize + ln.row, ctx);
         }
     }
@@ -377,7 +409,7 @@ __device__ __forceinline__ int clamp_ctx(int ctx, int max_ctx)
 // split schedule: workgroup = (request, split, KV head), KV head fastest so
 // consecutive workgroups read neighbouring head rows of the same pages.
 // ---------------------------------------------------------------------------
-template <int G, int WAVES, bool OUT_F32>
+template <int G, int WAVES, bool OUT_F32, bool FUSED>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4)))
 void paged_decode_kernel(DecodeArgs a)
 {
@@ -413,10 +445,31 @@ void paged_decode_kernel(DecodeArgs a)
 
     u32x4 qv[G];
     load_q<G>(qv, a, row0, ln.sub);
+    const double2 *rope_cs = nullptr;
+    if constexpr (FUSED) {
+        // RoPE of this lane's 8 dimensions of its G query heads at position
+        // ctx - 1; the 64 angles come from the first wavefront through LDS.
+        __shared__ double2 angles[rope::kHalf];
+        if (a.rope_theta > 0.0) {
+            if (ln.wave == 0)
+                angles[ln.lane] = rope::angle(a.rope_theta, ctx - 1, ln.lane);
+            __syncthreads();
+            const int base = 8 * (ln.sub & 7);
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const u32x4 qp = load16(a.q + (row0 + h) * kHeadDim + (ln.sub ^ 8) * 8);
+                const uint4 r = rope::rotate8(make_uint4(qv[h].x, qv[h].y, qv[h].z, qv[h].w),
+                                              make_uint4(qp.x, qp.y, qp.z, qp.w), ln.sub >= 8,
+                                              [&](int e) { return angles[base + e]; });
+                qv[h] = u32x4{r.x, r.y, r.z, r.w};
+            }
+            rope_cs = angles;
+        }
+    }
     Stream<G> st;
     st.init();
-    fold_range<G, WAVES>(st, a, qv, trow, g, p_begin, min(p_begin + a.partition_pages, n_pages), n_pages, ctx,
-                         spec_entry, ln);
+    fold_range<G, WAVES, FUSED>(st, a, qv, trow, g, p_begin, min(p_begin + a.partition_pages, n_pages), n_pages,
+                                ctx, spec_entry, ln, b, rope_cs);
     publish_streams<G, WAVES>(st, sm, ln);
     __syncthreads();
 
@@ -594,19 +647,26 @@ __global__ void zero_fill_kernel(uint8_t *p, size_t bytes)
 }
 
 template <int G, int WAVES>
-hipError_t launch_split(const DecodeArgs &a, bool out_f32, unsigned grid, hipStream_t stream)
+hipError_t launch_split(const DecodeArgs &a, bool out_f32, unsigned grid, hipStream_t stream, bool fused)
 {
-    if (out_f32)
-        hipLaunchKernelGGL((paged_decode_kernel<G, WAVES, true>), dim3(grid), dim3(64 * WAVES), 0, stream, a);
+    const dim3 block(64 * WAVES);
+    if (fused && out_f32)
+        hipLaunchKernelGGL((paged_decode_kernel<G, WAVES, true, true>), dim3(grid), block, 0, stream, a);
+    else if (fused)
+        hipLaunchKernelGGL((paged_decode_kernel<G, WAVES, false, true>), dim3(grid), block, 0, stream, a);
+    else if (out_f32)
+        hipLaunchKernelGGL((paged_decode_kernel<G, WAVES, true, false>), dim3(grid), block, 0, stream, a);
     else
-        hipLaunchKernelGGL((paged_decode_kernel<G, WAVES, false>), dim3(grid), dim3(64 * WAVES), 0, stream, a);
+        hipLaunchKernelGGL((paged_decode_kernel<G, WAVES, false, false>), dim3(grid), block, 0, stream, a);
     return hipGetLastError();
 }
 
 template <int G>
-hipError_t launch_g(const DecodeArgs &a, int waves, int schedule, bool out_f32, hipStream_t stream)
+hipError_t launch_g(const DecodeArgs &a, int waves, int schedule, bool out_f32, hipStream_t stream, bool fused)
 {
     if (schedule == kScheduleStream) {
+        if (fused)
+            return hipErrorInvalidValue;
         const unsigned grid = (unsigned)a.stream_workgroups;
         if (out_f32)
             hipLaunchKernelGGL((paged_decode_stream_kernel<G, true>), dim3(grid), dim3(256), 0, stream, a);
@@ -617,22 +677,22 @@ hipError_t launch_g(const DecodeArgs &a, int waves, int schedule, bool out_f32, 
     const unsigned grid = (unsigned)((size_t)a.num_seqs * a.nsplit_max * a.num_kv_heads);
     if constexpr (G <= 2) {   // G = 4 at 16 wavefronts would not fit 128 VGPRs without spilling
         if (waves == 16)
-            return launch_split<G, 16>(a, out_f32, grid, stream);
+            return launch_split<G, 16>(a, out_f32, grid, stream, fused);
     }
-    return waves == 4 ? launch_split<G, 4>(a, out_f32, grid, stream) : hipErrorInvalidValue;
+    return waves == 4 ? launch_split<G, 4>(a, out_f32, grid, stream, fused) : hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_paged_decode(const DecodeArgs &a, int group, int waves, int schedule, bool out_f32,
-                               hipStream_t stream)
+                               hipStream_t stream, bool fused)
 {
     if (a.num_seqs == 0)
         return hipSuccess;
     switch (group) {
-    case 1: return launch_g<1>(a, waves, schedule, out_f32, stream);
-    case 2: return launch_g<2>(a, waves, schedule, out_f32, stream);
-    case 4: return launch_g<4>(a, waves, schedule, out_f32, stream);
+    case 1: return launch_g<1>(a, waves, schedule, out_f32, stream, fused);
+    case 2: return launch_g<2>(a, waves, schedule, out_f32, stream, fused);
+    case 4: return launch_g<4>(a, waves, schedule, out_f32, stream, fused);
     default: return hipErrorInvalidValue;
     }
 }

@@ -1,0 +1,89 @@
+// rope_round.h -- RoPE angles and the exact fp64 -> bf16 rounding shared by the
+// KV-append kernel and the decode kernel's fused append.
+//
+// RoPE (Qwen3 decoder, theta 1e6: audio.cpp "Fun-ASR-Nano Native Runtime
+// Design", "Decoder And Prompt"), rotate-half pairing: dimension i pairs with
+// i + 64, frequency f_i = theta^(-2i/128).  Rotations are evaluated in fp64
+// from the exactly widened bf16 inputs and rounded once to bf16.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+namespace hipdecode {
+namespace rope {
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kHalf = 64;   // rotation pairs of a 128-dimension head
+
+// (cos, sin) of pair i's angle at position pos, in fp64.
+__device__ inline double2 angle(double theta, int pos, int i)
+{
+    const double freq = pow(theta, -2.0 * (double)i / 128.0);
+    double sn, c;
+    sincos((double)pos * freq, &sn, &c);
+    return make_double2(c, sn);
+}
+
+// fp64 -> fp32 rounded to odd: the fp32 number next to x towards zero, with
+// its last bit set when x is not exactly representable.  fp32 keeps 16 more
+// significand bits than bf16 (normal or subnormal alike, the exponent ranges
+// being the same), more than the two that rounding to odd needs for a second
+// rounding, to bf16 nearest even, to equal the direct one (Boldo and
+// Melquiond, "Emulation of FMA and correctly rounded sums: proved algorithms
+// using rounding to odd", IEEE Trans. Computers, 2008).  The hardware
+// conversion rounds to nearest; it is stepped back by one unit in the last
+// place when that went away from zero.
+__device__ inline float round_to_odd_f32(double x)
+{
+    const float t = (float)x;
+    const double back = (double)t;
+    const bool inexact = back != x;
+    uint32_t b = __float_as_uint(t);
+    b -= (inexact && fabs(back) > fabs(x)) ? 1u : 0u;
+    b |= inexact ? 1u : 0u;
+    return __uint_as_float(b);
+}
+
+// Nearest-even bf16 bits of x (low half) and y (high half); NaN gives 0x7FC0.
+__device__ inline uint32_t pack_bf16(double x, double y)
+{
+    const f32x2_t v = {round_to_odd_f32(x), round_to_odd_f32(y)};
+    uint32_t u = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+    u = x != x ? (u & 0xFFFF0000u) | 0x7FC0u : u;
+    u = y != y ? (u & 0x0000FFFFu) | 0x7FC00000u : u;
+    return u;
+}
+
+// bf16 bits of the low (element 0) or high (element 1) half widened to fp64.
+__device__ inline double lo_f64(uint32_t w) { return (double)__uint_as_float(w << 16); }
+__device__ inline double hi_f64(uint32_t w) { return (double)__uint_as_float(w & 0xFFFF0000u); }
+
+// Rotates 8 consecutive dimensions [8c, 8c + 8) of a head held in `own`
+// (c = 0..15), given the 8 partner dimensions `partner` (8c + 64 or 8c - 64):
+// pairs 8(c % 8) + e use angles cs(e).  The first half of a head takes
+// x cos - partner sin, the second partner sin + x cos.
+template <typename CS>
+__device__ inline uint4 rotate8(uint4 own, uint4 partner, bool second_half, CS cs)
+{
+    const uint32_t o[4] = {own.x, own.y, own.z, own.w};
+    const uint32_t p[4] = {partner.x, partner.y, partner.z, partner.w};
+    uint32_t r[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const double2 c0 = cs(2 * w);
+        const double2 c1 = cs(2 * w + 1);
+        const double x0 = lo_f64(o[w]), x1 = hi_f64(o[w]);
+        const double y0 = lo_f64(p[w]), y1 = hi_f64(p[w]);
+        const double r0 = second_half ? x0 * c0.x + y0 * c0.y : x0 * c0.x - y0 * c0.y;
+        const double r1 = second_half ? x1 * c1.x + y1 * c1.y : x1 * c1.x - y1 * c1.y;
+        r[w] = pack_bf16(r0, r1);
+    }
+    return make_uint4(r[0], r[1], r[2], r[3]);
+}
+
+}  // namespace rope
+}  // namespace hipdecode

@@ -4,9 +4,10 @@
 // Decode steps are replayed as captured graphs with the batch padded to a
 // fixed bucket size, and the host prepares step t+1 while the GPU runs step t
 // (MOSS-TD article, "Autoregressive decoding").  One graph per power-of-two
-// bucket holds, layer after layer, the KV append and the paged attention of
-// that bucket's rows; it is captured from this library's own entry points on
-// a private stream the first time the bucket is used.  The per-step input the
+// bucket holds, layer after layer, the fused KV append and paged attention
+// (hipdecode_paged_attn_append, one launch per layer) of that bucket's rows;
+// it is captured from this library's own entry point on a private stream the
+// first time the bucket is used.  The per-step input the
 // graphs read -- the context lengths -- goes through two pinned host buffers
 // used in turn, each released by an event recorded after its copy.
 #include "hipdecode.h"
@@ -149,22 +150,20 @@ void release(hipdecode_step_runner *r)
     delete r;
 }
 
-// Captures every layer's append and attention for `bucket` rows.
+// Captures every layer's fused append and attention for `bucket` rows.
 hipdecode_status capture(hipdecode_step_runner *r, int32_t bucket, hipGraphExec_t *exec)
 {
     const hipdecode_params p = attn_params(r->cfg, bucket);
-    const hipdecode_append_params ap = append_params(r->cfg, bucket);
+    const hipdecode_append_params ap = append_params(r->cfg, bucket);   // checked at create
     if (hipStreamBeginCapture(r->capture, hipStreamCaptureModeThreadLocal) != hipSuccess)
         return HIPDECODE_ERR_HIP;
     hipdecode_status st = HIPDECODE_OK;
-    for (int32_t l = 0; l < r->cfg.num_layers && st == HIPDECODE_OK; ++l) {
-        st = hipdecode_kv_append(&ap, r->q[l], r->k_new[l], r->v_new[l], nullptr, r->block_table,
-                                 r->context_lens, r->k_pool[l], r->v_pool[l], r->capture);
-        if (st == HIPDECODE_OK)
-            st = hipdecode_paged_attn(&p, r->q[l], r->k_pool[l], r->v_pool[l], r->block_table, r->context_lens,
-                                      r->out[l], r->lse != nullptr ? r->lse[l] : nullptr, r->workspace,
-                                      r->workspace_bytes, r->capture);
-    }
+    (void)ap;
+    for (int32_t l = 0; l < r->cfg.num_layers && st == HIPDECODE_OK; ++l)
+        st = hipdecode_paged_attn_append(&p, r->cfg.rope_theta, r->q[l], r->k_new[l], r->v_new[l], r->k_pool[l],
+                                         r->v_pool[l], r->block_table, r->context_lens, r->out[l],
+                                         r->lse != nullptr ? r->lse[l] : nullptr, r->workspace, r->workspace_bytes,
+                                         r->capture);
     hipGraph_t graph = nullptr;
     const hipError_t end = hipStreamEndCapture(r->capture, &graph);
     if (st != HIPDECODE_OK || end != hipSuccess || graph == nullptr) {

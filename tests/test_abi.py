@@ -416,3 +416,23 @@ def test_step_runner_rejects_before_allocating():
         == hd.HIPDECODE_ERR_NULL
     assert lib.hipdecode_step_runner_step(None, 1, None, None) == hd.HIPDECODE_ERR_NULL
     assert lib.hipdecode_step_runner_destroy(None) == hd.HIPDECODE_ERR_NULL
+
+
+def test_fused_call_rejects_before_any_launch():
+    lib = hd.library()
+    fake = ctypes.c_void_p(1 << 20)
+    call = lib.hipdecode_paged_attn_append
+    stream_sched = base(schedule=2)
+    assert call(ctypes.byref(stream_sched), 1e6, fake, fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                1 << 30, None) == hd.HIPDECODE_ERR_UNSUPPORTED
+    for theta in (float("nan"), -1.0, float("inf")):
+        assert call(ctypes.byref(base()), theta, fake, fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                    1 << 30, None) == hd.HIPDECODE_ERR_SCALE
+    p = base()
+    ws = hd.hipdecode_workspace_bytes(p)
+    assert call(ctypes.byref(p), 1e6, fake, None, fake, fake, fake, fake, fake, fake, fake, fake, ws,
+                None) == hd.HIPDECODE_ERR_NULL
+    assert call(ctypes.byref(p), 1e6, fake, ctypes.c_void_p((1 << 20) + 4), fake, fake, fake, fake, fake, fake,
+                fake, fake, ws, None) == hd.HIPDECODE_ERR_ALIGN
+    assert call(ctypes.byref(base(num_seqs=0)), 1e6, None, None, None, None, None, None, None, None, None, None, 0,
+                None) == hd.HIPDECODE_OK

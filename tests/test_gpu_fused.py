@@ -1,0 +1,85 @@
+"""GPU parity of the fused decode step (``hipdecode_paged_attn_append``:
+append of each request's new token and attention in one launch) against the
+fp64 oracle doing the two steps in turn.
+
+The bar is the append's and the attention's own: V pools bit-exact, K pools
+bit-exact up to rounding ties of the RoPE rotation, out within 1e-2 and LSE
+within 1e-4 relative of the oracle (plus the rounding-level bound).  Cases
+cover a last page that is partial, full, or a single token, padding rows,
+contexts long enough that the last page sits in the last of many splits,
+group sizes 1, 2 and 4, 4 and 16 wavefronts, fp32 output, and RoPE off.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_decode_gqa_amd as hd
+from tests.gpu_util import DeviceCase, bits_to_bf16, compare, log
+from tests.test_gpu_append import check_rotated, to_bits
+from workloads import make_append_inputs, make_case
+
+pytestmark = pytest.mark.gpu
+
+THETA = 1e6
+CTX = [300, 1, 517, 4096, 0, 2049, 16, 32, 17]
+
+
+def run_case(case, inputs, *, theta, waves=0, partition=0, out_dtype=None, what=""):
+    dc = DeviceCase(case)
+    q = bits_to_bf16(inputs.q)
+    q_before = q.clone()
+    out, lse = hd.paged_attn_append(q, bits_to_bf16(inputs.k_new), bits_to_bf16(inputs.v_new), dc.k, dc.v, dc.table,
+                                    dc.ctx, case.scale, max_context_len=case.max_context_len, rope_theta=theta,
+                                    out_dtype=out_dtype or dc.out_dtype, partition_tokens=partition,
+                                    workgroup_waves=waves)
+    torch.cuda.synchronize()
+    assert torch.equal(q, q_before), f"{what}: q must not be modified"
+    rope = theta > 0
+    kp, vp, q_rot = oracle.kv_append(inputs.k_new, inputs.v_new, case.block_table, case.context_lens, case.k_pool,
+                                     case.v_pool, q=inputs.q, rope=rope, theta=theta if rope else 1e6)
+    ref_out, ref_lse = oracle.paged_attn(q_rot if rope else inputs.q, kp, vp, case.block_table,
+                                         case.context_lens, case.scale)
+    err, lerr = compare(out, lse, ref_out, ref_lse, what=what)
+    gk, gv = to_bits(dc.k), to_bits(dc.v)
+    assert np.array_equal(gv, vp), f"{what}: V pool differs"
+    if rope:
+        for b, c in enumerate(case.context_lens):
+            if c == 0:
+                continue
+            p = int(c) - 1
+            page, slot = int(case.block_table[b, p // 16]), p % 16
+            check_rotated(gk[page, slot], kp[page, slot], inputs.k_new[b], p, theta, f"{what} K")
+        diff = np.any(gk != kp, axis=(2, 3))
+        written = {(int(case.block_table[b, (int(c) - 1) // 16]), (int(c) - 1) % 16)
+                   for b, c in enumerate(case.context_lens) if c > 0}
+        assert all((int(p), int(s)) in written for p, s in np.argwhere(diff)), f"{what}: K changed elsewhere"
+    else:
+        assert np.array_equal(gk, kp), f"{what}: K pool differs"
+    log(f"[fused] {what}: max|dout|={err:.2e} max rel dlse={lerr:.2e}")
+
+
+@pytest.mark.parametrize("theta", [THETA, 0.0])
+def test_fused_mixed_contexts(theta):
+    case = make_case(CTX, seed=71, pool_pages=800)
+    run_case(case, make_append_inputs(case, None, seed=71), theta=theta, what=f"mixed theta={theta}")
+
+
+@pytest.mark.parametrize("waves,partition", [(4, 0), (4, 64), (16, 0), (16, 256)])
+def test_fused_splits_and_waves(waves, partition):
+    case = make_case([28672, 1000, 64], seed=72, pool_pages=1900)
+    run_case(case, make_append_inputs(case, None, seed=72), theta=THETA, waves=waves, partition=partition,
+             what=f"waves={waves} part={partition}")
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 4), (32, 16)])
+def test_fused_group_sizes(hq, hkv):
+    case = make_case([700, 33, 1500, 16], seed=73, Hq=hq, Hkv=hkv, pool_pages=200)
+    run_case(case, make_append_inputs(case, None, seed=73), theta=THETA, what=f"{hq}/{hkv}")
+
+
+def test_fused_fp32_out():
+    case = make_case([512, 97], seed=74, pool_pages=64)
+    run_case(case, make_append_inputs(case, None, seed=74), theta=THETA, out_dtype=torch.float32, what="fp32")
