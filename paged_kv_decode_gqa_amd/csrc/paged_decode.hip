@@ -10,8 +10,10 @@
 // Two schedules share everything below the workgroup level.
 //
 //  * split: one workgroup per (request b, KV head g, partition of the
-//    context).  The grid is sized by the host's max_context_len; partitions
-//    past a request's length exit at once.
+//    context).  The grid is sized by the host's max_context_len.  In a
+//    ragged batch the workgroups map onto the real (request, partition)
+//    units in order, so the slots past the last one, not slots scattered
+//    through the grid, are the ones that exit at once.
 //  * stream: a fixed number W of workgroups (the resident count) take equal
 //    contiguous slices of the flattened (request, KV head, page) sequence,
 //    so a batch of very different context lengths still keeps every CU busy
@@ -405,9 +407,63 @@ __device__ __forceinline__ int clamp_ctx(int ctx, int max_ctx)
     return ctx < 0 ? 0 : (ctx > max_ctx ? max_ctx : ctx);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wavefront: four DPP row shifts
+// sum inside each row of 16 lanes, then the rows' totals (read into scalar
+// registers) are added to the rows after them.
+__device__ __forceinline__ int wave_inclusive_scan(int v, int lane)
+{
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);   // row_shr:8
+    const int r0 = __builtin_amdgcn_readlane(v, 15);
+    const int r1 = __builtin_amdgcn_readlane(v, 31);
+    const int r2 = __builtin_amdgcn_readlane(v, 47);
+    const int row = lane >> 4;
+    return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
+
+// The split schedule's work list.  The grid has a slot for every partition
+// the longest context could need, but a ragged batch has far fewer real
+// (request, partition) units.  Unit u is the u-th real unit in request order,
+// partitions ascending; an empty request counts one unit, which writes its
+// empty output.  Slots past the last real unit get b = -1 and exit, so every
+// workgroup the dispatcher places early carries work.
+struct RealUnit {
+    int b, split, ctx;
+};
+
+__device__ __forceinline__ RealUnit real_unit(const DecodeArgs &a, int u)
+{
+    const int lane = (int)(threadIdx.x & 63);
+    const int span = kPageSize * a.partition_pages;
+    RealUnit r{-1, 0, 0};
+    int carry = 0;
+    for (int c0 = 0; c0 < a.num_seqs; c0 += 64) {
+        const int j = c0 + lane;
+        const int cj = j < a.num_seqs ? clamp_ctx(a.context_lens[j], a.max_context_len) : 0;
+        const int nj = j < a.num_seqs ? max(1, (cj + span - 1) / span) : 0;
+        const int incl = wave_inclusive_scan(nj, lane);
+        const int excl = incl - nj;
+        const unsigned long long hit = __ballot(u >= carry + excl && u < carry + incl);
+        if (hit != 0ull) {
+            const int l = __builtin_amdgcn_readfirstlane(__ffsll(hit) - 1);
+            r.b = c0 + l;
+            r.split = u - carry - __builtin_amdgcn_readlane(excl, l);
+            r.ctx = __builtin_amdgcn_readlane(cj, l);
+            break;
+        }
+        carry += __builtin_amdgcn_readlane(incl, 63);
+    }
+    return r;
+}
+
 // ---------------------------------------------------------------------------
-// split schedule: workgroup = (request, split, KV head), KV head fastest so
-// consecutive workgroups read neighbouring head rows of the same pages.
+// split schedule: workgroup = (real unit, KV head), KV head fastest so
+// consecutive workgroups read neighbouring head rows of the same pages.  A
+// single request, or a batch with one partition per request, maps the grid
+// directly (unit = request * nsplit_max + partition; units past a request's
+// partition count exit); any other batch goes through real_unit().
 // ---------------------------------------------------------------------------
 template <int G, int WAVES, bool OUT_F32, bool FUSED>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4)))
@@ -418,30 +474,53 @@ void paged_decode_kernel(DecodeArgs a)
     const int Hkv = a.num_kv_heads;
     const int g = blockIdx.x % Hkv;
     const int rest = blockIdx.x / Hkv;
-    const int split = rest % a.nsplit_max;
-    const int b = rest / a.nsplit_max;
+    const int pp = a.partition_pages;
+    // Unit `rest` in the full grid: request rest / nsplit_max, partition rest % nsplit_max.
+    const int b_full = rest / a.nsplit_max;
+    const int split_full = rest % a.nsplit_max;
 
     // Issued before the context length arrives: lane i of each wavefront
     // fetches the table entry of its i-th page of this partition, bounded by
     // the table row (entries past the request's pages are never used).
-    const int32_t *trow = a.block_table + (size_t)b * a.max_blocks;
-    const int p_begin = split * a.partition_pages;
-    const int spec_idx = p_begin + ln.wave + WAVES * ln.lane;
-    const int spec_entry =
-        (spec_idx < a.max_blocks && ln.lane * WAVES < a.partition_pages) ? trow[spec_idx] : -1;
+    const int spec_idx = split_full * pp + ln.wave + WAVES * ln.lane;
+    const int spec_full = (spec_idx < a.max_blocks && ln.lane * WAVES < pp)
+                              ? a.block_table[(size_t)b_full * a.max_blocks + spec_idx] : -1;
 
-    const int ctx = clamp_ctx(a.context_lens[b], a.max_context_len);
+    int b, split, ctx, spec_entry;
+    if (a.num_seqs == 1 || a.nsplit_max == 1) {
+        // Every unit of the full grid up to a request's partition count is real.
+        b = b_full;
+        split = split_full;
+        ctx = clamp_ctx(a.context_lens[b], a.max_context_len);
+        spec_entry = spec_full;
+        const int nsplit_b = (ctx + kPageSize * pp - 1) / (kPageSize * pp);
+        if (ctx == 0 ? split != 0 : split >= nsplit_b)
+            return;
+    } else {
+        const RealUnit u = real_unit(a, rest);
+        const int span = kPageSize * pp;
+        if (u.b < 0 || u.split < 0 || u.split >= max(1, (u.ctx + span - 1) / span))
+            return;   // past the last real unit
+        b = u.b;
+        split = u.split;
+        ctx = u.ctx;
+        spec_entry = spec_full;
+        if (b != b_full || split != split_full) {   // ragged batch: fetch this partition's entries
+            const int idx = split * pp + ln.wave + WAVES * ln.lane;
+            spec_entry = (idx < a.max_blocks && ln.lane * WAVES < pp)
+                             ? a.block_table[(size_t)b * a.max_blocks + idx] : -1;
+        }
+    }
+    const int32_t *trow = a.block_table + (size_t)b * a.max_blocks;
+    const int p_begin = split * pp;
     const int n_pages = (ctx + kPageSize - 1) / kPageSize;
-    const int nsplit_b = (n_pages + a.partition_pages - 1) / a.partition_pages;
+    const int nsplit_b = (n_pages + pp - 1) / pp;
     const size_t row0 = (size_t)b * a.num_q_heads + (size_t)g * G;   // first query row of the group
 
     if (ctx == 0) {
-        if (split == 0)
-            write_empty<OUT_F32>(a, row0, G, ln.tid, 64 * WAVES);
+        write_empty<OUT_F32>(a, row0, G, ln.tid, 64 * WAVES);
         return;
     }
-    if (split >= nsplit_b)
-        return;
 
     u32x4 qv[G];
     load_q<G>(qv, a, row0, ln.sub);

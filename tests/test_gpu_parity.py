@@ -252,3 +252,21 @@ def test_maximum_split_count():
     # 65536 tokens at 64-token partitions: 1024 partials per (request, KV head)
     case = make_case([65536, 100], seed=23)
     _check(case, "1024 splits", partition_tokens=64)
+
+
+WORK_LIST_CASES = {
+    # more requests than one wavefront's lanes, so the unit scan runs over several chunks
+    "65 mixed with empties": [0 if i % 9 == 4 else int(x) for i, x in
+                              enumerate(np.random.default_rng(40).integers(1, 3000, size=65))],
+    "130 log-uniform": [int(np.exp(x)) for x in np.random.default_rng(41).uniform(np.log(16), np.log(9000), 130)],
+    "long first then short": [20000] + [40] * 70,
+    "short first then long": [40] * 70 + [20000],
+    "leading and trailing empties": [0, 0, 5000, 0, 129, 0, 0],
+}
+
+
+@pytest.mark.parametrize("partition", [0, 64, 1024])
+@pytest.mark.parametrize("name", sorted(WORK_LIST_CASES))
+def test_split_work_list(name, partition):
+    case = make_case(WORK_LIST_CASES[name], seed=42, poison=True)
+    _check(case, f"work list: {name}, partition {partition}", partition_tokens=partition)
