@@ -42,13 +42,15 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kPfWaves = 8;
 constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kRowsPerWave = 32;          // one 32x32 MFMA tile of (token, head) rows
-constexpr int kKeys = 64;                 // keys per LDS step: four pages, used in two halves of 32
-constexpr int kKStride = kHeadDim + 8;    // LDS K row, bf16 elements (16 B of padding)
-constexpr int kVStride = kKeys + 8;       // LDS V^T row (one dimension), bf16 elements
+constexpr int kKeys = 64;                 // keys per step: four pages, used in two halves of 32
+constexpr int kRowBytes = kHeadDim * 2;   // one K or V row in LDS: 16 chunks of 16 bytes
+constexpr int kStepBytes = kKeys * kRowBytes;
+constexpr int kStages = 3;                // LDS stages: the copy runs two steps ahead
 constexpr int kDimBlocks = kHeadDim / 32; // O^T is four 32x32 accumulators
 constexpr float kNegBig = -1.0e30f;       // running-max start: finite, so no inf - inf
 constexpr int64_t kMaxGrid = (int64_t)1 << 31;
@@ -73,8 +75,16 @@ struct PrefillArgs {
     uint32_t q_sign;        // 0x80008000 when scale < 0: q is negated on load instead
 };
 
-// Position of key index t inside an LDS row of V^T: bits 2 and 3 swapped.
-__device__ inline int vt_slot(int t) { return (t & ~0xC) | ((t & 4) << 1) | ((t & 8) >> 1); }
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
+
+// LDS rows are stored with their 16-byte chunks permuted: chunk c of step
+// row r sits at position c ^ swz(r).  Eight consecutive rows then put any one
+// chunk in eight different bank groups (the K reads of the first product),
+// and the four rows of a transposing V read put their 32-byte pieces in four
+// different ones; swz keeps chunk pairs (2i, 2i + 1) together.
+__device__ inline int swz(int r) { return 2 * (r & 7); }
 
 __device__ inline float pair_max(float x)
 {
@@ -103,13 +113,53 @@ __device__ inline uint32_t pack2_bf16(float x, float y)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
+// Wait until at most N of this wavefront's vector-memory loads are
+// outstanding (the copies into LDS count among them).
+template <int N>
+__device__ inline void wait_vm()
+{
+    static_assert(N >= 0 && N < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | N);   // expcnt and lgkmcnt left at their maxima
+}
+
+// Workgroup barrier for the LDS stages.  A plain s_barrier: every wavefront
+// has already waited for its own copies (wait_vm) and consumed its LDS reads,
+// and a fence here would make the compiler wait for all loads, including the
+// copies still running for later steps.  The memory clobber keeps LDS accesses
+// on their side of it.
+__device__ inline void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Copy 16 bytes per lane from global memory (uniform base + 32-bit lane
+// offset) straight into LDS: lane i lands at byte lds_addr + 16 i.  Written
+// out here, rather than through the compiler's builtin, because the compiler
+// then waits for every such copy before any LDS read, which would leave no
+// copy in flight behind the compute; the waits are wait_vm() calls instead.
+__device__ inline void copy_to_lds(const uint8_t *base, uint32_t off, const lds_u8_t *dst)
+{
+    const uint32_t lds_addr = (uint32_t)(uintptr_t)dst;
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(off), "s"(base), "s"(lds_addr)
+                 : "memory", "m0");
+}
+
+// A wave-uniform 4-byte load through the scalar cache, waited for at once.
+// Its wait (lgkmcnt) is independent of the copies into LDS (vmcnt), which a
+// vector load of the same value would have to wait behind.
+__device__ inline int scalar_load(const int32_t *p)
+{
+    int v;
+    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+    return v;
+}
+
 template <int G, bool OUT_F32>
 __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
 {
     constexpr int kTokPerWave = kRowsPerWave / G;
     constexpr int kTileTokens = kPfWaves * kTokPerWave;
-    __shared__ __align__(16) uint16_t k_lds[2][kKeys * kKStride];
-    __shared__ __align__(16) uint16_t vt_lds[2][kHeadDim * kVStride];
+    __shared__ __align__(16) uint8_t k_lds[kStages][kStepBytes];
+    __shared__ __align__(16) uint8_t v_lds[kStages][kStepBytes];
 
     // KV head fastest, heavier (later) tiles first.
     const int bid = blockIdx.x;
@@ -161,39 +211,59 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
     const int nblk = (kv_end + kKeys - 1) / kKeys;
     const int full_blk = (ctx - n + t0 + 1) / kKeys;      // steps with no masked key in any row
 
-    // Staging: for K, thread tid moves dims 8 dc .. 8 dc + 7 of keys 2 tp and
-    // 2 tp + 1 (always on one page; 16 consecutive threads read a key's whole
-    // row).  For V the key pair varies fastest instead (vp = tid % 32, dims
-    // 8 vd .. 8 vd + 7 with vd = tid / 32), so that the transposed 4-byte
-    // writes of one wavefront -- 32 key pairs of two dimensions -- fall on 64
-    // different LDS banks.  Pipeline: at step kb the K/V loads of step kb + 2
-    // are issued, with a page id fetched one step earlier, and the page id of
-    // step kb + 3 is fetched; step kb + 1 goes from registers to LDS at the end
-    // of step kb.  Keys past kv_end are clamped to the last one (masked).
-    const int dc = tid & 15;
-    const int tp = tid >> 4;
-    const int vp = tid & 31;
-    const int vd = tid >> 5;
-    const size_t kv_row = (size_t)a.num_kv_heads * kHeadDim;
+    // Copies into LDS.  Wavefront w moves step rows 8w .. 8w + 7 of K and of
+    // V -- eight consecutive keys, so one page -- as two 1 KiB copies of four
+    // rows each (global_load_lds: lane i lands at byte 16 i of the copy).
+    // Lane i takes row 4k + i / 16 of the pair and fetches the chunk whose
+    // swizzled position is i % 16.  Keys past kv_end are fetched as key
+    // kv_end - 1, so masked keys still hold finite values (their weight is an
+    // exact 0, and 0 times a finite V is 0).
+    const int drow = lane >> 4;
+    const uint32_t kv_row_bytes = (uint32_t)a.num_kv_heads * kRowBytes;
+    const size_t page_bytes = (size_t)kPageSize * kv_row_bytes;
+    const uint8_t *k_bytes = reinterpret_cast<const uint8_t *>(a.k_pool) + (size_t)g * kRowBytes;
+    const uint8_t *v_bytes = reinterpret_cast<const uint8_t *>(a.v_pool) + (size_t)g * kRowBytes;
+    uint32_t chunk_off[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+        chunk_off[k] = (uint32_t)(((lane & 15) ^ swz(8 * w + 4 * k + drow)) * 16);
     const int32_t *table = a.block_table + (size_t)b * a.max_blocks;
-    auto first_key = [&](int kb) __attribute__((always_inline)) { return min(kb * kKeys + 2 * tp, kv_end - 1); };
-    auto page_of = [&](int kb) __attribute__((always_inline)) {
-        const int blk = min(first_key(kb) / kPageSize, a.max_blocks - 1);
-        const int page = table[blk];
-        return (unsigned)page < (unsigned)a.num_pages ? page : 0;
+    auto issue = [&](int kb, int stage) __attribute__((always_inline)) {
+        const int key_w = kb * kKeys + 8 * w;                // first of this wavefront's eight keys
+        const int pidx = min(key_w, kv_end - 1) / kPageSize;
+        int page = scalar_load(table + pidx);
+        page = (unsigned)page < (unsigned)a.num_pages ? page : 0;
+        const size_t pbase = (size_t)page * page_bytes;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int key = min(key_w + 4 * k + drow, kv_end - 1);
+            const uint32_t off = (uint32_t)(key % kPageSize) * kv_row_bytes + chunk_off[k];
+            const int r0 = 8 * w + 4 * k;
+            copy_to_lds(k_bytes + pbase, off, (const lds_u8_t *)&k_lds[stage][r0 * kRowBytes]);
+            copy_to_lds(v_bytes + pbase, off, (const lds_u8_t *)&v_lds[stage][r0 * kRowBytes]);
+        }
     };
-    auto v_first_key = [&](int kb) __attribute__((always_inline)) { return min(kb * kKeys + 2 * vp, kv_end - 1); };
-    auto v_page_of = [&](int kb) __attribute__((always_inline)) {
-        const int blk = min(v_first_key(kb) / kPageSize, a.max_blocks - 1);
-        const int page = table[blk];
-        return (unsigned)page < (unsigned)a.num_pages ? page : 0;
-    };
-    auto offsets = [&](int key0, int page, int chunk, size_t &o0, size_t &o1) __attribute__((always_inline)) {
-        const int key1 = min(key0 + 1, kv_end - 1);
-        const size_t base = (size_t)page * kPageSize * kv_row + (size_t)g * kHeadDim + chunk * 8;
-        o0 = base + (size_t)(key0 % kPageSize) * kv_row;
-        o1 = base + (size_t)(key1 % kPageSize) * kv_row;
-    };
+
+    // LDS read offsets inside a stage.  K operand of S^T: row 32 hh + j,
+    // chunk 2 ks + half.  V^T operand of O^T (two transposing 8-byte reads per
+    // MFMA): in the 16-lane group q = lane / 16, lane i reads row
+    // 4 (q / 2) + i / 4 (plus 16 kh + 8 e + 32 hh) at dims 32 db + 16 (q % 2) +
+    // 4 (i % 4); the read hands lane i the four rows' values of dim
+    // 32 db + 16 (q % 2) + i, which is the A layout (row = dim, k = key).
+    uint32_t k_off[kHeadDim / 16];
+#pragma unroll
+    for (int ks = 0; ks < kHeadDim / 16; ++ks)
+        k_off[ks] = (uint32_t)(j * kRowBytes + ((2 * ks + half) ^ swz(j)) * 16);
+    uint32_t v_off[kDimBlocks];
+    {
+        const int q = lane >> 4;
+        const int i = lane & 15;
+        const int vr = 4 * (q >> 1) + (i >> 2);
+#pragma unroll
+        for (int db = 0; db < kDimBlocks; ++db)
+            v_off[db] = (uint32_t)(vr * kRowBytes + ((4 * db + 2 * (q & 1) + ((i & 3) >> 1)) ^ swz(vr)) * 16 +
+                                   8 * (i & 1));
+    }
 
     f32x16_t acc[kDimBlocks];
 #pragma unroll
@@ -202,19 +272,20 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
     float m_run = kNegBig;
     float l_run = 0.f;
 
-    auto scores = [&](int buf, int hh) __attribute__((always_inline)) {
+    auto scores = [&](int stage, int hh) __attribute__((always_inline)) {
         // S^T = K Q^T for keys 32 hh .. 32 hh + 31 of this step
-        f32x16_t s = zero16();
-        const uint16_t *kl = &k_lds[buf][(32 * hh + j) * kKStride + 8 * half];
+        const uint8_t *kl = &k_lds[stage][32 * hh * kRowBytes];
+        bf16x8_t kop[kHeadDim / 16];
 #pragma unroll
-        for (int ks = 0; ks < kHeadDim / 16; ++ks) {
-            const bf16x8_t kop = *reinterpret_cast<const bf16x8_t *>(kl + 16 * ks);
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[ks], s, 0, 0, 0);
-        }
+        for (int ks = 0; ks < kHeadDim / 16; ++ks)
+            kop[ks] = *reinterpret_cast<const bf16x8_t *>(kl + k_off[ks]);
+        f32x16_t s = zero16();
+#pragma unroll
+        for (int ks = 0; ks < kHeadDim / 16; ++ks)
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qop[ks], s, 0, 0, 0);
         return s;
     };
-    auto softmax_pv = [&](int kb, int buf, int hh, f32x16_t s) __attribute__((always_inline)) {
-
+    auto softmax_pv = [&](int kb, int stage, int hh, f32x16_t s) __attribute__((always_inline)) {
         // Online softmax in base 2 (row j; keys 8(r/4) + 4 half + r%4).  With
         // c = |scale| log2(e) > 0, the row maximum of c s is c max(s) and
         // p = 2^(c s - m) is one FMA and one v_exp_f32 (weights below 2^-126
@@ -251,97 +322,54 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
                 acc[db] *= alpha;
         }
 
-        // O^T += V^T P^T, two k-steps of 16 keys
-        const uint16_t *vl = &vt_lds[buf][j * kVStride + 32 * hh + 8 * half];
+        // O^T += V^T P^T, two k-steps of 16 keys.  P^T: lane l holds keys
+        // 16 kh + 4 half + e and 16 kh + 8 + 4 half + e (e < 4) of this half,
+        // in the S^T accumulator's own order; the V^T reads take the same keys.
+        const lds_u8_t *vl = (const lds_u8_t *)&v_lds[stage][32 * hh * kRowBytes];
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
             const uint4 u = make_uint4(pp[4 * kh], pp[4 * kh + 1], pp[4 * kh + 2], pp[4 * kh + 3]);
             const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, u);
 #pragma unroll
             for (int db = 0; db < kDimBlocks; ++db) {
-                const bf16x8_t vop = *reinterpret_cast<const bf16x8_t *>(vl + (32 * db) * kVStride + 16 * kh);
-                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop, acc[db], 0, 0, 0);
+                const lds_u8_t *p = vl + 16 * kh * kRowBytes + v_off[db];
+                const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p);
+                const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(p + 8 * kRowBytes));
+                const i16x8_t v8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, v8), pop,
+                                                                  acc[db], 0, 0, 0);
             }
         }
     };
     // Both halves' scores are issued first: the matrix cores work on the
     // second half's S while the first half's softmax runs on the VALU, and on
-    // the first half's P.V while the second softmax runs.  (Staggering the
-    // second wavefront of each SIMD by half a step, with a third LDS buffer,
-    // measured 12% slower: it takes the kernel to 256 registers.)
-    auto compute_step = [&](int kb, int buf) __attribute__((always_inline)) {
-        const f32x16_t s0 = scores(buf, 0);
-        const f32x16_t s1 = scores(buf, 1);
-        softmax_pv(kb, buf, 0, s0);
-        softmax_pv(kb, buf, 1, s1);
+    // the first half's P.V while the second softmax runs.
+    auto compute_step = [&](int kb, int stage) __attribute__((always_inline)) {
+        const f32x16_t s0 = scores(stage, 0);
+        const f32x16_t s1 = scores(stage, 1);
+        softmax_pv(kb, stage, 0, s0);
+        softmax_pv(kb, stage, 1, s1);
     };
 
-    // Two register stages, A and B, alternate; the loop is unrolled by two so
-    // that every register is named statically.
-    uint4 a_k0, a_k1, a_v0, a_v1, b_k0, b_k1, b_v0, b_v1;
-#define HIPDECODE_PF_LOAD(P, KB, PAGE, VPAGE)                                   \
-    do {                                                                        \
-        size_t o0_, o1_;                                                        \
-        offsets(first_key(KB), (PAGE), dc, o0_, o1_);                           \
-        P##_k0 = *reinterpret_cast<const uint4 *>(a.k_pool + o0_);              \
-        P##_k1 = *reinterpret_cast<const uint4 *>(a.k_pool + o1_);              \
-        offsets(v_first_key(KB), (VPAGE), vd, o0_, o1_);                        \
-        P##_v0 = *reinterpret_cast<const uint4 *>(a.v_pool + o0_);              \
-        P##_v1 = *reinterpret_cast<const uint4 *>(a.v_pool + o1_);              \
-    } while (0)
-#define HIPDECODE_PF_STORE(P, BUF) store_step(P##_k0, P##_k1, P##_v0, P##_v1, (BUF))
-    auto store_step = [&](uint4 k0, uint4 k1, uint4 v0, uint4 v1, int buf) __attribute__((always_inline)) {
-        *reinterpret_cast<uint4 *>(&k_lds[buf][(2 * tp) * kKStride + dc * 8]) = k0;
-        *reinterpret_cast<uint4 *>(&k_lds[buf][(2 * tp + 1) * kKStride + dc * 8]) = k1;
-        // V^T: dimensions 8 vd + 2 i and 8 vd + 2 i + 1, keys 2 vp and 2 vp + 1 side by side
-        uint16_t *vt = &vt_lds[buf][(vd * 8) * kVStride + vt_slot(2 * vp)];
-        const uint32_t x0[4] = {v0.x, v0.y, v0.z, v0.w};
-        const uint32_t x1[4] = {v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            *reinterpret_cast<uint32_t *>(vt + (2 * i) * kVStride) = (x0[i] & 0xFFFFu) | (x1[i] << 16);
-            *reinterpret_cast<uint32_t *>(vt + (2 * i + 1) * kVStride) = (x0[i] >> 16) | (x1[i] & 0xFFFF0000u);
-        }
-    };
-
-    int page_ahead = 0, vpage_ahead = 0;      // pages of step kb + 2 (K and V mappings)
-    HIPDECODE_PF_LOAD(a, 0, page_of(0), v_page_of(0));
+    // Pipeline: step kb + 2 is copied into LDS while step kb is computed.
+    // Per step each wavefront issues four copies; before the barrier of step
+    // kb it waits until only step kb + 1's four may still be in flight.
+    issue(0, 0);
     if (nblk > 1)
-        HIPDECODE_PF_LOAD(b, 1, page_of(1), v_page_of(1));
-    if (nblk > 2) {
-        page_ahead = page_of(2);
-        vpage_ahead = v_page_of(2);
-    }
-    HIPDECODE_PF_STORE(a, 0);
-    __syncthreads();
-    for (int kb = 0; kb < nblk; kb += 2) {
-        // step kb: A is free (step kb is in LDS), B holds step kb + 1
-        if (kb + 2 < nblk)
-            HIPDECODE_PF_LOAD(a, kb + 2, page_ahead, vpage_ahead);
-        if (kb + 3 < nblk) {
-            page_ahead = page_of(kb + 3);
-            vpage_ahead = v_page_of(kb + 3);
-        }
-        compute_step(kb, 0);
+        issue(1, 1);
+    wait_vm<0>();   // q and the first copies: nothing older than a step's copies stays in flight in the loop
+    int stage = 0;
+    for (int kb = 0; kb < nblk; ++kb) {
         if (kb + 1 < nblk)
-            HIPDECODE_PF_STORE(b, 1);
-        __syncthreads();
-        if (kb + 1 >= nblk)
-            break;
-        // step kb + 1: B is free, A holds step kb + 2
-        if (kb + 3 < nblk)
-            HIPDECODE_PF_LOAD(b, kb + 3, page_ahead, vpage_ahead);
-        if (kb + 4 < nblk) {
-            page_ahead = page_of(kb + 4);
-            vpage_ahead = v_page_of(kb + 4);
-        }
-        compute_step(kb + 1, 1);
+            wait_vm<4>();
+        else
+            wait_vm<0>();
+        stage_barrier();
         if (kb + 2 < nblk)
-            HIPDECODE_PF_STORE(a, 0);
-        __syncthreads();
+            issue(kb + 2, stage == 0 ? 2 : stage - 1);
+        compute_step(kb, stage);
+        stage = stage == kStages - 1 ? 0 : stage + 1;
     }
-#undef HIPDECODE_PF_LOAD
-#undef HIPDECODE_PF_STORE
 
     // Rows: out[row][h][dim], dims 32 db + 8 (r/4) + 4 half + r%4.
     const float l_tot = pair_sum(l_run);

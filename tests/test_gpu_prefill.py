@@ -83,6 +83,17 @@ def test_prefill_ragged_chunks():
     check_full(case, inp, o, l, "ragged chunks")
 
 
+def test_prefill_poisoned_unused_slots():
+    # Unused slots of last pages and unused pool pages hold NaN; keys past a
+    # tile's last position are masked, and must not turn the output into NaN.
+    ctx = [301, 77, 1000, 16, 129, 4097]
+    new = [301, 5, 64, 16, 128, 1000]
+    case, inp = make_prefill_case(ctx, new, seed=44, poison=True,
+                                  pool_pages=sum((c + 15) // 16 for c in ctx) + 9)
+    o, l = run_gpu(case, inp)
+    check_full(case, inp, o, l, "poisoned unused slots")
+
+
 @pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 4), (4, 1), (32, 16)])
 def test_prefill_group_shapes(hq, hkv):
     case, inp = make_prefill_case([200, 70, 513], [200, 33, 129], seed=42, Hq=hq, Hkv=hkv)

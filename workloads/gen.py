@@ -431,12 +431,14 @@ class PrefillInputs:
 
 def make_prefill_case(ctx_lens, new_lens, *, seed: int = 0, Hq: int = HQ, Hkv: int = HKV,
                       pool_pages: int | None = None, max_blocks: int | None = None, extra_rows: int = 0,
-                      threads: int | None = None, name: str = "prefill") -> tuple[Case, PrefillInputs]:
+                      poison: bool = False, threads: int | None = None,
+                      name: str = "prefill") -> tuple[Case, PrefillInputs]:
     """A full cache (``make_case``) and the query rows of one chunk per
     request: the last ``new_lens[b]`` tokens of request b's context.  The
-    rows come from the append generator's q stream."""
+    rows come from the append generator's q stream.  ``poison`` fills every
+    slot no context covers with NaN."""
     case = make_case(ctx_lens, seed=seed, Hq=Hq, Hkv=Hkv, pool_pages=pool_pages, max_blocks=max_blocks,
-                     threads=threads, name=name)
+                     poison=poison, threads=threads, name=name)
     rows = make_append_inputs(case, new_lens, seed=seed, extra_rows=extra_rows)
     return case, PrefillInputs(q=rows.q, new_start=rows.new_start, max_new_tokens=rows.max_new_tokens)
 
