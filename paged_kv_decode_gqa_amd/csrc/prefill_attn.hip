@@ -80,11 +80,16 @@ typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
 
 // LDS rows are stored with their 16-byte chunks permuted: chunk c of step
-// row r sits at position c ^ swz(r).  Eight consecutive rows then put any one
-// chunk in eight different bank groups (the K reads of the first product),
-// and the four rows of a transposing V read put their 32-byte pieces in four
-// different ones; swz keeps chunk pairs (2i, 2i + 1) together.
-__device__ inline int swz(int r) { return 2 * (r & 7); }
+// row r sits at position c ^ swz(r), with a different permutation for K and
+// for V to suit their reads.  K is read 16 bytes per lane, one chunk of rows
+// j = 0..31: swz_k(r) = r mod 16 puts sixteen consecutive rows' chunk in
+// sixteen different positions.  V is read with transposing 8-byte reads, in
+// which 32 lanes touch chunks 4 db .. 4 db + 3 of four consecutive rows:
+// swz_v spreads those 16 (row, chunk) pairs over all 16 positions.  Either
+// way no two lanes of one LDS cycle meet in a bank, for 64 banks (256 bytes a
+// cycle) as for 32.
+__device__ inline int swz_k(int r) { return r & 15; }
+__device__ inline int swz_v(int r) { return ((r & 3) << 2) | (r & 2); }
 
 __device__ inline float pair_max(float x)
 {
@@ -215,7 +220,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
     // V -- eight consecutive keys, so one page -- as two 1 KiB copies of four
     // rows each (global_load_lds: lane i lands at byte 16 i of the copy).
     // Lane i takes row 4k + i / 16 of the pair and fetches the chunk whose
-    // swizzled position is i % 16.  Keys past kv_end are fetched as key
+    // permuted position is i % 16.  Keys past kv_end are fetched as key
     // kv_end - 1, so masked keys still hold finite values (their weight is an
     // exact 0, and 0 times a finite V is 0).
     const int drow = lane >> 4;
@@ -223,10 +228,13 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
     const size_t page_bytes = (size_t)kPageSize * kv_row_bytes;
     const uint8_t *k_bytes = reinterpret_cast<const uint8_t *>(a.k_pool) + (size_t)g * kRowBytes;
     const uint8_t *v_bytes = reinterpret_cast<const uint8_t *>(a.v_pool) + (size_t)g * kRowBytes;
-    uint32_t chunk_off[2];
+    uint32_t k_chunk[2], v_chunk[2];
 #pragma unroll
-    for (int k = 0; k < 2; ++k)
-        chunk_off[k] = (uint32_t)(((lane & 15) ^ swz(8 * w + 4 * k + drow)) * 16);
+    for (int k = 0; k < 2; ++k) {
+        const int r = 8 * w + 4 * k + drow;
+        k_chunk[k] = (uint32_t)(((lane & 15) ^ swz_k(r)) * 16);
+        v_chunk[k] = (uint32_t)(((lane & 15) ^ swz_v(r)) * 16);
+    }
     const int32_t *table = a.block_table + (size_t)b * a.max_blocks;
     auto issue = [&](int kb, int stage) __attribute__((always_inline)) {
         const int key_w = kb * kKeys + 8 * w;                // first of this wavefront's eight keys
@@ -237,10 +245,10 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const int key = min(key_w + 4 * k + drow, kv_end - 1);
-            const uint32_t off = (uint32_t)(key % kPageSize) * kv_row_bytes + chunk_off[k];
+            const uint32_t row_off = (uint32_t)(key % kPageSize) * kv_row_bytes;
             const int r0 = 8 * w + 4 * k;
-            copy_to_lds(k_bytes + pbase, off, (const lds_u8_t *)&k_lds[stage][r0 * kRowBytes]);
-            copy_to_lds(v_bytes + pbase, off, (const lds_u8_t *)&v_lds[stage][r0 * kRowBytes]);
+            copy_to_lds(k_bytes + pbase, row_off + k_chunk[k], (const lds_u8_t *)&k_lds[stage][r0 * kRowBytes]);
+            copy_to_lds(v_bytes + pbase, row_off + v_chunk[k], (const lds_u8_t *)&v_lds[stage][r0 * kRowBytes]);
         }
     };
 
@@ -253,7 +261,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
     uint32_t k_off[kHeadDim / 16];
 #pragma unroll
     for (int ks = 0; ks < kHeadDim / 16; ++ks)
-        k_off[ks] = (uint32_t)(j * kRowBytes + ((2 * ks + half) ^ swz(j)) * 16);
+        k_off[ks] = (uint32_t)(j * kRowBytes + ((2 * ks + half) ^ swz_k(j)) * 16);
     uint32_t v_off[kDimBlocks];
     {
         const int q = lane >> 4;
@@ -261,7 +269,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
         const int vr = 4 * (q >> 1) + (i >> 2);
 #pragma unroll
         for (int db = 0; db < kDimBlocks; ++db)
-            v_off[db] = (uint32_t)(vr * kRowBytes + ((4 * db + 2 * (q & 1) + ((i & 3) >> 1)) ^ swz(vr)) * 16 +
+            v_off[db] = (uint32_t)(vr * kRowBytes + ((4 * db + 2 * (q & 1) + ((i & 3) >> 1)) ^ swz_v(vr)) * 16 +
                                    8 * (i & 1));
     }
 
