@@ -34,6 +34,7 @@
 #include "internal.h"
 
 #include <math.h>
+#include <type_traits>
 
 namespace hipdecode {
 namespace {
@@ -53,6 +54,7 @@ constexpr int kStepBytes = kKeys * kRowBytes;
 constexpr int kStages = 3;                // LDS stages: the copy runs two steps ahead
 constexpr int kDimBlocks = kHeadDim / 32; // O^T is four 32x32 accumulators
 constexpr float kNegBig = -1.0e30f;       // running-max start: finite, so no inf - inf
+constexpr float kMaxSlack = 8.0f;         // log2 units a row maximum may exceed the running max
 constexpr int64_t kMaxGrid = (int64_t)1 << 31;
 
 struct PrefillArgs {
@@ -293,13 +295,13 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qop[ks], s, 0, 0, 0);
         return s;
     };
-    auto softmax_pv = [&](int kb, int stage, int hh, f32x16_t s) __attribute__((always_inline)) {
+    auto softmax_pv = [&](auto masked, int kb, int stage, int hh, f32x16_t s) __attribute__((always_inline)) {
         // Online softmax in base 2 (row j; keys 8(r/4) + 4 half + r%4).  With
         // c = |scale| log2(e) > 0, the row maximum of c s is c max(s) and
         // p = 2^(c s - m) is one FMA and one v_exp_f32 (weights below 2^-126
         // of the row maximum may flush to zero); a masked score is -inf, so
         // its weight is exactly 0.
-        if (kb >= full_blk) {  // only steps reaching past the tile's first position
+        if constexpr (decltype(masked)::value) {  // only steps reaching past the tile's first position
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int key = kb * kKeys + 32 * hh + 8 * (r / 4) + 4 * half + (r % 4);
@@ -311,8 +313,14 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
         for (int r = 0; r < 16; ++r)
             mx = fmaxf(mx, s[r]);
         const float c = a.scale_log2;
-        const float m_new = fmaxf(m_run, pair_max(mx) * c);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        // The running max m moves only when the row maximum rises more than
+        // kMaxSlack above it.  Until then weights reach at most 2^kMaxSlack,
+        // which fp32 sums and bf16 operands carry with unchanged relative
+        // rounding; out and lse use the same reference m, so the result is
+        // the same and the accumulators are rescaled far less often.
+        const float m_cand = pair_max(mx) * c;
+        const float m_new = m_cand > m_run + kMaxSlack ? m_cand : m_run;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // exactly 1 unless m moved
         m_run = m_new;
         float psum = 0.f;
         uint32_t pp[8];
@@ -352,11 +360,11 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
     // Both halves' scores are issued first: the matrix cores work on the
     // second half's S while the first half's softmax runs on the VALU, and on
     // the first half's P.V while the second softmax runs.
-    auto compute_step = [&](int kb, int stage) __attribute__((always_inline)) {
+    auto compute_step = [&](auto masked, int kb, int stage) __attribute__((always_inline)) {
         const f32x16_t s0 = scores(stage, 0);
         const f32x16_t s1 = scores(stage, 1);
-        softmax_pv(kb, stage, 0, s0);
-        softmax_pv(kb, stage, 1, s1);
+        softmax_pv(masked, kb, stage, 0, s0);
+        softmax_pv(masked, kb, stage, 1, s1);
     };
 
     // Pipeline: step kb + 2 is copied into LDS while step kb is computed.
@@ -366,8 +374,9 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
     if (nblk > 1)
         issue(1, 1);
     wait_vm<0>();   // q and the first copies: nothing older than a step's copies stays in flight in the loop
+    // The steps before full_blk mask nothing and run without the mask code.
     int stage = 0;
-    for (int kb = 0; kb < nblk; ++kb) {
+    auto run_step = [&](auto masked, int kb) __attribute__((always_inline)) {
         if (kb + 1 < nblk)
             wait_vm<4>();
         else
@@ -375,9 +384,15 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
         stage_barrier();
         if (kb + 2 < nblk)
             issue(kb + 2, stage == 0 ? 2 : stage - 1);
-        compute_step(kb, stage);
+        compute_step(masked, kb, stage);
         stage = stage == kStages - 1 ? 0 : stage + 1;
-    }
+    };
+    const int unmasked = min(full_blk, nblk);
+    int kb = 0;
+    for (; kb < unmasked; ++kb)
+        run_step(std::false_type{}, kb);
+    for (; kb < nblk; ++kb)
+        run_step(std::true_type{}, kb);
 
     // Rows: out[row][h][dim], dims 32 db + 8 (r/4) + 4 half + r%4.
     const float l_tot = pair_sum(l_run);
