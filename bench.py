@@ -7,7 +7,9 @@ Qwen3-0.6B-shaped decoder (audio.cpp "Fun-ASR-Nano Native Runtime Design",
 ``hipdecode_paged_attn``, layer i reading its own KV pools.  The pools are
 rotated over R distinct device copies so that every call streams from HBM
 rather than from the 256 MB last-level cache.  All inputs are resident in HBM
-before the timed region starts.
+before the timed region starts.  By default a step replays one captured HIP
+graph of its 28 launches, as a serving loop replays its decode step;
+``--eager`` issues the launches one by one instead.
 
 value   = decode tokens/s = B * steps / (timed seconds)
 roofline.achieved = algorithmic bytes per call / average call duration,
@@ -139,11 +141,17 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default=None,
                     help="decode: c1 c2 c3 c4 c5 c3b (default c4); append: a1 a2 (default a2); "
                          "prefill: p1 p2 (default p1); step: s1 s2 (default s2)")
+    ap.add_argument("--context", type=int, default=0,
+                    help="decode: one request of this many tokens (a shuffled pool of exactly its pages, "
+                         "N(0,1) bf16) instead of a named workload; for sweeps of the per-call fixed cost")
     ap.add_argument("--partition", type=int, default=0, help="split-K partition tokens (0 = planner)")
     ap.add_argument("--waves", type=int, default=0, help="wavefronts per workgroup, 4 or 16 (0 = planner)")
     ap.add_argument("--schedule", type=int, default=0, help="1 = split, 2 = stream (0 = planner)")
     ap.add_argument("--rotate", type=int, default=0, help="distinct KV pool copies (0 = auto)")
-    ap.add_argument("--graph", action="store_true", help="replay one captured step per step")
+    ap.add_argument("--graph", dest="graph", action="store_true", default=True,
+                    help="replay one captured HIP graph per step (the default: the decode step of the "
+                         "MOSS-TD article runs from captured graphs)")
+    ap.add_argument("--eager", dest="graph", action="store_false", help="issue the 28 launches of a step eagerly")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for the traffic counters)")
@@ -190,14 +198,20 @@ def main(argv=None) -> int:
         return run_prefill(args, dev)
     if args.op == "step":
         return run_step(args, dev)
-    args.workload = args.workload or "c4"
-    if args.workload not in ("c1", "c2", "c3", "c4", "c5", "c3b"):
-        print(f"unknown decode workload {args.workload}", file=sys.stderr)
-        return 2
-
-    t0 = time.time()
-    case = make_config(args.workload)
-    t_gen = time.time() - t0
+    if args.context > 0:
+        from workloads import make_case
+        t0 = time.time()
+        args.workload = f"b1_ctx{args.context}"
+        case = make_case([args.context], seed=3, name=args.workload)
+        t_gen = time.time() - t0
+    else:
+        args.workload = args.workload or "c4"
+        if args.workload not in ("c1", "c2", "c3", "c4", "c5", "c3b"):
+            print(f"unknown decode workload {args.workload}", file=sys.stderr)
+            return 2
+        t0 = time.time()
+        case = make_config(args.workload)
+        t_gen = time.time() - t0
     out_dtype = torch.float32 if case.out_dtype == "f32" else torch.bfloat16
     out_bytes = 4 if case.out_dtype == "f32" else 2
     alg_bytes = algorithmic_bytes(case, out_bytes)
