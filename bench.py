@@ -75,6 +75,22 @@ def kernel_source_hash(kernel: str = "paged_decode_kernel") -> str:
     return h.hexdigest()[:16]
 
 
+def per_step_spread(run, stream, steps: int) -> list[float]:
+    """p10, p50 and p90 of the per-call time, from `steps` more steps timed
+    one by one with HIP events on the launch stream (after the main timed
+    region, which they do not touch)."""
+    import numpy as np
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        run()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    per_call_us = np.array([e0.elapsed_time(e1) for e0, e1 in evs]) * 1e3 / LAYERS
+    return [round(float(np.percentile(per_call_us, q)), 3) for q in (10, 50, 90)]
+
+
 def algorithmic_bytes(case, out_bytes: int) -> int:
     """Bytes the method must move per call: every cached K and V row of the
     context once, q, out, lse, the block-table entries used and the lengths."""
@@ -281,6 +297,7 @@ def main(argv=None) -> int:
     call_s = ms * 1e-3 / n_calls
     value = case.B * args.steps / (ms * 1e-3)
     achieved = alg_bytes / call_s / 1e9
+    spread = per_step_spread(run, stream, args.steps)
 
     # parity of the last call against the oracle, and the oracle's own speed
     result = {
@@ -314,6 +331,7 @@ def main(argv=None) -> int:
             "out_dtype": case.out_dtype,
         },
         "us_per_layer": round(call_s * 1e6, 3),
+        "us_per_layer_p10_p50_p90": spread,
         "kv_tokens_per_s": round(case.total_tokens / call_s, 1),
         "wall_s_timed": round(wall, 4),
         "roofline": {
