@@ -54,7 +54,7 @@ constexpr int kStepBytes = kKeys * kRowBytes;
 constexpr int kStages = 3;                // LDS stages: the copy runs two steps ahead
 constexpr int kDimBlocks = kHeadDim / 32; // O^T is four 32x32 accumulators
 constexpr float kNegBig = -1.0e30f;       // running-max start: finite, so no inf - inf
-constexpr float kMaxSlack = 8.0f;         // log2 units a row maximum may exceed the running max
+constexpr float kPsumMax = 65536.0f;      // a half's weights summing past this move the running max
 constexpr int64_t kMaxGrid = (int64_t)1 << 31;
 
 struct PrefillArgs {
@@ -230,12 +230,15 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
     const size_t page_bytes = (size_t)kPageSize * kv_row_bytes;
     const uint8_t *k_bytes = reinterpret_cast<const uint8_t *>(a.k_pool) + (size_t)g * kRowBytes;
     const uint8_t *v_bytes = reinterpret_cast<const uint8_t *>(a.v_pool) + (size_t)g * kRowBytes;
-    uint32_t k_chunk[2], v_chunk[2];
+    uint32_t k_chunk[2], v_chunk[2], k_full[2], v_full[2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
         const int r = 8 * w + 4 * k + drow;
         k_chunk[k] = (uint32_t)(((lane & 15) ^ swz_k(r)) * 16);
         v_chunk[k] = (uint32_t)(((lane & 15) ^ swz_v(r)) * 16);
+        // a step with all eight keys in range: the key's slot is r mod 16
+        k_full[k] = (uint32_t)(r % kPageSize) * kv_row_bytes + k_chunk[k];
+        v_full[k] = (uint32_t)(r % kPageSize) * kv_row_bytes + v_chunk[k];
     }
     const int32_t *table = a.block_table + (size_t)b * a.max_blocks;
     auto issue = [&](int kb, int stage) __attribute__((always_inline)) {
@@ -244,13 +247,18 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
         int page = scalar_load(table + pidx);
         page = (unsigned)page < (unsigned)a.num_pages ? page : 0;
         const size_t pbase = (size_t)page * page_bytes;
+        const bool full = key_w + 8 <= kv_end;   // uniform
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
-            const int key = min(key_w + 4 * k + drow, kv_end - 1);
-            const uint32_t row_off = (uint32_t)(key % kPageSize) * kv_row_bytes;
+            uint32_t ko = k_full[k], vo = v_full[k];
+            if (!full) {
+                const uint32_t row_off = (uint32_t)(min(key_w + 4 * k + drow, kv_end - 1) % kPageSize) * kv_row_bytes;
+                ko = row_off + k_chunk[k];
+                vo = row_off + v_chunk[k];
+            }
             const int r0 = 8 * w + 4 * k;
-            copy_to_lds(k_bytes + pbase, row_off + k_chunk[k], (const lds_u8_t *)&k_lds[stage][r0 * kRowBytes]);
-            copy_to_lds(v_bytes + pbase, row_off + v_chunk[k], (const lds_u8_t *)&v_lds[stage][r0 * kRowBytes]);
+            copy_to_lds(k_bytes + pbase, ko, (const lds_u8_t *)&k_lds[stage][r0 * kRowBytes]);
+            copy_to_lds(v_bytes + pbase, vo, (const lds_u8_t *)&v_lds[stage][r0 * kRowBytes]);
         }
     };
 
@@ -308,35 +316,48 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
                 s[r] = key > pos ? -INFINITY : s[r];
             }
         }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            mx = fmaxf(mx, s[r]);
+        // The running max m is not brought up to date on every half.  The
+        // weights p = 2^(c s - m) are computed against the m in hand; only
+        // when some lane's half sums past kPsumMax -- a row maximum well
+        // above m, or m still at its start value on a row's first half --
+        // does the wavefront find the row maxima, move m, rescale l and the
+        // accumulators, and recompute the weights.  Every weight is then at
+        // most kPsumMax, which fp32 sums and bf16 operands carry with
+        // unchanged relative rounding; out and lse share the reference m.
         const float c = a.scale_log2;
-        // The running max m moves only when the row maximum rises more than
-        // kMaxSlack above it.  Until then weights reach at most 2^kMaxSlack,
-        // which fp32 sums and bf16 operands carry with unchanged relative
-        // rounding; out and lse use the same reference m, so the result is
-        // the same and the accumulators are rescaled far less often.
-        const float m_cand = pair_max(mx) * c;
-        const float m_new = m_cand > m_run + kMaxSlack ? m_cand : m_run;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // exactly 1 unless m moved
-        m_run = m_new;
+        float pw[16];
         float psum = 0.f;
-        uint32_t pp[8];
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[r], c, -m_new));   // masked: 2^-inf = 0
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1], c, -m_new));
-            psum += p0 + p1;
-            pp[r / 2] = pack2_bf16(p0, p1);
+            pw[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c, -m_run));   // masked: 2^-inf = 0
+            pw[r + 1] = __builtin_amdgcn_exp2f(fmaf(s[r + 1], c, -m_run));
+            psum += pw[r] + pw[r + 1];
         }
-        l_run = l_run * alpha + psum;
-        if (__any(alpha != 1.f)) {
+        if (__any(!(psum <= kPsumMax))) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                mx = fmaxf(mx, s[r]);
+            const float m_new = fmaxf(m_run, pair_max(mx) * c);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
 #pragma unroll
             for (int db = 0; db < kDimBlocks; ++db)
                 acc[db] *= alpha;
+            psum = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                pw[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c, -m_new));
+                pw[r + 1] = __builtin_amdgcn_exp2f(fmaf(s[r + 1], c, -m_new));
+                psum += pw[r] + pw[r + 1];
+            }
         }
+        l_run += psum;
+        uint32_t pp[8];
+#pragma unroll
+        for (int r = 0; r < 16; r += 2)
+            pp[r / 2] = pack2_bf16(pw[r], pw[r + 1]);
 
         // O^T += V^T P^T, two k-steps of 16 keys.  P^T: lane l holds keys
         // 16 kh + 4 half + e and 16 kh + 8 + 4 half + e (e < 4) of this half,
