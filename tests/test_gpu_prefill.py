@@ -1,13 +1,21 @@
 """GPU parity of chunked-prefill attention against the fp64 oracle, through the
 C ABI.
 
-Tolerances: max |out - oracle| <= 1e-2 (bf16 and fp32 outputs) and
-|lse - oracle| <= 1e-4 * max(1, |oracle|).  The matrix cores take the softmax
-weights in bf16, so unlike the decode kernel the outputs are not at bf16
-rounding level: each weight carries a relative error of up to 2^-9, which
-bounds the output error by about 2^-9 times the largest |V| a row attends to
-(here about 5, so under 1e-2); the tests also report the mean error.
-Rows that no request names must be left exactly as they were.
+Tolerances, derived from the arithmetic (the decode bar of 1e-2 assumes fp32
+softmax weights, which the matrix cores do not take).  Each weight enters the
+P.V product rounded to bf16: 8 significant bits, a relative error of at most
+u = 2^-8.  So |sum p~ v / l - sum p v / l| <= u max|V|, and a bf16 output
+adds its own rounding, at most u |out|.  Per element:
+
+    |out - oracle| <= u (1 + u) Vmax + u |oracle| (bf16 out only) + 1e-5
+
+with Vmax the largest |V| in the pool.  With N(0,1) values Vmax is about 5,
+so the bound is about 2e-2, plus the output's share.  Spread-out attention
+stays near 1e-2 (the weights' roundings partly cancel); where one key
+dominates, the error approaches u (Vmax + |out|).  The scores,
+running sums and lse stay in fp32: |lse - oracle| <= 1e-4 * max(1, |oracle|).
+The tests also report the mean error.  Rows that no request names must be
+left exactly as they were.
 """
 from __future__ import annotations
 
@@ -20,11 +28,12 @@ import torch
 import oracle
 import paged_kv_decode_gqa_amd as hd
 from tests.gpu_util import DeviceCase, bits_to_bf16, compare, log, run_hip
-from workloads import make_append_inputs, make_case, make_prefill_case, make_prefill_config
+from workloads import (bf16_bits_to_f32, f32_to_bf16_bits, make_append_inputs, make_case, make_prefill_case,
+                       make_prefill_config)
 
 pytestmark = pytest.mark.gpu
 
-OUT_ATOL = 1e-2
+BF16_EPS = 2.0 ** -8      # unit roundoff of bf16 (8 significant bits, nearest even)
 LSE_RTOL = 1e-4
 SENTINEL = 7.0
 
@@ -52,23 +61,32 @@ def named_rows(new_start, T):
     return named
 
 
-def check_rows(o, l, ref_o, ref_l, what):
+def v_max(v_pool):
+    return float(np.nanmax(np.abs(bf16_bits_to_f32(v_pool))))
+
+
+def out_bound(ref_o, vmax, bf16_out=True):
+    return BF16_EPS * (1 + BF16_EPS) * vmax + (BF16_EPS * np.abs(ref_o) if bf16_out else 0.0) + 1e-5
+
+
+def check_rows(o, l, ref_o, ref_l, what, vmax, bf16_out=True):
     err = np.abs(o - ref_o)
     assert np.all(np.isfinite(o)), f"{what}: non-finite output"
     max_err = float(err.max()) if err.size else 0.0
-    assert max_err <= OUT_ATOL, f"{what}: max |out err| {max_err}"
+    over = err - out_bound(ref_o, vmax, bf16_out)
+    assert not np.any(over > 0), f"{what}: max |out err| {max_err}, worst excess {float(over.max())}"
     lerr = np.abs(l - ref_l) / np.maximum(1.0, np.abs(ref_l))
     assert np.all(lerr <= LSE_RTOL), f"{what}: lse err {float(lerr.max())}"
     log(f"[prefill] {what}: max|dout|={max_err:.2e} mean|dout|={float(err.mean()):.2e} "
-        f"max rel dlse={float(lerr.max()):.2e}")
+        f"max rel dlse={float(lerr.max()):.2e} (Vmax {vmax:.2f})")
     return max_err
 
 
-def check_full(case, inp, o, l, what):
+def check_full(case, inp, o, l, what, bf16_out=True):
     ref_o, ref_l = oracle.prefill_attn(inp.q, case.k_pool, case.v_pool, case.block_table, case.context_lens,
                                        inp.new_start, case.scale)
     named = named_rows(inp.new_start, inp.rows)
-    check_rows(o[named], l[named], ref_o[named], ref_l[named], what)
+    check_rows(o[named], l[named], ref_o[named], ref_l[named], what, v_max(case.v_pool), bf16_out)
     assert np.all(o[~named] == SENTINEL) and np.all(l[~named] == SENTINEL), f"{what}: an unnamed row was written"
 
 
@@ -101,10 +119,25 @@ def test_prefill_group_shapes(hq, hkv):
     check_full(case, inp, o, l, f"{hq}/{hkv}")
 
 
+def test_prefill_rising_scores():
+    # Keys grow with their position, so a row's maximum keeps rising past the
+    # running reference: the rescale path runs on many halves, not only the first.
+    ctx, new = [3000, 700], [512, 700]
+    case, inp = make_prefill_case(ctx, new, seed=45)
+    k = bf16_bits_to_f32(case.k_pool).astype(np.float32)
+    for b, n in enumerate(ctx):
+        for t in range(n):
+            page, slot = case.block_table[b, t // 16], t % 16
+            k[page, slot] *= np.float32(1.0 + 7.0 * (t / n) ** 2)
+    case = replace(case, k_pool=f32_to_bf16_bits(k))
+    o, l = run_gpu(case, inp)
+    check_full(case, inp, o, l, "rising scores")
+
+
 def test_prefill_fp32_out():
     case, inp = make_prefill_case([450, 97], [160, 97], seed=43)
     o, l = run_gpu(case, inp, out_dtype=torch.float32)
-    check_full(case, inp, o, l, "fp32 out")
+    check_full(case, inp, o, l, "fp32 out", bf16_out=False)
 
 
 def sampled_pairs(inp, Hq, rng, extra=48):
@@ -124,7 +157,8 @@ def test_prefill_named_workloads_sampled(name):
     ref_o, ref_l = oracle.prefill_attn_pairs(inp.q, case.k_pool, case.v_pool, case.block_table,
                                              case.context_lens, inp.new_start, case.scale, pairs)
     idx = np.array(pairs)
-    check_rows(o[idx[:, 0], idx[:, 1]], l[idx[:, 0], idx[:, 1]], ref_o, ref_l, f"{name} sampled")
+    check_rows(o[idx[:, 0], idx[:, 1]], l[idx[:, 0], idx[:, 1]], ref_o, ref_l, f"{name} sampled",
+               v_max(case.v_pool))
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(l)), f"{name}: non-finite rows"
 
 
@@ -139,7 +173,8 @@ def test_prefill_last_rows_match_decode_kernel():
     d_out, d_lse = run_hip(dc)
     d_o = d_out.float().cpu().numpy()
     d_l = d_lse.cpu().numpy()
-    assert np.abs(o[last] - d_o).max() <= 2 * OUT_ATOL
+    # prefill's bound plus the decode kernel's rounding-level one (fp32 weights, bf16 out)
+    assert np.all(np.abs(o[last] - d_o) <= out_bound(d_o, v_max(case.v_pool)) + 2.0 ** -8 * np.abs(d_o) + 2e-5)
     assert np.all(np.abs(l[last] - d_l) <= 2 * LSE_RTOL * np.maximum(1.0, np.abs(d_l)))
 
 
@@ -152,7 +187,7 @@ def test_prefill_skips_what_breaks_the_contract():
     ok_rows = np.r_[0:20, 30:70]
     ref_o, ref_l = oracle.prefill_attn(inp.q, case.k_pool, case.v_pool, case.block_table, case.context_lens,
                                        inp.new_start, case.scale)
-    check_rows(o[ok_rows], l[ok_rows], ref_o[ok_rows], ref_l[ok_rows], "valid requests")
+    check_rows(o[ok_rows], l[ok_rows], ref_o[ok_rows], ref_l[ok_rows], "valid requests", v_max(case.v_pool))
     assert np.all(o[20:30] == SENTINEL) and np.all(l[20:30] == SENTINEL), "a broken request wrote rows"
 
 
@@ -183,4 +218,4 @@ def test_chunked_prefill_pipeline_with_append():
         k_ref, v_ref, q_rot = oracle.kv_append(rows.k_new, rows.v_new, case.block_table, ctx, k_ref, v_ref,
                                                new_start=rows.new_start, q=rows.q, rope=True, theta=rows.theta)
         ref_o, ref_l = oracle.prefill_attn(q_rot, k_ref, v_ref, case.block_table, ctx, rows.new_start, case.scale)
-        check_rows(out.float().cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, f"pipeline chunk {i}")
+        check_rows(out.float().cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, f"pipeline chunk {i}", v_max(v_ref))
