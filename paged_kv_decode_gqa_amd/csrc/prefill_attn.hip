@@ -15,8 +15,9 @@
 // 32x32 MFMA tile, so a workgroup holds 256 rows: every K/V byte brought into
 // LDS serves 256 rows, which keeps the re-reads of the context (one pass per
 // tile) within what the caches deliver.  Keys go by in steps of 64 (four
-// pages), staged in LDS and double-buffered -- K row-major, V transposed --
-// and used in two halves of 32.
+// pages), copied straight from the pools into a three-stage LDS ring
+// (global_load_lds, two steps ahead), both K and V row-major, and used in two
+// halves of 32.
 //
 // Per step and wavefront, with v_mfma_f32_32x32x16_bf16 (A 32x16, B 16x32):
 //   S^T[key][row]  = sum_d K[key][d] Q[row][d]        8 MFMAs, A = K, B = Q^T
@@ -24,12 +25,13 @@
 // Lane l of the S^T accumulator holds row l % 32 and keys
 // 8(r/4) + 4(l/32) + r%4 for registers r = 0..15, which is exactly how the
 // B operand of the second product wants P^T, provided both products agree
-// on the order of the key index: V^T is stored in LDS with bits 2 and 3 of
-// the key index swapped, so that each lane's eight keys are one contiguous
-// 16-byte read.  The softmax is online, in base 2 with scale*log2(e) folded
-// in (one FMA and one v_exp_f32 per score); the two lanes (l, l ^ 32) that
-// share a row combine their maxima with v_permlane32_swap.  P is rounded to bf16 for the matrix cores; the running
-// sum uses the fp32 values.
+// on the order of the key index: the V^T operand is read with transposing
+// LDS reads (ds_read_b64_tr_b16) that take those same keys.  The softmax is
+// online, in base 2 with scale*log2(e) folded in (one FMA and one v_exp_f32
+// per score), against a running maximum that moves only when the weights
+// grow large; the two lanes (l, l ^ 32) that share a row combine their
+// maxima and sums with v_permlane32_swap.  P is rounded to bf16 for the
+// matrix cores; the running sum uses the fp32 values.
 #include "hipdecode.h"
 #include "internal.h"
 
