@@ -365,27 +365,48 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
         // 16 kh + 4 half + e and 16 kh + 8 + 4 half + e (e < 4) of this half,
         // in the S^T accumulator's own order; the V^T reads take the same keys.
         const lds_u8_t *vl = (const lds_u8_t *)&v_lds[stage][32 * hh * kRowBytes];
+        i16x8_t vv[2][kDimBlocks];
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-            const uint4 u = make_uint4(pp[4 * kh], pp[4 * kh + 1], pp[4 * kh + 2], pp[4 * kh + 3]);
-            const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, u);
+        for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
             for (int db = 0; db < kDimBlocks; ++db) {
                 const lds_u8_t *p = vl + 16 * kh * kRowBytes + v_off[db];
                 const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p);
                 const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(p + 8 * kRowBytes));
-                const i16x8_t v8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, v8), pop,
-                                                                  acc[db], 0, 0, 0);
+                vv[kh][db] = i16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+            const uint4 u = make_uint4(pp[4 * kh], pp[4 * kh + 1], pp[4 * kh + 2], pp[4 * kh + 3]);
+            const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, u);
+#pragma unroll
+            for (int db = 0; db < kDimBlocks; ++db)
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vv[kh][db]), pop,
+                                                                  acc[db], 0, 0, 0);
         }
     };
     // Both halves' scores are issued first: the matrix cores work on the
     // second half's S while the first half's softmax runs on the VALU, and on
     // the first half's P.V while the second softmax runs.
     auto compute_step = [&](auto masked, int kb, int stage) __attribute__((always_inline)) {
-        const f32x16_t s0 = scores(stage, 0);
-        const f32x16_t s1 = scores(stage, 1);
+        // all sixteen K operands of the step are read before the first MFMA
+        bf16x8_t k0[kHeadDim / 16], k1[kHeadDim / 16];
+        const uint8_t *kl0 = &k_lds[stage][0];
+        const uint8_t *kl1 = &k_lds[stage][32 * kRowBytes];
+#pragma unroll
+        for (int ks = 0; ks < kHeadDim / 16; ++ks) {
+            k0[ks] = *reinterpret_cast<const bf16x8_t *>(kl0 + k_off[ks]);
+            k1[ks] = *reinterpret_cast<const bf16x8_t *>(kl1 + k_off[ks]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16_t s0 = zero16(), s1 = zero16();
+#pragma unroll
+        for (int ks = 0; ks < kHeadDim / 16; ++ks)
+            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0[ks], qop[ks], s0, 0, 0, 0);
+#pragma unroll
+        for (int ks = 0; ks < kHeadDim / 16; ++ks)
+            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1[ks], qop[ks], s1, 0, 0, 0);
         softmax_pv(masked, kb, stage, 0, s0);
         softmax_pv(masked, kb, stage, 1, s1);
     };
