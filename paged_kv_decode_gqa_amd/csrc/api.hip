@@ -84,7 +84,9 @@ WorkspaceLayout layout_of(const hipdecode_params &p)
 {
     WorkspaceLayout w;
     w.counters = 0;
-    w.part_ml = align256((size_t)p.num_seqs * (size_t)p.num_kv_heads * sizeof(int32_t));
+    // one 256-byte line per counter: the tickets of different KV heads never
+    // meet on one line (measured 4% at the 32-request mix, 14% at 1 x 3.5k)
+    w.part_ml = align256((size_t)p.num_seqs * (size_t)p.num_kv_heads * kCounterStride * sizeof(int32_t));
     size_t partials;
     if (plan_schedule(p) == kScheduleStream) {
         // two per tile; tiles <= W + B * Hkv (a tile is a full block, or a request's last)

@@ -16,13 +16,14 @@ constexpr int kMinPartition = 64;     // split-K partitions are multiples of thi
 constexpr int kMaxPartition = 4096;   // at most 256 pages, so at most 64 per wavefront: one table entry per lane
 constexpr int kMaxMergeSplits = 1024; // partitions per request the final merge can weigh in LDS
 constexpr int kMaxStreamSeqs = 1024;  // stream schedule: requests whose page counts fit the LDS prefix sum
+constexpr int kCounterStride = 64;   // int32 per arrival counter: each on its own 256-byte line
 constexpr int kScheduleSplit = 1;
 constexpr int kScheduleStream = 2;
 
 // Byte offsets inside the caller's workspace.  Partials are indexed
 // [B][Hq][nsplit] by the split schedule and [2W][G] by the stream schedule.
 struct WorkspaceLayout {
-    size_t counters;   // int32 [B][Hkv]: arrivals per (request, KV head); zero between calls
+    size_t counters;   // int32 [B][Hkv][kCounterStride]: arrivals per (request, KV head) in element 0; zero between calls
     size_t part_ml;    // fp32  [partials][2]: (running max, running sum) in log2 units
     size_t part_acc;   // fp32  [partials][128]: unnormalised weighted sums of V
     size_t total;

@@ -37,7 +37,7 @@ namespace {
 
 using namespace dev;
 
-constexpr int kRegPartials = 4;   // final merge: partial sums per thread loaded up front
+constexpr int kRegPartials = 8;   // final merge: partial sums per thread loaded up front
 
 __device__ __forceinline__ float wave_max(float v)
 {
@@ -557,7 +557,7 @@ void paged_decode_kernel(DecodeArgs a)
     emit<G, WAVES, OUT_F32>(a, sm, row0, single, [&](int h) { return (row0 + h) * nsm + split; }, ln);
     if (single)
         return;
-    int32_t *ticket = a.counters + (size_t)b * Hkv + g;
+    int32_t *ticket = a.counters + ((size_t)b * Hkv + g) * kCounterStride;
     if (!arrive<G, WAVES>(ticket, nsplit_b, sm, ln))
         return;
     merge_partials<G, WAVES, OUT_F32>(a, sm, row0, nsplit_b,
@@ -701,7 +701,7 @@ __global__ __launch_bounds__(256) void paged_decode_stream_kernel(DecodeArgs a)
             emit<G, WAVES, OUT_F32>(a, sm, row0, false, [&](int h) { return slot * G + h; }, ln);
             if (whole)
                 emit_empty<G, WAVES>(a, (slot + 1) * G, ln);
-            int32_t *ticket = a.counters + (size_t)b * Hkv + g;
+            int32_t *ticket = a.counters + ((size_t)b * Hkv + g) * kCounterStride;
             if (arrive<G, WAVES>(ticket, 2 * J, sm, ln, whole ? 2 : 1)) {
                 merge_partials<G, WAVES, OUT_F32>(
                     a, sm, row0, 2 * J,

@@ -185,12 +185,13 @@ def test_planner_and_workspace_sizes():
     assert 256 <= part <= 4096 and part % 64 == 0
     assert 16 * 8 * nsplit >= 1024
     rows = 16 * 16
-    expect = 512 + ((rows * nsplit * 8 + 255) // 256) * 256 + rows * nsplit * 128 * 4
+    counters = 16 * 8 * 256   # one 256-byte line per (request, KV head)
+    expect = counters + ((rows * nsplit * 8 + 255) // 256) * 256 + rows * nsplit * 128 * 4
     assert hd.hipdecode_workspace_bytes(p) == expect
     # stream: counters plus two partial slots per tile, tiles <= W + B * Hkv (768 workgroups, G = 2)
     ps = base(schedule=2)
     slots = 2 * (768 + 16 * 8) * 2
-    assert hd.hipdecode_workspace_bytes(ps) == 512 + ((slots * 8 + 255) // 256) * 256 + slots * 128 * 4
+    assert hd.hipdecode_workspace_bytes(ps) == counters + ((slots * 8 + 255) // 256) * 256 + slots * 128 * 4
     # B=1 at 28672: 8 KV heads x 32 partitions = one workgroup per CU
     p1 = base(num_seqs=1, num_pages=2048)
     part1 = hd.hipdecode_partition_tokens(p1)
@@ -198,7 +199,7 @@ def test_planner_and_workspace_sizes():
     # one partition per request: only the counters
     p2 = base(num_seqs=16, max_context_len=200, num_pages=64, max_blocks_per_seq=13)
     assert hd.hipdecode_partition_tokens(p2) == 256
-    assert hd.hipdecode_workspace_bytes(p2) == 512
+    assert hd.hipdecode_workspace_bytes(p2) == counters
     # one short request is split for latency: 512 tokens in 64-token partitions
     p3 = base(num_seqs=1, max_context_len=512, num_pages=64, max_blocks_per_seq=32)
     assert hd.hipdecode_partition_tokens(p3) == 64

@@ -165,7 +165,7 @@ def test_workspace_reuse_leaves_counters_zero():
         log(f"[parity] workspace reuse, call {it}")
         out, lse = run_hip(dc, workspace=ws)
         compare(out, lse, ref_out, ref_lse, what=f"reuse {it}")
-        assert int(ws[: case.B * 8].abs().sum().item()) == 0, "tickets must return to zero"
+        assert int(ws[: case.B * 8 * 64].abs().sum().item()) == 0, "tickets must return to zero"
         if first is None:
             first = (out.clone(), lse.clone())
         else:
@@ -245,7 +245,7 @@ def test_alternating_inputs_share_one_workspace():
             assert torch.equal(out, first[name][0]) and torch.equal(lse, first[name][1])
         else:
             first[name] = (out.clone(), lse.clone())
-    assert int(ws[:3 * 8].abs().sum().item()) == 0
+    assert int(ws[:3 * 8 * 64].abs().sum().item()) == 0
 
 
 def test_maximum_split_count():
