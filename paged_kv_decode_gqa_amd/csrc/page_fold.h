@@ -214,6 +214,13 @@ __device__ __forceinline__ float coherent_load(const float *p)
     return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Two consecutive floats, 8-byte aligned, as one 64-bit coherent load.
+__device__ __forceinline__ uint64_t coherent_load8(const float *p)
+{
+    return __hip_atomic_load(reinterpret_cast<uint64_t *>(const_cast<float *>(p)), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Four consecutive floats, 8-byte aligned, as two 64-bit coherent loads.
 __device__ __forceinline__ f32x4 coherent_load4(const float *p)
 {

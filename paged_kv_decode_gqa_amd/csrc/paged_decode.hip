@@ -320,25 +320,34 @@ __device__ __forceinline__ void merge_partials(const DecodeArgs &a, Smem<G, WAVE
 {
     using S = Smem<G, WAVES>;
     // Every thread owns 4 dims of one head and a 1/kSets share of the
-    // partials.  Its first kRegPartials partial sums and the (m, l) of every
-    // partial are loaded in one batch, so the merge waits on memory once.
+    // partials.  Its first kRegPartials partial sums and the (m, l) pair of
+    // partial tid are loaded in one batch, without branches (indices past the
+    // end are clamped and their values dropped), so the merge waits on
+    // memory once; (m, l) pairs past the first kThreadsWG follow in a loop.
     const int chunk = ln.tid % S::kChunks;
     const int set = ln.tid / S::kChunks;
     const int h = chunk / (kHeadDim / 4);
     const int c = chunk % (kHeadDim / 4);
+    const int n_ml = G * count;
+    const int idx0 = min(ln.tid, n_ml - 1);
+    const int hh0 = idx0 / count;
+    const uint64_t ml0 = coherent_load8(a.part_ml + part_index(idx0 - hh0 * count, hh0) * 2);
     f32x4 pre[kRegPartials];
 #pragma unroll
     for (int r = 0; r < kRegPartials; ++r) {
-        const int i = set + r * S::kSets;
-        pre[r] = i < count ? coherent_load4(a.part_acc + part_index(i, h) * kHeadDim + 4 * c)
-                           : f32x4{0.f, 0.f, 0.f, 0.f};
+        const int i = min(set + r * S::kSets, count - 1);
+        pre[r] = coherent_load4(a.part_acc + part_index(i, h) * kHeadDim + 4 * c);
     }
-    for (int idx = ln.tid; idx < G * count; idx += S::kThreadsWG) {
+    if (ln.tid < n_ml) {
+        sm.w[hh0][idx0 - hh0 * count] = __uint_as_float((uint32_t)ml0);
+        sm.lw[hh0][idx0 - hh0 * count] = __uint_as_float((uint32_t)(ml0 >> 32));
+    }
+    for (int idx = ln.tid + S::kThreadsWG; idx < n_ml; idx += S::kThreadsWG) {
         const int hh = idx / count;
         const int i = idx - hh * count;
-        const float *ml = a.part_ml + part_index(i, hh) * 2;
-        sm.w[hh][i] = coherent_load(ml);
-        sm.lw[hh][i] = coherent_load(ml + 1);
+        const uint64_t ml = coherent_load8(a.part_ml + part_index(i, hh) * 2);
+        sm.w[hh][i] = __uint_as_float((uint32_t)ml);
+        sm.lw[hh][i] = __uint_as_float((uint32_t)(ml >> 32));
     }
     __syncthreads();
     // wavefront hw turns head hw's maxima into weights and sums L
