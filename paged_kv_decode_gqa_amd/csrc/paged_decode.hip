@@ -39,20 +39,77 @@ using namespace dev;
 
 constexpr int kRegPartials = 8;   // final merge: partial sums per thread loaded up front
 
+// Reductions over a wavefront: four DPP steps inside each row of 16 lanes
+// (as row_sum16 does), then the four rows' results through v_readlane, so no
+// step waits on an LDS-based lane shuffle.
+__device__ __forceinline__ float row_max16(float x)
+{
+    x = fmaxf(x, dpp_f32<0xB1>(x));    // quad_perm [1,0,3,2]
+    x = fmaxf(x, dpp_f32<0x4E>(x));    // quad_perm [2,3,0,1]
+    x = fmaxf(x, dpp_f32<0x141>(x));   // row_half_mirror
+    x = fmaxf(x, dpp_f32<0x140>(x));   // row_mirror
+    return x;
+}
+
+__device__ __forceinline__ float lane_value(float x, int l)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
 __device__ __forceinline__ float wave_max(float v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-        v = fmaxf(v, __shfl_xor(v, o));
-    return v;
+    v = row_max16(v);
+    return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)), fmaxf(lane_value(v, 32), lane_value(v, 48)));
 }
 
 __device__ __forceinline__ float wave_sum(float v)
 {
+    v = row_sum16(v);
+    return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+}
+
+// The values of x in the two lanes of each pair (l, l ^ O), O = 16 or 32,
+// handed to both of them in the same order: `lo` from the member with the
+// bit clear, `hi` from the other (v_permlane16_swap / v_permlane32_swap).
+template <int O>
+__device__ __forceinline__ void pair_values(float x, float &lo, float &hi)
+{
+    const uint32_t u = __float_as_uint(x);
+    if constexpr (O == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        lo = __uint_as_float(r[0]);
+        hi = __uint_as_float(r[1]);
+    } else {
+        static_assert(O == 32, "pairs 16 or 32 lanes apart");
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        lo = __uint_as_float(r[0]);
+        hi = __uint_as_float(r[1]);
+    }
+}
+
+// Merge the two streams of each lane pair (l, l ^ O); both lanes end with the
+// same merged stream.
+template <int G, int O>
+__device__ __forceinline__ void merge_pairs(Stream<G> &st)
+{
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-        v += __shfl_xor(v, o);
-    return v;
+    for (int h = 0; h < G; ++h) {
+        float m_lo, m_hi, l_lo, l_hi;
+        pair_values<O>(st.m[h], m_lo, m_hi);
+        pair_values<O>(st.l[h], l_lo, l_hi);
+        const float M = fmaxf(m_lo, m_hi);
+        const float M_use = (M == -INFINITY) ? 0.f : M;
+        const float w_lo = merge_weight(m_lo, M_use);
+        const float w_hi = merge_weight(m_hi, M_use);
+        st.l[h] = fmaf(l_lo, w_lo, l_hi * w_hi);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float a_lo, a_hi;
+            pair_values<O>(st.acc[h][e], a_lo, a_hi);
+            st.acc[h][e] = fmaf(a_lo, w_lo, a_hi * w_hi);
+        }
+        st.m[h] = M;
+    }
 }
 
 // Merge the four row-group streams of a wavefront (lanes l, l^16, l^32, l^48
@@ -60,23 +117,8 @@ __device__ __forceinline__ float wave_sum(float v)
 template <int G>
 __device__ __forceinline__ void merge_row_groups(Stream<G> &st)
 {
-#pragma unroll
-    for (int o = 16; o <= 32; o <<= 1) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float m_o = __shfl_xor(st.m[h], o);
-            const float l_o = __shfl_xor(st.l[h], o);
-            const float M = fmaxf(st.m[h], m_o);
-            const float M_use = (M == -INFINITY) ? 0.f : M;
-            const float w_s = merge_weight(st.m[h], M_use);
-            const float w_o = merge_weight(m_o, M_use);
-            st.l[h] = fmaf(st.l[h], w_s, l_o * w_o);
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                st.acc[h][e] = fmaf(st.acc[h][e], w_s, __shfl_xor(st.acc[h][e], o) * w_o);
-            st.m[h] = M;
-        }
-    }
+    merge_pairs<G, 16>(st);
+    merge_pairs<G, 32>(st);
 }
 
 // LDS shared by both kernels.
