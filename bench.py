@@ -9,7 +9,10 @@ rotated over R distinct device copies so that every call streams from HBM
 rather than from the 256 MB last-level cache.  All inputs are resident in HBM
 before the timed region starts.  By default a step replays one captured HIP
 graph of its 28 launches, as a serving loop replays its decode step;
-``--eager`` issues the launches one by one instead.
+``--eager`` issues the launches one by one instead.  Each pool copy is its
+own allocation; ``--v-offset BYTES`` puts a copy's V pool BYTES after the end
+of its K pool in one allocation instead (rows whose address has bit 8 set
+stream more slowly on this GPU, so an odd multiple of 256 evens out the heads).
 
 value   = decode tokens/s = B * steps / (timed seconds)
 roofline.achieved = algorithmic bytes per call / average call duration,
@@ -73,6 +76,32 @@ def kernel_source_hash(kernel: str = "paged_decode_kernel") -> str:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def host_cpu_model() -> str:
+    """The host CPU's model name, read from /proc/cpuinfo (empty if unavailable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
+def shifted_pools(k, v, offset: int):
+    """Copies of the K and V pools in one allocation, V starting `offset` bytes after K ends."""
+    import torch
+    if offset < 0 or offset % 16:
+        raise ValueError("--v-offset must be a non-negative multiple of 16")
+    n = k.numel() * k.element_size()
+    raw = torch.empty(2 * n + offset, dtype=torch.uint8, device=k.device)
+    kk = raw[:n].view(k.dtype).view(k.shape)
+    vv = raw[n + offset: 2 * n + offset].view(v.dtype).view(v.shape)
+    kk.copy_(k)
+    vv.copy_(v)
+    return kk, vv
 
 
 def per_step_spread(run, stream, steps: int) -> list[float]:
@@ -164,6 +193,9 @@ def main(argv=None) -> int:
     ap.add_argument("--waves", type=int, default=0, help="wavefronts per workgroup, 4 or 16 (0 = planner)")
     ap.add_argument("--schedule", type=int, default=0, help="1 = split, 2 = stream (0 = planner)")
     ap.add_argument("--rotate", type=int, default=0, help="distinct KV pool copies (0 = auto)")
+    ap.add_argument("--v-offset", type=int, default=None, metavar="BYTES",
+                    help="decode: place each V pool BYTES after the end of its K pool in one allocation "
+                         "(default: separate allocations)")
     ap.add_argument("--graph", dest="graph", action="store_true", default=True,
                     help="replay one captured HIP graph per step (the default: the decode step of the "
                          "MOSS-TD article runs from captured graphs)")
@@ -240,7 +272,11 @@ def main(argv=None) -> int:
     R = args.rotate or max(2, min(LAYERS, math.ceil(ROTATE_MIN_BYTES / max(1, kv_bytes_call))))
     q = bf(case.q)
     k0, v0 = bf(case.k_pool), bf(case.v_pool)
-    pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(R - 1)]
+    if args.v_offset is None:
+        pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(R - 1)]
+    else:
+        pools = [shifted_pools(k0, v0, args.v_offset) for _ in range(R)]
+        del k0, v0
     table = torch.from_numpy(case.block_table).to(dev)
     ctx = torch.from_numpy(case.context_lens).to(dev)
     params = hd.make_params(num_seqs=case.B, num_q_heads=case.Hq, num_kv_heads=case.Hkv,
@@ -327,6 +363,7 @@ def main(argv=None) -> int:
             "workgroup_waves": waves,
             "schedule": schedule,
             "kv_pool_copies": R,
+            "v_pool_offset": args.v_offset,
             "mode": "hipgraph" if graph is not None else "eager",
             "out_dtype": case.out_dtype,
         },
@@ -367,6 +404,7 @@ def main(argv=None) -> int:
             "unit": "tokens/s",
             "cores": oracle.max_threads(),
             "kind": "oracle",
+            "cpu_model": host_cpu_model(),
             "sample": f"fp64 oracle over all {case.B * case.Hq} (request, head) pairs of one layer call, "
                       f"{reps} run(s), {t_layer:.3f} s per layer, scaled to {LAYERS} layers per token",
             "parity_max_abs_err": float(np.abs(o_gpu - ref_out).max()),
@@ -508,6 +546,7 @@ def run_append(args, dev) -> int:
             "unit": "tokens/s",
             "cores": 1,
             "kind": "oracle",
+            "cpu_model": host_cpu_model(),
             "sample": f"fp64 oracle append of the same {T} new tokens (copies of the pools included), "
                       f"{reps} run(s), {t_call * 1e3:.2f} ms per call",
         }
@@ -778,6 +817,7 @@ def run_prefill(args, dev) -> int:
             "unit": "tokens/s",
             "cores": oracle.max_threads(),
             "kind": "oracle",
+            "cpu_model": host_cpu_model(),
             "sample": f"fp64 oracle over 16 random chunk rows x all {case.Hq} heads, {reps} run(s), "
                       f"{t_rows:.3f} s per 16 rows",
         }
