@@ -10,11 +10,15 @@
 // matrix cores.
 //
 // Work decomposition.  One workgroup of eight wavefronts per (request, KV
-// head, tile of query tokens).  A wavefront owns 32 query rows -- 32/G chunk
-// tokens times the G query heads that share the KV head -- which is one
-// 32x32 MFMA tile, so a workgroup holds 256 rows: every K/V byte brought into
-// LDS serves 256 rows, which keeps the re-reads of the context (one pass per
-// tile) within what the caches deliver.  Keys go by in steps of 64 (four
+// head, pair of half-tiles of query tokens).  A wavefront owns 32 query rows
+// -- 32/G chunk tokens times the G query heads that share the KV head --
+// which is one 32x32 MFMA tile, so a workgroup holds 256 rows: every K/V byte
+// brought into LDS serves up to 256 rows, which keeps the re-reads of the
+// context (one pass per workgroup) within what the caches deliver.  Causal
+// attention gives late chunk tokens more keys than early ones, so wavefronts
+// 0-3 take an early half-tile and wavefronts 4-7 the matching late one; past
+// the early rows' last key those wavefronts only copy and wait, and the late
+// ones run at one wavefront per SIMD.  Keys go by in steps of 64 (four
 // pages), copied straight from the pools into a three-stage LDS ring
 // (global_load_lds, two steps ahead), both K and V row-major, and used in two
 // halves of 32.
@@ -74,7 +78,7 @@ struct PrefillArgs {
     int32_t max_blocks;
     int32_t num_rows;
     int32_t max_new;
-    int32_t tiles;          // query tiles per request
+    int32_t tiles;          // workgroups (pairs of half-tiles) per request and KV head
     float scale_log2;       // max(|scale| * log2(e), 2^-100): positive, see the launch
     uint32_t q_sign;        // 0x80008000 when scale < 0: q is negated on load instead
 };
@@ -166,24 +170,32 @@ template <int G, bool OUT_F32>
 __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
 {
     constexpr int kTokPerWave = kRowsPerWave / G;
-    constexpr int kTileTokens = kPfWaves * kTokPerWave;
+    constexpr int kHalfWaves = kPfWaves / 2;
+    constexpr int kHalfTokens = kHalfWaves * kTokPerWave;   // chunk tokens of one half-tile
     __shared__ __align__(16) uint8_t k_lds[kStages][kStepBytes];
     __shared__ __align__(16) uint8_t v_lds[kStages][kStepBytes];
 
-    // KV head fastest, heavier (later) tiles first.
+    // KV head fastest.  Workgroup `pair` of a request takes two half-tiles of
+    // its chunk: half-tile `pair` (wavefronts 0-3) and half-tile
+    // halves - 1 - pair (wavefronts 4-7), an early and a late stretch of the
+    // chunk, so that every workgroup has about the same number of keys to
+    // attend over.  With an odd number of half-tiles the middle one comes
+    // alone and wavefronts 4-7 of its workgroup hold no rows.
     const int bid = blockIdx.x;
     const int g = bid % a.num_kv_heads;
     const int rest = bid / a.num_kv_heads;
-    const int tile = a.tiles - 1 - rest % a.tiles;
+    const int pair = rest % a.tiles;
     const int b = rest / a.tiles;
     const int ctx = a.context_lens[b];
     const int start = a.new_start[b];
     const int n = a.new_start[b + 1] - start;
-    const int t0 = tile * kTileTokens;
     // Uniform across the workgroup: a request that breaks the contract, or a
-    // tile past its chunk, does nothing.
-    if (n <= 0 || n > ctx || n > a.max_new || start < 0 || (int64_t)start + n > a.num_rows || t0 >= n ||
+    // pair past its chunk, does nothing.
+    if (n <= 0 || n > ctx || n > a.max_new || start < 0 || (int64_t)start + n > a.num_rows ||
         (int64_t)ctx > (int64_t)a.max_blocks * kPageSize)
+        return;
+    const int halves = (n + kHalfTokens - 1) / kHalfTokens;
+    if (pair >= (halves + 1) / 2)
         return;
 
     const int tid = threadIdx.x;
@@ -191,9 +203,13 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j = lane & 31;          // this lane's row in the wavefront's tile
     const int half = lane >> 5;       // which 8 of each 16 along the contracted index
-    const int tq = t0 + w * kTokPerWave + j / G;
+    const bool upper = w >= kHalfWaves;
+    const int half_tile = upper ? halves - 1 - pair : pair;
+    const bool wave_live = !(upper && half_tile == pair);   // uniform
+    const int tw0 = half_tile * kHalfTokens + (w % kHalfWaves) * kTokPerWave;   // this wavefront's first token
+    const int tq = tw0 + j / G;
     const int h = g * G + j % G;
-    const bool row_ok = tq < n;
+    const bool row_ok = wave_live && tq < n;
     const int pos = row_ok ? ctx - n + tq : -1;      // -1: every key masked
     const size_t row = (size_t)start + min(tq, n - 1);
 
@@ -215,10 +231,17 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
         }
     }
 
-    const int tile_last = min(t0 + kTileTokens, n) - 1;
-    const int kv_end = ctx - n + tile_last + 1;          // keys [0, kv_end)
+    const int last_tok = min((halves - pair) * kHalfTokens, n) - 1;   // the workgroup's last chunk token
+    const int kv_end = ctx - n + last_tok + 1;           // keys [0, kv_end)
     const int nblk = (kv_end + kKeys - 1) / kKeys;
-    const int full_blk = (ctx - n + t0 + 1) / kKeys;      // steps with no masked key in any row
+    // Step bounds, uniform across the workgroup.  Steps before e1 mask no key
+    // of any row (wavefront 0 holds the first token); the early half-tile
+    // attends to keys of steps before e2; the late half-tile, if any, masks
+    // no key before e3 and attends up to the last step.
+    const bool has_upper = halves - 1 - pair != pair;
+    const int e1 = (ctx - n + pair * kHalfTokens + 1) / kKeys;
+    const int e2 = (ctx - n + min((pair + 1) * kHalfTokens, n) - 1) / kKeys + 1;
+    const int e3 = has_upper ? (ctx - n + (halves - 1 - pair) * kHalfTokens + 1) / kKeys : 0;
 
     // Copies into LDS.  Wavefront w moves step rows 8w .. 8w + 7 of K and of
     // V -- eight consecutive keys, so one page -- as two 1 KiB copies of four
@@ -418,9 +441,8 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
     if (nblk > 1)
         issue(1, 1);
     wait_vm<0>();   // q and the first copies: nothing older than a step's copies stays in flight in the loop
-    // The steps before full_blk mask nothing and run without the mask code.
     int stage = 0;
-    auto run_step = [&](auto masked, int kb) __attribute__((always_inline)) {
+    auto sync_step = [&](int kb) __attribute__((always_inline)) {
         if (kb + 1 < nblk)
             wait_vm<4>();
         else
@@ -428,15 +450,37 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
         stage_barrier();
         if (kb + 2 < nblk)
             issue(kb + 2, stage == 0 ? 2 : stage - 1);
-        compute_step(masked, kb, stage);
-        stage = stage == kStages - 1 ? 0 : stage + 1;
     };
-    const int unmasked = min(full_blk, nblk);
+    // Four stretches of steps, each with one form of the step: every
+    // wavefront unmasked; the early half-tile's causal edge (all masked; the
+    // mask changes nothing for the late rows there); the late half-tile alone,
+    // unmasked; its causal edge, masked.  A wavefront with nothing to do in a
+    // stretch still copies its share and meets the barriers.
     int kb = 0;
-    for (; kb < unmasked; ++kb)
-        run_step(std::false_type{}, kb);
-    for (; kb < nblk; ++kb)
-        run_step(std::true_type{}, kb);
+    for (const int end = min(e1, nblk); kb < end; ++kb) {
+        sync_step(kb);
+        if (wave_live)
+            compute_step(std::false_type{}, kb, stage);
+        stage = stage == kStages - 1 ? 0 : stage + 1;
+    }
+    for (const int end = min(e2, nblk); kb < end; ++kb) {
+        sync_step(kb);
+        if (wave_live)
+            compute_step(std::true_type{}, kb, stage);
+        stage = stage == kStages - 1 ? 0 : stage + 1;
+    }
+    for (const int end = min(e3, nblk); kb < end; ++kb) {
+        sync_step(kb);
+        if (upper)
+            compute_step(std::false_type{}, kb, stage);
+        stage = stage == kStages - 1 ? 0 : stage + 1;
+    }
+    for (; kb < nblk; ++kb) {
+        sync_step(kb);
+        if (upper && has_upper)
+            compute_step(std::true_type{}, kb, stage);
+        stage = stage == kStages - 1 ? 0 : stage + 1;
+    }
 
     // Rows: out[row][h][dim], dims 32 db + 8 (r/4) + 4 half + r%4.
     const float l_tot = pair_sum(l_run);
@@ -484,9 +528,9 @@ hipdecode_status check_prefill(const hipdecode_prefill_params *pp)
         return HIPDECODE_ERR_UNSUPPORTED;
     if (!isfinite(p.scale))
         return HIPDECODE_ERR_SCALE;
-    const int64_t tile_tokens = kPfWaves * (kRowsPerWave / group);
-    const int64_t tiles = ((int64_t)p.max_new_tokens + tile_tokens - 1) / tile_tokens;
-    if ((int64_t)p.num_seqs * tiles * p.num_kv_heads >= kMaxGrid)
+    const int64_t half_tokens = (kPfWaves / 2) * (kRowsPerWave / group);
+    const int64_t pairs = (((int64_t)p.max_new_tokens + half_tokens - 1) / half_tokens + 1) / 2;
+    if ((int64_t)p.num_seqs * pairs * p.num_kv_heads >= kMaxGrid)
         return HIPDECODE_ERR_SHAPE;
     return HIPDECODE_OK;
 }
@@ -533,7 +577,7 @@ HIPDECODE_API hipdecode_status hipdecode_prefill_attn(const hipdecode_prefill_pa
         return HIPDECODE_ERR_ALIGN;
 
     const int group = p.num_q_heads / p.num_kv_heads;
-    const int tile_tokens = kPfWaves * (kRowsPerWave / group);
+    const int half_tokens = (kPfWaves / 2) * (kRowsPerWave / group);
     PrefillArgs a;
     a.q = static_cast<const uint16_t *>(q);
     a.k_pool = static_cast<const uint16_t *>(k_pool);
@@ -549,7 +593,7 @@ HIPDECODE_API hipdecode_status hipdecode_prefill_attn(const hipdecode_prefill_pa
     a.max_blocks = p.max_blocks_per_seq;
     a.num_rows = p.num_rows;
     a.max_new = p.max_new_tokens;
-    a.tiles = (p.max_new_tokens + tile_tokens - 1) / tile_tokens;
+    a.tiles = ((p.max_new_tokens + half_tokens - 1) / half_tokens + 1) / 2;   // workgroups per (request, KV head)
     // c = |scale| log2(e), kept at least 2^-100 so that c * -inf = -inf: for
     // any scale that small every weight 2^(c s - m) is 1.0f anyway (|s| stays
     // far below 2^70), so scale 0 still gives the mean of V and ln(n).
