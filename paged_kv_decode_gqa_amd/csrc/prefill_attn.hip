@@ -16,9 +16,11 @@
 // brought into LDS serves up to 256 rows, which keeps the re-reads of the
 // context (one pass per workgroup) within what the caches deliver.  Causal
 // attention gives late chunk tokens more keys than early ones, so wavefronts
-// 0-3 take an early half-tile and wavefronts 4-7 the matching late one; past
-// the early rows' last key those wavefronts only copy and wait, and the late
-// ones run at one wavefront per SIMD.  Keys go by in steps of 64 (four
+// 0-3 take an early half-tile and wavefronts 4-7 the matching late one.
+// Past the early rows' last key their wavefronts write them out and each
+// takes half of every remaining step of a late wavefront's rows, with a
+// softmax state of its own that is merged through LDS at the end.  Keys go
+// by in steps of 64 (four
 // pages), copied straight from the pools into a three-stage LDS ring
 // (global_load_lds, two steps ahead), both K and V row-major, and used in two
 // halves of 32.
@@ -207,18 +209,18 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
     const int half_tile = upper ? halves - 1 - pair : pair;
     const bool wave_live = !(upper && half_tile == pair);   // uniform
     const int tw0 = half_tile * kHalfTokens + (w % kHalfWaves) * kTokPerWave;   // this wavefront's first token
-    const int tq = tw0 + j / G;
+    int tq = tw0 + j / G;
     const int h = g * G + j % G;
-    const bool row_ok = wave_live && tq < n;
-    const int pos = row_ok ? ctx - n + tq : -1;      // -1: every key masked
-    const size_t row = (size_t)start + min(tq, n - 1);
+    bool row_ok = wave_live && tq < n;
+    int pos = row_ok ? ctx - n + tq : -1;      // -1: every key masked
+    size_t row = (size_t)start + min(tq, n - 1);
 
     // Q^T operand: dims 16 ks + 8 half .. +7 of this lane's row.  A negative
     // scale is applied as a sign flip of q (exact), so that the scale factor
     // used below is never negative and the row maximum of scale * s is
     // scale times the maximum of s.
     bf16x8_t qop[kHeadDim / 16];
-    {
+    auto load_q = [&]() __attribute__((always_inline)) {
         const uint16_t *qrow = a.q + (row * a.num_q_heads + h) * kHeadDim;
 #pragma unroll
         for (int ks = 0; ks < kHeadDim / 16; ++ks) {
@@ -229,7 +231,8 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
             u.w ^= a.q_sign;
             qop[ks] = __builtin_bit_cast(bf16x8_t, u);
         }
-    }
+    };
+    load_q();
 
     const int last_tok = min((halves - pair) * kHalfTokens, n) - 1;   // the workgroup's last chunk token
     const int kv_end = ctx - n + last_tok + 1;           // keys [0, kv_end)
@@ -453,9 +456,10 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
     };
     // Four stretches of steps, each with one form of the step: every
     // wavefront unmasked; the early half-tile's causal edge (all masked; the
-    // mask changes nothing for the late rows there); the late half-tile alone,
-    // unmasked; its causal edge, masked.  A wavefront with nothing to do in a
-    // stretch still copies its share and meets the barriers.
+    // mask changes nothing for the late rows there); then the late rows alone,
+    // each step split between their wavefront and a helper (below), unmasked
+    // and then, over their causal edge, masked.  A wavefront with nothing to
+    // do in a stretch still copies its share and meets the barriers.
     int kb = 0;
     for (const int end = min(e1, nblk); kb < end; ++kb) {
         sync_step(kb);
@@ -469,45 +473,110 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
             compute_step(std::true_type{}, kb, stage);
         stage = stage == kStages - 1 ? 0 : stage + 1;
     }
+    // Rows: out[row][h][dim], dims 32 db + 8 (r/4) + 4 half + r%4.
+    auto write_rows = [&]() __attribute__((always_inline)) {
+        const float l_tot = pair_sum(l_run);
+        if (!row_ok)
+            return;
+        const float inv = 1.f / l_tot;
+        if (OUT_F32) {
+            float *o = static_cast<float *>(a.out) + (row * a.num_q_heads + h) * kHeadDim;
+#pragma unroll
+            for (int db = 0; db < kDimBlocks; ++db)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+                    *reinterpret_cast<float4 *>(o + 32 * db + 8 * rr + 4 * half) =
+                        make_float4(acc[db][4 * rr] * inv, acc[db][4 * rr + 1] * inv, acc[db][4 * rr + 2] * inv,
+                                    acc[db][4 * rr + 3] * inv);
+        } else {
+            uint16_t *o = static_cast<uint16_t *>(a.out) + (row * a.num_q_heads + h) * kHeadDim;
+#pragma unroll
+            for (int db = 0; db < kDimBlocks; ++db)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+                    *reinterpret_cast<uint2 *>(o + 32 * db + 8 * rr + 4 * half) =
+                        make_uint2(pack2_bf16(acc[db][4 * rr] * inv, acc[db][4 * rr + 1] * inv),
+                                   pack2_bf16(acc[db][4 * rr + 2] * inv, acc[db][4 * rr + 3] * inv));
+        }
+        if (a.lse != nullptr && half == 0)
+            a.lse[row * a.num_q_heads + h] = (m_run + log2f(l_tot)) * 0.69314718055994530942f;
+    };
+
+    // The early rows are done.  Their wavefronts write them and then help the
+    // late wavefront of the same position (w + 4): from here each of the two
+    // takes one 32-key half of every step for the late rows -- the late
+    // wavefront the first half, its helper the second -- with a softmax state
+    // of its own, and the two states are merged at the end.
+    const int tw0_late = (halves - 1 - pair) * kHalfTokens + (w % kHalfWaves) * kTokPerWave;
+    const bool late_rows = has_upper && tw0_late < n;   // uniform
+    if (!upper) {
+        write_rows();
+        if (late_rows) {
+            tq = tw0_late + j / G;
+            row_ok = tq < n;
+            pos = row_ok ? ctx - n + tq : -1;
+            row = (size_t)start + min(tq, n - 1);
+            load_q();
+            wait_vm<0>();   // q, and with it the copies issued before it
+#pragma unroll
+            for (int db = 0; db < kDimBlocks; ++db)
+                acc[db] = zero16();
+            m_run = kNegBig;
+            l_run = 0.f;
+        }
+    }
+    const int my_half = upper ? 0 : 1;
     for (const int end = min(e3, nblk); kb < end; ++kb) {
         sync_step(kb);
-        if (upper)
-            compute_step(std::false_type{}, kb, stage);
+        if (late_rows) {
+            const f32x16_t sc = scores(stage, my_half);
+            softmax_pv(std::false_type{}, kb, stage, my_half, sc);
+        }
         stage = stage == kStages - 1 ? 0 : stage + 1;
     }
     for (; kb < nblk; ++kb) {
         sync_step(kb);
-        if (upper && has_upper)
-            compute_step(std::true_type{}, kb, stage);
+        if (late_rows) {
+            const f32x16_t sc = scores(stage, my_half);
+            softmax_pv(std::true_type{}, kb, stage, my_half, sc);
+        }
         stage = stage == kStages - 1 ? 0 : stage + 1;
     }
 
-    // Rows: out[row][h][dim], dims 32 db + 8 (r/4) + 4 half + r%4.
-    const float l_tot = pair_sum(l_run);
-    if (!row_ok)
-        return;
-    const float inv = 1.f / l_tot;
-    if (OUT_F32) {
-        float *o = static_cast<float *>(a.out) + (row * a.num_q_heads + h) * kHeadDim;
+    if (has_upper) {
+        // Merge each helper's state into its late wavefront's, through the
+        // LDS stages (no step reads them any more): 64 lanes x (64 sums,
+        // running max, running sum) floats per helper, lane-major.
+        __syncthreads();
+        float *xch = reinterpret_cast<float *>((w % kHalfWaves) < 2 ? &k_lds[0][0] : &v_lds[0][0]) +
+                     (w % 2) * (kDimBlocks * 16 + 2) * 64;
+        if (!upper && late_rows) {
 #pragma unroll
-        for (int db = 0; db < kDimBlocks; ++db)
+            for (int db = 0; db < kDimBlocks; ++db)
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr)
-                *reinterpret_cast<float4 *>(o + 32 * db + 8 * rr + 4 * half) =
-                    make_float4(acc[db][4 * rr] * inv, acc[db][4 * rr + 1] * inv, acc[db][4 * rr + 2] * inv,
-                                acc[db][4 * rr + 3] * inv);
-    } else {
-        uint16_t *o = static_cast<uint16_t *>(a.out) + (row * a.num_q_heads + h) * kHeadDim;
+                for (int r = 0; r < 16; ++r)
+                    xch[(db * 16 + r) * 64 + lane] = acc[db][r];
+            xch[(kDimBlocks * 16) * 64 + lane] = m_run;
+            xch[(kDimBlocks * 16 + 1) * 64 + lane] = l_run;
+        }
+        __syncthreads();
+        if (upper && late_rows) {
+            const float m_h = xch[(kDimBlocks * 16) * 64 + lane];
+            const float l_h = xch[(kDimBlocks * 16 + 1) * 64 + lane];
+            const float m_new = fmaxf(m_run, m_h);
+            const float a_u = __builtin_amdgcn_exp2f(m_run - m_new);
+            const float a_h = __builtin_amdgcn_exp2f(m_h - m_new);
+            l_run = l_run * a_u + l_h * a_h;
 #pragma unroll
-        for (int db = 0; db < kDimBlocks; ++db)
+            for (int db = 0; db < kDimBlocks; ++db)
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr)
-                *reinterpret_cast<uint2 *>(o + 32 * db + 8 * rr + 4 * half) =
-                    make_uint2(pack2_bf16(acc[db][4 * rr] * inv, acc[db][4 * rr + 1] * inv),
-                               pack2_bf16(acc[db][4 * rr + 2] * inv, acc[db][4 * rr + 3] * inv));
+                for (int r = 0; r < 16; ++r)
+                    acc[db][r] = acc[db][r] * a_u + xch[(db * 16 + r) * 64 + lane] * a_h;
+            m_run = m_new;
+        }
     }
-    if (a.lse != nullptr && half == 0)
-        a.lse[row * a.num_q_heads + h] = (m_run + log2f(l_tot)) * 0.69314718055994530942f;
+    if (upper)
+        write_rows();
 }
 
 hipdecode_status check_prefill(const hipdecode_prefill_params *pp)

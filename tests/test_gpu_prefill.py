@@ -101,6 +101,22 @@ def test_prefill_ragged_chunks():
     check_full(case, inp, o, l, "ragged chunks")
 
 
+# Chunk lengths around the half-tile size of each group size (64 tokens at
+# G = 2, 128 at G = 1, 32 at G = 4): even and odd half-tile counts, a lone
+# middle half-tile, and late half-tiles whose last wavefronts hold no rows.
+PAIRED = [(700, 191), (192, 192), (900, 193), (1255, 255), (256, 256), (3000, 257), (2047, 1023), (40, 33)]
+
+
+@pytest.mark.parametrize("hq,hkv", [(16, 8), (8, 8), (16, 4)])
+def test_prefill_half_tile_pairs(hq, hkv):
+    ctx = [c for c, _ in PAIRED]
+    new = [n for _, n in PAIRED]
+    case, inp = make_prefill_case(ctx, new, seed=45, Hq=hq, Hkv=hkv, poison=True,
+                                  pool_pages=sum((c + 15) // 16 for c in ctx) + 5)
+    o, l = run_gpu(case, inp)
+    check_full(case, inp, o, l, f"half-tile pairs, Hq={hq} Hkv={hkv}")
+
+
 def test_prefill_poisoned_unused_slots():
     # Unused slots of last pages and unused pool pages hold NaN; keys past a
     # tile's last position are masked, and must not turn the output into NaN.
