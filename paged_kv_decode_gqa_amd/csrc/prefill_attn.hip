@@ -80,7 +80,7 @@ struct PrefillArgs {
     int32_t max_blocks;
     int32_t num_rows;
     int32_t max_new;
-    int32_t tiles;          // workgroups (pairs of half-tiles) per request and KV head
+    int32_t pairs;          // workgroups (pairs of half-tiles) per request and KV head
     float scale_log2;       // max(|scale| * log2(e), 2^-100): positive, see the launch
     uint32_t q_sign;        // 0x80008000 when scale < 0: q is negated on load instead
 };
@@ -186,8 +186,8 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
     const int bid = blockIdx.x;
     const int g = bid % a.num_kv_heads;
     const int rest = bid / a.num_kv_heads;
-    const int pair = rest % a.tiles;
-    const int b = rest / a.tiles;
+    const int pair = rest % a.pairs;
+    const int b = rest / a.pairs;
     const int ctx = a.context_lens[b];
     const int start = a.new_start[b];
     const int n = a.new_start[b + 1] - start;
@@ -662,13 +662,13 @@ HIPDECODE_API hipdecode_status hipdecode_prefill_attn(const hipdecode_prefill_pa
     a.max_blocks = p.max_blocks_per_seq;
     a.num_rows = p.num_rows;
     a.max_new = p.max_new_tokens;
-    a.tiles = ((p.max_new_tokens + half_tokens - 1) / half_tokens + 1) / 2;   // workgroups per (request, KV head)
+    a.pairs = ((p.max_new_tokens + half_tokens - 1) / half_tokens + 1) / 2;   // workgroups per (request, KV head)
     // c = |scale| log2(e), kept at least 2^-100 so that c * -inf = -inf: for
     // any scale that small every weight 2^(c s - m) is 1.0f anyway (|s| stays
     // far below 2^70), so scale 0 still gives the mean of V and ln(n).
     a.scale_log2 = fmaxf(fabsf(p.scale) * 1.44269504088896340736f, 0x1p-100f);
     a.q_sign = p.scale < 0.f ? 0x80008000u : 0u;
-    const unsigned grid = (unsigned)((int64_t)p.num_seqs * a.tiles * p.num_kv_heads);
+    const unsigned grid = (unsigned)((int64_t)p.num_seqs * a.pairs * p.num_kv_heads);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool f32 = p.out_dtype == HIPDECODE_F32;
     hipError_t e;
