@@ -154,11 +154,9 @@ void release(hipdecode_step_runner *r)
 hipdecode_status capture(hipdecode_step_runner *r, int32_t bucket, hipGraphExec_t *exec)
 {
     const hipdecode_params p = attn_params(r->cfg, bucket);
-    const hipdecode_append_params ap = append_params(r->cfg, bucket);   // checked at create
     if (hipStreamBeginCapture(r->capture, hipStreamCaptureModeThreadLocal) != hipSuccess)
         return HIPDECODE_ERR_HIP;
     hipdecode_status st = HIPDECODE_OK;
-    (void)ap;
     for (int32_t l = 0; l < r->cfg.num_layers && st == HIPDECODE_OK; ++l)
         st = hipdecode_paged_attn_append(&p, r->cfg.rope_theta, r->q[l], r->k_new[l], r->v_new[l], r->k_pool[l],
                                          r->v_pool[l], r->block_table, r->context_lens, r->out[l],
