@@ -5,7 +5,8 @@ configuration the benchmark times) and are compared on every output.  The edge
 matrix covers empty and one-token contexts, page and partition boundaries,
 NaN-poisoned unused slots, split-count invariance, page relabelling,
 duplicates, CFG pairs, aliased pages, the three group sizes, fp32 output,
-B = 0, workspace reuse and HIP-graph replay.
+B = 0, workspace reuse and HIP-graph replay; 24 seeded random small shapes
+mix all of these parameters.
 """
 import numpy as np
 import pytest
@@ -270,3 +271,35 @@ WORK_LIST_CASES = {
 def test_split_work_list(name, partition):
     case = make_case(WORK_LIST_CASES[name], seed=42, poison=True)
     _check(case, f"work list: {name}, partition {partition}", partition_tokens=partition)
+
+
+def _random_configs(n, seed=2026):
+    """Seeded random small shapes: batch, lengths, group size, wavefronts,
+    schedule, partition, output type, scale sign, poisoned slots."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        G, Hkv = [(1, 8), (2, 8), (4, 4), (2, 2), (1, 1), (4, 1)][rng.integers(6)]
+        B = int(rng.integers(1, 9))
+        ctx = [int(x) for x in rng.choice([0, 1, 15, 16, 17, 64, 65, 200, 1000, 2047, 2048, 4097, 7000], size=B)]
+        schedule = int(rng.choice([0, 1, 2]))
+        if schedule == 2 and Hkv == 1:   # the stream schedule merges at most 1024 partials per KV head
+            schedule = 1
+        waves = 16 if (G <= 2 and schedule != 2 and rng.random() < 0.3) else 0
+        partition = int(rng.choice([0, 64, 128, 512, 2048]))
+        out_dtype = "f32" if rng.random() < 0.3 else "bf16"
+        scale = float(rng.choice([1 / np.sqrt(128), -0.05, 0.0, 0.3]))
+        poison = bool(rng.random() < 0.5)
+        out.append(dict(i=i, G=G, Hkv=Hkv, ctx=ctx, schedule=schedule, waves=waves, partition=partition,
+                        out_dtype=out_dtype, scale=scale, poison=poison))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _random_configs(24), ids=lambda c: f"r{c['i']}")
+def test_randomized_shapes(cfg):
+    c = dict(cfg)
+    case = make_case(c["ctx"], seed=100 + c["i"], Hq=c["G"] * c["Hkv"], Hkv=c["Hkv"], out_dtype=c["out_dtype"],
+                     scale=c["scale"], poison=c["poison"],
+                     pool_pages=sum((n + 15) // 16 for n in c["ctx"]) + 3)
+    _check(case, f"random r{c['i']} G={c['G']} Hkv={c['Hkv']} ctx={c['ctx']}", schedule=c["schedule"],
+           workgroup_waves=c["waves"], partition_tokens=c["partition"])
