@@ -235,3 +235,50 @@ def test_chunked_prefill_pipeline_with_append():
                                                new_start=rows.new_start, q=rows.q, rope=True, theta=rows.theta)
         ref_o, ref_l = oracle.prefill_attn(q_rot, k_ref, v_ref, case.block_table, ctx, rows.new_start, case.scale)
         check_rows(out.float().cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, f"pipeline chunk {i}", v_max(v_ref))
+
+
+def test_prefill_graph_replays():
+    """A captured prefill call replayed three times, with eager work and a
+    changed query in between: each replay equals an eager call on the same
+    inputs bit for bit, and the oracle to the derived bound."""
+    case, inp = make_prefill_case([2500, 700, 64], [600, 700, 64], seed=47)
+    dc = DeviceCase(case)
+    T = inp.rows
+    q = bits_to_bf16(inp.q)
+    new_start = i32(inp.new_start)
+    out = torch.empty((T, case.Hq, case.D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, case.Hq), dtype=torch.float32, device="cuda")
+
+    def call():
+        hd.prefill_attn(q, dc.k, dc.v, dc.table, dc.ctx, new_start, case.scale,
+                        max_new_tokens=inp.max_new_tokens, out=out, lse=lse)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        call()                      # warm-up on the capture stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            call()
+    torch.cuda.synchronize()
+    q0 = q.clone()
+    for rep in range(3):
+        if rep == 1:
+            q.mul_(-1)              # the graph reads q through its pointer
+        out.fill_(SENTINEL)
+        lse.fill_(SENTINEL)
+        g.replay()
+        torch.cuda.synchronize()
+        o_g, l_g = out.clone(), lse.clone()
+        call()
+        torch.cuda.synchronize()
+        assert torch.equal(o_g, out) and torch.equal(l_g, lse), f"replay {rep} differs from the eager call"
+        log(f"[prefill] graph replay {rep}: equal to the eager call")
+    q.copy_(q0)
+    g.replay()
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy().astype(np.float64)
+    l = lse.cpu().numpy().astype(np.float64)
+    check_full(case, inp, o, l, "graph replay")
