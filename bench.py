@@ -207,7 +207,7 @@ def main(argv=None) -> int:
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the path has no multi-GPU sharding in this build)", file=sys.stderr)
+              "(the library has no multi-GPU sharding)", file=sys.stderr)
         return 2
 
     import numpy as np
