@@ -169,11 +169,15 @@ __device__ __forceinline__ void load_q(u32x4 (&qv)[G], const DecodeArgs &a, size
 // (slot (ctx - 1) % 16, row b of k_new/v_new) is taken from k_new/v_new --
 // K rotated with `angles` when RoPE is on -- written to the pool and folded
 // from registers; no other workgroup reads that page.
-template <int G, int WAVES, bool FUSED = false>
+struct NoHook {
+    __device__ __forceinline__ void operator()() const {}
+};
+
+template <int G, int WAVES, bool FUSED = false, class Hook = NoHook>
 __device__ __forceinline__ void fold_range(Stream<G> &st, const DecodeArgs &a, const u32x4 (&qv)[G],
                                            const int32_t *trow, int g, int p_begin, int p_end,
                                            int n_pages, int ctx, int entry, const Lane &ln, int b = 0,
-                                           const double2 *angles = nullptr)
+                                           const double2 *angles = nullptr, Hook before_fold = Hook())
 {
     const uint32_t tok_bytes = (uint32_t)a.num_kv_heads * kHeadDim * 2;   // bytes between slots
     const size_t page_elems = (size_t)kPageSize * a.num_kv_heads * kHeadDim;
@@ -204,8 +208,12 @@ __device__ __forceinline__ void fold_range(Stream<G> &st, const DecodeArgs &a, c
             fold_page<G, false>(st, r, qv, a.scale_log2, 0, 0);
     };
 
-    if (npw > 0) {
+    // before_fold runs in every wavefront once the first page is in flight
+    // (the fused kernel rotates q there); it may hold a workgroup barrier.
+    if (npw > 0)
         issue(ra, 0);
+    before_fold();
+    if (npw > 0) {
         int i = 0;
         for (; i + 2 < npw; i += 2) {
             issue(rb, i + 1);
@@ -575,31 +583,45 @@ void paged_decode_kernel(DecodeArgs a)
 
     u32x4 qv[G];
     load_q<G>(qv, a, row0, ln.sub);
-    const double2 *rope_cs = nullptr;
+    // Fused: RoPE of this lane's 8 dimensions of its G query heads at position
+    // ctx - 1.  The partner dimensions are loaded here, before the first page;
+    // the 64 angles (first wavefront, through LDS) and the rotation run while
+    // that page is in flight.
+    __shared__ double2 angles[FUSED ? rope::kHalf : 1];
+    const bool rope_on = FUSED && a.rope_theta > 0.0;
+    u32x4 qp[G];
     if constexpr (FUSED) {
-        // RoPE of this lane's 8 dimensions of its G query heads at position
-        // ctx - 1; the 64 angles come from the first wavefront through LDS.
-        __shared__ double2 angles[rope::kHalf];
-        if (a.rope_theta > 0.0) {
-            if (ln.wave == 0)
-                angles[ln.lane] = rope::angle(a.rope_theta, ctx - 1, ln.lane);
-            __syncthreads();
-            const int base = 8 * (ln.sub & 7);
+        if (rope_on) {
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
-                const u32x4 qp = load16(a.q + (row0 + h) * kHeadDim + (ln.sub ^ 8) * 8);
-                const uint4 r = rope::rotate8(make_uint4(qv[h].x, qv[h].y, qv[h].z, qv[h].w),
-                                              make_uint4(qp.x, qp.y, qp.z, qp.w), ln.sub >= 8,
-                                              [&](int e) { return angles[base + e]; });
-                qv[h] = u32x4{r.x, r.y, r.z, r.w};
-            }
-            rope_cs = angles;
+            for (int h = 0; h < G; ++h)
+                qp[h] = load16(a.q + (row0 + h) * kHeadDim + (ln.sub ^ 8) * 8);
         }
     }
+    auto rotate_q = [&]() __attribute__((always_inline)) {
+        if constexpr (FUSED) {
+            if (rope_on) {
+                if (ln.wave == 0)
+                    angles[ln.lane] = rope::angle(a.rope_theta, ctx - 1, ln.lane);
+                __syncthreads();
+                const int base = 8 * (ln.sub & 7);
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    const uint4 r = rope::rotate8(make_uint4(qv[h].x, qv[h].y, qv[h].z, qv[h].w),
+                                                  make_uint4(qp[h].x, qp[h].y, qp[h].z, qp[h].w), ln.sub >= 8,
+                                                  [&](int e) { return angles[base + e]; });
+                    qv[h] = u32x4{r.x, r.y, r.z, r.w};
+                }
+            }
+        }
+    };
     Stream<G> st;
     st.init();
-    fold_range<G, WAVES, FUSED>(st, a, qv, trow, g, p_begin, min(p_begin + a.partition_pages, n_pages), n_pages,
-                                ctx, spec_entry, ln, b, rope_cs);
+    if constexpr (FUSED)
+        fold_range<G, WAVES, FUSED>(st, a, qv, trow, g, p_begin, min(p_begin + a.partition_pages, n_pages),
+                                    n_pages, ctx, spec_entry, ln, b, rope_on ? angles : nullptr, rotate_q);
+    else
+        fold_range<G, WAVES, FUSED>(st, a, qv, trow, g, p_begin, min(p_begin + a.partition_pages, n_pages),
+                                    n_pages, ctx, spec_entry, ln, b);
     publish_streams<G, WAVES>(st, sm, ln);
     __syncthreads();
 
