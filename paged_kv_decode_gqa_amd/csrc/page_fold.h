@@ -75,26 +75,37 @@ struct PageRegs {
     u32x4 v[4];
 };
 
-// kpage/vpage: the page's first element (wave-uniform); lane_off: this
-// lane's byte offset inside the page (head, row-group and dims); tok4: the
-// byte distance of four slots.  A uniform 64-bit base plus a 32-bit lane
-// offset keeps the address arithmetic in scalar registers.
-__device__ __forceinline__ const u32x4 *at_bytes(const uint16_t *base, uint32_t off)
+// A buffer resource for one page: the page's first byte as a wave-uniform
+// 64-bit base in scalar registers, and a record limit no lane offset reaches
+// (offsets stay inside the 32 KiB page).  Each lane then supplies only a
+// 32-bit byte offset, so a pool may be any size.
+constexpr int kBufferWord3 = 0x00020000;   // raw (untyped) loads
+constexpr int kCachePolicyNt = 2;          // non-temporal: stream through the caches
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_resource(const uint16_t *page)
 {
-    return reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(base) + off);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(page), (short)0, 0x7fffffff, kBufferWord3);
 }
 
-// K/V rows are read once per call: non-temporal loads stream them through the
-// caches without displacing anything (measured 8-9% faster on MI355X).
+// kpage/vpage: the page's first element (wave-uniform); lane_off: this
+// lane's byte offset inside the page (head, row-group and dims); tok4: the
+// byte distance of four slots.  K/V rows are read once per call:
+// non-temporal loads stream them through the caches without displacing
+// anything (measured 8-9% faster on MI355X; the scope bits sc0/sc1 on top
+// of it measured no different).
 __device__ __forceinline__ void load_page(PageRegs &r, const uint16_t *kpage, const uint16_t *vpage,
                                           uint32_t lane_off, uint32_t tok4)
 {
+    const __amdgpu_buffer_rsrc_t rk = page_resource(kpage);
+    const __amdgpu_buffer_rsrc_t rv = page_resource(vpage);
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-        r.k[t] = __builtin_nontemporal_load(at_bytes(kpage, lane_off + t * tok4));
+        r.k[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, lane_off + t * tok4, 0,
+                                                                                 kCachePolicyNt));
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-        r.v[t] = __builtin_nontemporal_load(at_bytes(vpage, lane_off + t * tok4));
+        r.v[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, lane_off + t * tok4, 0,
+                                                                                 kCachePolicyNt));
 }
 
 template <int G>
