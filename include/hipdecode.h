@@ -366,7 +366,9 @@ hipdecode_status hipdecode_step_runner_create(const hipdecode_step_config *confi
                                               hipdecode_step_runner **runner);
 
 /* One decode step for num_seqs requests (0 is a no-op) with host context
- * lengths context_lens_host[0 .. num_seqs), enqueued on `stream`. */
+ * lengths context_lens_host[0 .. num_seqs), enqueued on `stream`.  A length
+ * below 0 or above max_context_len gives HIPDECODE_ERR_SHAPE and enqueues
+ * nothing. */
 hipdecode_status hipdecode_step_runner_step(hipdecode_step_runner *runner, int32_t num_seqs,
                                             const int32_t *context_lens_host, void *stream);
 
@@ -384,7 +386,10 @@ hipdecode_status hipdecode_step_runner_destroy(hipdecode_step_runner *runner);
  * rotates its query heads itself.  Split schedule only (schedule 0 or 1):
  * a stream schedule gives HIPDECODE_ERR_UNSUPPORTED; a rope_theta that is
  * negative or not finite gives HIPDECODE_ERR_SCALE.  Same buffers, workspace
- * and contract as hipdecode_paged_attn otherwise; the pools are written. */
+ * and contract as hipdecode_paged_attn otherwise; the pools are written.  A
+ * request whose context_lens[b] exceeds max_context_len (a broken contract)
+ * writes nothing to the pools, as hipdecode_kv_append would not; its out and
+ * lse are unspecified. */
 hipdecode_status hipdecode_paged_attn_append(const hipdecode_params *params,
                                              double rope_theta,
                                              const void *q,

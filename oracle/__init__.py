@@ -59,9 +59,6 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.oracle_attend_one.restype = ctypes.c_int
     lib.oracle_paged_attn.argtypes = [ctypes.POINTER(OracleShape), p, p, p, p, p, ctypes.c_double, p, p]
     lib.oracle_paged_attn.restype = ctypes.c_int
-    lib.oracle_paged_attn_pairs.argtypes = [ctypes.POINTER(OracleShape), p, p, p, p, p, ctypes.c_double,
-                                            p, ctypes.c_int32, p, p]
-    lib.oracle_paged_attn_pairs.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_round_bf16.argtypes = [ctypes.c_double]
@@ -112,23 +109,6 @@ def paged_attn(q, k_pool, v_pool, block_table, context_lens, scale, *, lib: ctyp
                                out.ctypes.data, lse.ctypes.data)
     if rc != 0:
         raise OracleError(f"oracle_paged_attn returned {rc}")
-    return out, lse
-
-
-def paged_attn_pairs(q, k_pool, v_pool, block_table, context_lens, scale, pairs, *,
-                     lib: ctypes.CDLL | None = None):
-    """fp64 (out [n,D], lse [n]) for the (request, query head) pairs listed."""
-    lib = lib or load()
-    shape, q, k_pool, v_pool, block_table, context_lens = _prep(q, k_pool, v_pool, block_table, context_lens)
-    pairs = np.ascontiguousarray(np.asarray(pairs, dtype=np.int32).reshape(-1, 2))
-    n = pairs.shape[0]
-    out = np.zeros((n, shape.head_dim), dtype=np.float64)
-    lse = np.zeros((n,), dtype=np.float64)
-    rc = lib.oracle_paged_attn_pairs(ctypes.byref(shape), q.ctypes.data, k_pool.ctypes.data,
-                                     v_pool.ctypes.data, block_table.ctypes.data, context_lens.ctypes.data,
-                                     float(scale), pairs.ctypes.data, n, out.ctypes.data, lse.ctypes.data)
-    if rc != 0:
-        raise OracleError(f"oracle_paged_attn_pairs returned {rc}")
     return out, lse
 
 

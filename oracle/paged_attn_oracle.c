@@ -136,33 +136,6 @@ int oracle_paged_attn(const oracle_shape *s, const uint16_t *q,
     return err;
 }
 
-int oracle_paged_attn_pairs(const oracle_shape *s, const uint16_t *q,
-                            const uint16_t *k_pool, const uint16_t *v_pool,
-                            const int32_t *block_table, const int32_t *context_lens,
-                            double scale, const int32_t *pairs, int32_t n_pairs,
-                            double *out, double *lse)
-{
-    int rc = oracle_validate(s, block_table, context_lens);
-    if (rc != ORACLE_OK)
-        return rc;
-    for (int32_t i = 0; i < n_pairs; ++i)
-        if (pairs[2 * i] < 0 || pairs[2 * i] >= s->num_seqs ||
-            pairs[2 * i + 1] < 0 || pairs[2 * i + 1] >= s->num_q_heads)
-            return ORACLE_EINVAL;
-    int err = ORACLE_OK;
-#pragma omp parallel for schedule(dynamic, 1)
-    for (int32_t i = 0; i < n_pairs; ++i) {
-        int r = oracle_attend_one(s, q, k_pool, v_pool, block_table, context_lens, scale,
-                                  pairs[2 * i], pairs[2 * i + 1],
-                                  out + (size_t)i * s->head_dim, lse + i);
-        if (r != ORACLE_OK) {
-#pragma omp critical
-            err = r;
-        }
-    }
-    return err;
-}
-
 int oracle_max_threads(void)
 {
 #ifdef _OPENMP

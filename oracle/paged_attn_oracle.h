@@ -83,14 +83,6 @@ int oracle_paged_attn(const oracle_shape *s, const uint16_t *q,
                       const int32_t *block_table, const int32_t *context_lens,
                       double scale, double *out, double *lse);
 
-/* A chosen list of (request, query head) pairs, pairs[2*i] = b and
- * pairs[2*i+1] = h; out is [n_pairs][head_dim], lse is [n_pairs]. */
-int oracle_paged_attn_pairs(const oracle_shape *s, const uint16_t *q,
-                            const uint16_t *k_pool, const uint16_t *v_pool,
-                            const int32_t *block_table, const int32_t *context_lens,
-                            double scale, const int32_t *pairs, int32_t n_pairs,
-                            double *out, double *lse);
-
 /* Threads an OpenMP region of this library would use. */
 int oracle_max_threads(void);
 

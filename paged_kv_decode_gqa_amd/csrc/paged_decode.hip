@@ -168,7 +168,10 @@ __device__ __forceinline__ void load_q(u32x4 (&qv)[G], const DecodeArgs &a, size
 // FUSED: the request's last page always goes that way, and its new token
 // (slot (ctx - 1) % 16, row b of k_new/v_new) is taken from k_new/v_new --
 // K rotated with `angles` when RoPE is on -- written to the pool and folded
-// from registers; no other workgroup reads that page.
+// from registers; no other workgroup reads that page.  With append_new false
+// (a context length past the host bound, so ctx was clamped and slot ctx - 1
+// holds a real cached token) nothing is written and the page is folded as
+// the pool holds it.
 struct NoHook {
     __device__ __forceinline__ void operator()() const {}
 };
@@ -177,7 +180,8 @@ template <int G, int WAVES, bool FUSED = false, class Hook = NoHook>
 __device__ __forceinline__ void fold_range(Stream<G> &st, const DecodeArgs &a, const u32x4 (&qv)[G],
                                            const int32_t *trow, int g, int p_begin, int p_end,
                                            int n_pages, int ctx, int entry, const Lane &ln, int b = 0,
-                                           const double2 *angles = nullptr, Hook before_fold = Hook())
+                                           const double2 *angles = nullptr, Hook before_fold = Hook(),
+                                           bool append_new = true)
 {
     const uint32_t tok_bytes = (uint32_t)a.num_kv_heads * kHeadDim * 2;   // bytes between slots
     const size_t page_elems = (size_t)kPageSize * a.num_kv_heads * kHeadDim;
@@ -236,7 +240,7 @@ __device__ __forceinline__ void fold_range(Stream<G> &st, const DecodeArgs &a, c
                       lane_off, tok4);
             if constexpr (FUSED) {
                 const int slot = (ctx - 1) % kPageSize;
-                if (ln.row == (slot & 3)) {   // the 16 lanes holding the new token, in register slot / 4
+                if (append_new && ln.row == (slot & 3)) {   // the 16 lanes holding the new token, in register slot / 4
                     const size_t nrow = ((size_t)b * a.num_kv_heads + g) * kHeadDim;
                     u32x4 kn = load16(a.k_new + nrow + ln.sub * 8);
                     const u32x4 vn = load16(a.v_new + nrow + ln.sub * 8);
@@ -490,17 +494,19 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane)
 // workgroup the dispatcher places early carries work.
 struct RealUnit {
     int b, split, ctx;
+    bool over;   // the request's context length exceeds the host bound (ctx is clamped)
 };
 
 __device__ __forceinline__ RealUnit real_unit(const DecodeArgs &a, int u)
 {
     const int lane = (int)(threadIdx.x & 63);
     const int span = kPageSize * a.partition_pages;
-    RealUnit r{-1, 0, 0};
+    RealUnit r{-1, 0, 0, false};
     int carry = 0;
     for (int c0 = 0; c0 < a.num_seqs; c0 += 64) {
         const int j = c0 + lane;
-        const int cj = j < a.num_seqs ? clamp_ctx(a.context_lens[j], a.max_context_len) : 0;
+        const int raw = j < a.num_seqs ? a.context_lens[j] : 0;
+        const int cj = clamp_ctx(raw, a.max_context_len);
         const int nj = j < a.num_seqs ? max(1, (cj + span - 1) / span) : 0;
         const int incl = wave_inclusive_scan(nj, lane);
         const int excl = incl - nj;
@@ -510,6 +516,7 @@ __device__ __forceinline__ RealUnit real_unit(const DecodeArgs &a, int u)
             r.b = c0 + l;
             r.split = u - carry - __builtin_amdgcn_readlane(excl, l);
             r.ctx = __builtin_amdgcn_readlane(cj, l);
+            r.over = __builtin_amdgcn_readlane(raw, l) > a.max_context_len;
             break;
         }
         carry += __builtin_amdgcn_readlane(incl, 63);
@@ -546,11 +553,14 @@ void paged_decode_kernel(DecodeArgs a)
                               ? a.block_table[(size_t)b_full * a.max_blocks + spec_idx] : -1;
 
     int b, split, ctx, spec_entry;
+    [[maybe_unused]] bool over;   // context length past the host bound: the fused kernel appends nothing
     if (a.num_seqs == 1 || a.nsplit_max == 1) {
         // Every unit of the full grid up to a request's partition count is real.
         b = b_full;
         split = split_full;
-        ctx = clamp_ctx(a.context_lens[b], a.max_context_len);
+        const int raw = a.context_lens[b];
+        ctx = clamp_ctx(raw, a.max_context_len);
+        over = raw > a.max_context_len;
         spec_entry = spec_full;
         const int nsplit_b = (ctx + kPageSize * pp - 1) / (kPageSize * pp);
         if (ctx == 0 ? split != 0 : split >= nsplit_b)
@@ -563,6 +573,7 @@ void paged_decode_kernel(DecodeArgs a)
         b = u.b;
         split = u.split;
         ctx = u.ctx;
+        over = u.over;
         spec_entry = spec_full;
         if (b != b_full || split != split_full) {   // ragged batch: fetch this partition's entries
             const int idx = split * pp + ln.wave + WAVES * ln.lane;
@@ -618,7 +629,7 @@ void paged_decode_kernel(DecodeArgs a)
     st.init();
     if constexpr (FUSED)
         fold_range<G, WAVES, FUSED>(st, a, qv, trow, g, p_begin, min(p_begin + a.partition_pages, n_pages),
-                                    n_pages, ctx, spec_entry, ln, b, rope_on ? angles : nullptr, rotate_q);
+                                    n_pages, ctx, spec_entry, ln, b, rope_on ? angles : nullptr, rotate_q, !over);
     else
         fold_range<G, WAVES, FUSED>(st, a, qv, trow, g, p_begin, min(p_begin + a.partition_pages, n_pages),
                                     n_pages, ctx, spec_entry, ln, b);

@@ -261,6 +261,11 @@ HIPDECODE_API hipdecode_status hipdecode_step_runner_step(hipdecode_step_runner 
         return HIPDECODE_ERR_SHAPE;
     if (context_lens_host == nullptr)
         return HIPDECODE_ERR_NULL;
+    // the graphs were sized for max_context_len: a longer context would be
+    // clamped by the kernel and its new token written over a cached one
+    for (int32_t k = 0; k < num_seqs; ++k)
+        if (context_lens_host[k] < 0 || context_lens_host[k] > r->cfg.max_context_len)
+            return HIPDECODE_ERR_SHAPE;
     hipGraphExec_t &exec = r->graphs[log2_of(bucket)];
     if (exec == nullptr) {
         const hipdecode_status st = capture(r, bucket, &exec);

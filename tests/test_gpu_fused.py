@@ -83,3 +83,44 @@ def test_fused_group_sizes(hq, hkv):
 def test_fused_fp32_out():
     case = make_case([512, 97], seed=74, pool_pages=64)
     run_case(case, make_append_inputs(case, None, seed=74), theta=THETA, out_dtype=torch.float32, what="fp32")
+
+
+@pytest.mark.parametrize("theta", [0.0, THETA])
+def test_fused_context_past_bound_writes_nothing(theta):
+    """A request whose context length exceeds the host bound breaks the
+    contract: the kernel clamps its context, so slot ctx - 1 would be a real
+    cached token.  The fused call must then leave that request's pages
+    untouched, as the separate append does, while the other requests append
+    normally."""
+    case = make_case([300, 1000, 517], seed=75, pool_pages=120)
+    inputs = make_append_inputs(case, None, seed=75)
+    dc = DeviceCase(case)
+    bound = 800                     # request 1 (1000 tokens) is past it
+    k_before, v_before = to_bits(dc.k).copy(), to_bits(dc.v).copy()
+    hd.paged_attn_append(bits_to_bf16(inputs.q), bits_to_bf16(inputs.k_new), bits_to_bf16(inputs.v_new), dc.k, dc.v,
+                         dc.table, dc.ctx, case.scale, max_context_len=bound, rope_theta=theta)
+    torch.cuda.synchronize()
+    gk, gv = to_bits(dc.k), to_bits(dc.v)
+    pages_1 = {int(p) for p in case.block_table[1, :(1000 + 15) // 16]}
+    for p in pages_1:
+        assert np.array_equal(gk[p], k_before[p]) and np.array_equal(gv[p], v_before[p]), \
+            f"page {p} of the over-long request was written"
+    # the valid requests appended exactly what the oracle appends
+    valid_ctx = case.context_lens.copy()
+    valid_ctx[1] = 0
+    rope = theta > 0
+    kp, vp, _ = oracle.kv_append(inputs.k_new, inputs.v_new, case.block_table, valid_ctx, case.k_pool, case.v_pool,
+                                 q=inputs.q, rope=rope, theta=theta if rope else 1e6)
+    assert np.array_equal(gv, vp), "V pool differs"
+    if rope:
+        for b in (0, 2):
+            p = int(case.context_lens[b]) - 1
+            page, slot = int(case.block_table[b, p // 16]), p % 16
+            check_rotated(gk[page, slot], kp[page, slot], inputs.k_new[b], p, theta, f"K of request {b}")
+        diff = {(int(p), int(s)) for p, s in np.argwhere(np.any(gk != kp, axis=(2, 3)))}
+        written = {(int(case.block_table[b, (int(case.context_lens[b]) - 1) // 16]),
+                    (int(case.context_lens[b]) - 1) % 16) for b in (0, 2)}
+        assert diff <= written, "K changed outside the valid requests' new slots"
+    else:
+        assert np.array_equal(gk, kp), "K pool differs"
+    log(f"[fused] context past the bound (theta={theta}): pools as the oracle's, over-long request untouched")

@@ -147,3 +147,19 @@ def test_step_runner_pipelined_steps():
         err, _ = compare(layer["out"][:B], layer["lse"][:B], ref_out, ref_lse, what=f"pipelined layer {l}")
         log(f"[step] pipelined layer {l}: pools equal, max|dout|={err:.2e}")
     s.runner.close()
+
+
+def test_step_runner_rejects_context_past_bound():
+    """A host context length above the runner's max_context_len (or below 0)
+    is refused before anything is enqueued, so no graph sized for the bound
+    can clamp it and append over a cached token."""
+    s = Setup([300, 1, 517], layers=1, max_seqs=4, seed=65)
+    k_before = to_bits(s.layers[0]["k_pool"]).copy()
+    for bad in ([300, 1, s.max_context_len + 1], [300, -1, 517]):
+        with pytest.raises(hd.HipDecodeError) as ei:
+            s.runner.step(np.array(bad, dtype=np.int32))
+        assert ei.value.status == hd.HIPDECODE_ERR_SHAPE
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits(s.layers[0]["k_pool"]), k_before), "a refused step wrote the pool"
+    s.runner.close()
+    log("[step] context lengths outside [0, max_context_len] refused")
