@@ -405,6 +405,43 @@ hipdecode_status hipdecode_paged_attn_append(const hipdecode_params *params,
                                              size_t workspace_bytes,
                                              void *stream);
 
+/* ------------------------------------------------------------------------
+ * Allocation-free decode.
+ *
+ * For callers that cannot allocate device memory at all -- code running under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc --
+ * and so cannot provide the workspace hipdecode_paged_attn takes.  Same
+ * parameters, buffers, result and contract as hipdecode_paged_attn without
+ * `workspace`/`workspace_bytes`: the arrival counters and split partials live
+ * in a static device array of HIPDECODE_NOALLOC_SCRATCH_BYTES inside the
+ * library, one per GPU, held until the process ends.  The call allocates
+ * nothing: no hipMalloc, no hipFree, no allocating library routine.
+ *
+ * Limits: at most 4096 (request, KV head) pairs (num_seqs * num_kv_heads),
+ * and the split partials must fit the rest of the array (16 MiB minus 1 MiB of
+ * counters: for example 32 requests up to 67,500 tokens, or 16 at 28,672,
+ * fit); a call past either gives HIPDECODE_ERR_WORKSPACE and enqueues
+ * nothing.  The first call on a device looks up the array's address there and
+ * zero-fills its counter region with a kernel on `stream`; every completed
+ * call leaves the counters at zero again.
+ *
+ * Every call on a GPU shares that GPU's array: calls that may overlap in time
+ * on one GPU (different streams without ordering between them, or several
+ * host threads) race on it and give unspecified results.  Order them.
+ * ------------------------------------------------------------------------ */
+
+#define HIPDECODE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+hipdecode_status hipdecode_paged_attn_noalloc(const hipdecode_params *params,
+                                              const void *q,
+                                              const void *k_pool,
+                                              const void *v_pool,
+                                              const int32_t *block_table,
+                                              const int32_t *context_lens,
+                                              void *out,
+                                              float *lse,
+                                              void *stream);
+
 /* Static English text for a status code; never NULL. */
 const char *hipdecode_status_string(hipdecode_status status);
 

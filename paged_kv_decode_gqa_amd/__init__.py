@@ -48,8 +48,12 @@ EXPORTED = (
     "hipdecode_step_runner_create",
     "hipdecode_step_runner_step",
     "hipdecode_step_runner_destroy",
+    "hipdecode_paged_attn_noalloc",
     "hipdecode_status_string",
 )
+
+# Bytes of the library's static scratch behind hipdecode_paged_attn_noalloc.
+HIPDECODE_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class hipdecode_params(ctypes.Structure):
@@ -190,6 +194,8 @@ def library() -> ctypes.CDLL:
     lib.hipdecode_step_runner_step.restype = ctypes.c_int
     lib.hipdecode_step_runner_destroy.argtypes = [vp]
     lib.hipdecode_step_runner_destroy.restype = ctypes.c_int
+    lib.hipdecode_paged_attn_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.hipdecode_paged_attn_noalloc.restype = ctypes.c_int
     lib.hipdecode_status_string.argtypes = [ctypes.c_int]
     lib.hipdecode_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -283,6 +289,21 @@ def hipdecode_paged_attn(params: hipdecode_params, q, k_pool, v_pool, block_tabl
                                         _ptr(workspace), ws_bytes, _stream_handle(stream))
     if st != HIPDECODE_OK:
         raise HipDecodeError(st, "hipdecode_paged_attn")
+
+
+def hipdecode_paged_attn_noalloc(params: hipdecode_params, q, k_pool, v_pool, block_table, context_lens,
+                                 out, lse, stream=None) -> None:
+    """Enqueue one allocation-free call (the library's static scratch stands
+    in for the workspace).  Raises HipDecodeError on a non-OK status."""
+    for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool), ("block_table", block_table),
+                    ("context_lens", context_lens), ("out", out), ("lse", lse)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    st = library().hipdecode_paged_attn_noalloc(ctypes.byref(params), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                                _ptr(block_table), _ptr(context_lens), _ptr(out), _ptr(lse),
+                                                _stream_handle(stream))
+    if st != HIPDECODE_OK:
+        raise HipDecodeError(st, "hipdecode_paged_attn_noalloc")
 
 
 class PreparedCall:

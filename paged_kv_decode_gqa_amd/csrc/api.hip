@@ -5,6 +5,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 namespace hipdecode {
 namespace {
 
@@ -13,6 +15,12 @@ constexpr int64_t kTargetWorkgroupsFew = 256;     // one per CU, for a few long 
 constexpr int64_t kFewPairs = 32;                 // (request, KV head) pairs counted as few
 constexpr int64_t kSingleSplitMax = 2048;         // contexts up to this long are not split at all
 constexpr int64_t kBalancedPartition = 2048;      // partition when the target would exceed kMaxPartition
+
+// hipdecode_paged_attn_noalloc: its static scratch and the fixed region of
+// arrival counters at the start of it (4096 (request, KV head) pairs).
+constexpr size_t kNoallocBytes = HIPDECODE_NOALLOC_SCRATCH_BYTES;
+constexpr size_t kNoallocCounterBytes = (size_t)4096 * kCounterStride * sizeof(int32_t);
+static_assert(kNoallocBytes % 256 == 0 && kNoallocCounterBytes < kNoallocBytes, "scratch layout");
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -80,13 +88,22 @@ int32_t nsplit_max_of(const hipdecode_params &p, int32_t part)
     return n < 1 ? 1 : (int32_t)n;
 }
 
-WorkspaceLayout layout_of(const hipdecode_params &p)
+size_t counter_bytes(const hipdecode_params &p)
+{
+    return (size_t)p.num_seqs * (size_t)p.num_kv_heads * kCounterStride * sizeof(int32_t);
+}
+
+// counter_region: bytes reserved for the arrival counters at the start; the
+// caller-workspace layout reserves exactly what the call needs, the static
+// scratch of the allocation-free entry point a fixed region (so every call
+// finds its counters where the previous calls left them at zero).
+WorkspaceLayout layout_with(const hipdecode_params &p, size_t counter_region)
 {
     WorkspaceLayout w;
     w.counters = 0;
     // one 256-byte line per counter: the tickets of different KV heads never
     // meet on one line (measured 4% at the 32-request mix, 14% at 1 x 3.5k)
-    w.part_ml = align256((size_t)p.num_seqs * (size_t)p.num_kv_heads * kCounterStride * sizeof(int32_t));
+    w.part_ml = align256(counter_region);
     size_t partials;
     if (plan_schedule(p) == kScheduleStream) {
         // two per tile; tiles <= W + B * Hkv (a tile is a full block, or a request's last)
@@ -105,6 +122,8 @@ WorkspaceLayout layout_of(const hipdecode_params &p)
     w.total = w.part_acc + partials * kHeadDim * sizeof(float);
     return w;
 }
+
+WorkspaceLayout layout_of(const hipdecode_params &p) { return layout_with(p, counter_bytes(p)); }
 
 hipdecode_status check(const hipdecode_params *pp)
 {
@@ -222,12 +241,10 @@ HIPDECODE_API hipdecode_status hipdecode_workspace_init(void *workspace, size_t 
 namespace hipdecode {
 namespace {
 
-// The body of both decode entry points; `fused` also appends each request's
-// new token (k_new/v_new, RoPE with rope_theta when > 0) inside the kernel.
-hipdecode_status run_decode(const hipdecode_params *params, const void *q, const void *k_pool, const void *v_pool,
+// Pointer and argument checks of a decode call, before anything is enqueued.
+hipdecode_status check_call(const hipdecode_params *params, const void *q, const void *k_pool, const void *v_pool,
                             const int32_t *block_table, const int32_t *context_lens, void *out, float *lse,
-                            void *workspace, size_t workspace_bytes, void *stream, bool fused,
-                            const void *k_new, const void *v_new, double rope_theta)
+                            void *workspace, bool fused, const void *k_new, const void *v_new, double rope_theta)
 {
     const hipdecode_status st = check(params);
     if (st != HIPDECODE_OK)
@@ -255,13 +272,38 @@ hipdecode_status run_decode(const hipdecode_params *params, const void *q, const
         (reinterpret_cast<uintptr_t>(block_table) & 3u) != 0 ||
         (reinterpret_cast<uintptr_t>(context_lens) & 3u) != 0)
         return HIPDECODE_ERR_ALIGN;
+    return HIPDECODE_OK;
+}
 
-    const int32_t part = plan_partition(p);
-    const int32_t nsplit = nsplit_max_of(p, part);
-    const WorkspaceLayout w = layout_of(p);
+// The body of the decode entry points; `fused` also appends each request's
+// new token (k_new/v_new, RoPE with rope_theta when > 0) inside the kernel;
+// `scratch_mode`: `workspace` is the static scratch of the allocation-free
+// entry point.
+hipdecode_status run_decode(const hipdecode_params *params, const void *q, const void *k_pool, const void *v_pool,
+                            const int32_t *block_table, const int32_t *context_lens, void *out, float *lse,
+                            void *workspace, size_t workspace_bytes, void *stream, bool fused,
+                            const void *k_new, const void *v_new, double rope_theta, bool scratch_mode = false)
+{
+    const hipdecode_status st = check_call(params, q, k_pool, v_pool, block_table, context_lens, out, lse, workspace,
+                                           fused, k_new, v_new, rope_theta);
+    if (st != HIPDECODE_OK || params->num_seqs == 0)
+        return st;
+    const hipdecode_params &p = *params;
+    WorkspaceLayout w;
+    if (scratch_mode) {
+        // the allocation-free entry point: `workspace` is this device's static
+        // scratch, counters in a fixed region at its start
+        if (counter_bytes(p) > kNoallocCounterBytes)
+            return HIPDECODE_ERR_WORKSPACE;
+        w = layout_with(p, kNoallocCounterBytes);
+    } else {
+        w = layout_of(p);
+    }
     if (workspace_bytes < w.total)
         return HIPDECODE_ERR_WORKSPACE;
 
+    const int32_t part = plan_partition(p);
+    const int32_t nsplit = nsplit_max_of(p, part);
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     DecodeArgs a;
     a.num_seqs = p.num_seqs;
@@ -318,6 +360,70 @@ HIPDECODE_API hipdecode_status hipdecode_paged_attn_append(const hipdecode_param
 {
     return run_decode(params, q, k_pool, v_pool, block_table, context_lens, out, lse, workspace, workspace_bytes,
                       stream, true, k_new, v_new, rope_theta);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free decode.  The workspace of hipdecode_paged_attn (arrival
+// counters and split partials) lives in this file-scope device array instead
+// of caller memory.  Each device holds its own copy, for the life of the
+// process.  Host code never passes the array's name to a kernel: its address
+// on the current device comes from hipGetSymbolAddress, once per device, and
+// only that pointer is used.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[hipdecode::kNoallocBytes];
+
+namespace hipdecode {
+namespace {
+
+constexpr int kNoallocMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kNoallocMaxDevices];   // per device: the address of `scratch`, once looked up
+
+// The current device's scratch address; on the first call for a device the
+// counter region is zero-filled on `stream` (static storage starts at zero
+// as well; every completed call leaves its counters at zero again).
+hipdecode_status scratch_of_current_device(hipStream_t stream, void **ptr)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kNoallocMaxDevices)
+        return HIPDECODE_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return HIPDECODE_ERR_HIP;
+        if (launch_zero_fill(p, kNoallocCounterBytes, stream) != hipSuccess)
+            return HIPDECODE_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return HIPDECODE_OK;
+}
+
+}  // namespace
+}  // namespace hipdecode
+
+HIPDECODE_API hipdecode_status hipdecode_paged_attn_noalloc(const hipdecode_params *params, const void *q,
+                                                            const void *k_pool, const void *v_pool,
+                                                            const int32_t *block_table,
+                                                            const int32_t *context_lens, void *out, float *lse,
+                                                            void *stream)
+{
+    // every argument check happens before the scratch is looked up or cleared;
+    // a non-null stand-in passes the workspace pointer check
+    const hipdecode_status st = check_call(params, q, k_pool, v_pool, block_table, context_lens, out, lse,
+                                           reinterpret_cast<void *>(uintptr_t{256}), false, nullptr, nullptr, 0.0);
+    if (st != HIPDECODE_OK || params->num_seqs == 0)
+        return st;
+    if (counter_bytes(*params) > kNoallocCounterBytes ||
+        layout_with(*params, kNoallocCounterBytes).total > kNoallocBytes)
+        return HIPDECODE_ERR_WORKSPACE;
+    void *ws = nullptr;
+    const hipdecode_status sst = scratch_of_current_device(static_cast<hipStream_t>(stream), &ws);
+    if (sst != HIPDECODE_OK)
+        return sst;
+    return run_decode(params, q, k_pool, v_pool, block_table, context_lens, out, lse, ws, kNoallocBytes, stream,
+                      false, nullptr, nullptr, 0.0, true);
 }
 
 HIPDECODE_API const char *hipdecode_status_string(hipdecode_status status)

@@ -147,6 +147,32 @@ def test_call_rejects_before_any_launch():
         == hd.HIPDECODE_OK
 
 
+def test_noalloc_rejects_before_any_launch():
+    """The allocation-free entry point checks its arguments and its static
+    scratch's limits on the host, before it looks the scratch up."""
+    lib = hd.library()
+    fake = ctypes.c_void_p(1 << 20)          # never dereferenced: rejected on the host
+    odd = ctypes.c_void_p((1 << 20) + 2)
+    p = base()
+    assert lib.hipdecode_paged_attn_noalloc(ctypes.byref(p), None, *[fake] * 6, None) == hd.HIPDECODE_ERR_NULL
+    assert lib.hipdecode_paged_attn_noalloc(ctypes.byref(p), odd, *[fake] * 6, None) == hd.HIPDECODE_ERR_ALIGN
+    bad = base(head_dim=64)
+    assert lib.hipdecode_paged_attn_noalloc(ctypes.byref(bad), *[None] * 7, None) == hd.HIPDECODE_ERR_UNSUPPORTED
+    zero = base(num_seqs=0)
+    assert lib.hipdecode_paged_attn_noalloc(ctypes.byref(zero), *[None] * 7, None) == hd.HIPDECODE_OK
+    # more (request, KV head) pairs than the counter region holds
+    many = base(num_seqs=513, max_context_len=16)
+    assert lib.hipdecode_paged_attn_noalloc(ctypes.byref(many), *[fake] * 7, None) == hd.HIPDECODE_ERR_WORKSPACE
+    # partials past the array (64 requests split 1024 ways), though a caller workspace could hold them
+    split = base(num_seqs=64, max_blocks_per_seq=4096, max_context_len=65536, partition_tokens=64)
+    assert hd.hipdecode_workspace_bytes(split) > hd.HIPDECODE_NOALLOC_SCRATCH_BYTES
+    assert lib.hipdecode_paged_attn_noalloc(ctypes.byref(split), *[fake] * 7, None) == hd.HIPDECODE_ERR_WORKSPACE
+    # the named long-context batches fit: 16 x 28,672 and 32 up to 67,500 tokens
+    assert hd.hipdecode_workspace_bytes(base()) < hd.HIPDECODE_NOALLOC_SCRATCH_BYTES - (1 << 20)
+    mix = base(num_seqs=32, max_blocks_per_seq=4219, max_context_len=67500)
+    assert hd.hipdecode_workspace_bytes(mix) < hd.HIPDECODE_NOALLOC_SCRATCH_BYTES - (1 << 20)
+
+
 def test_planner_wave_choice():
     # 4-wave workgroups unless 16 are asked for
     assert hd.hipdecode_workgroup_waves(base()) == 4
