@@ -253,9 +253,10 @@ hipdecode_status hipdecode_kv_append(const hipdecode_append_params *params,
  * G = num_q_heads / num_kv_heads in {1, 2, 4}.  No workspace; asynchronous on
  * `stream`, graph-capturable.
  *
- * The matrix cores take softmax weights in bf16 (relative rounding 2^-9),
- * so the output carries an absolute error of up to about 2^-9 times the
- * largest |V| a row attends to; scores, the running sums and lse are fp32.
+ * Scores, softmax weights, the running sums and lse are fp32.  The matrix
+ * cores take each weight as the sum of two bf16 parts (within 2^-16 of it,
+ * relative), so the weighted mean of V is off by at most about 2^-16 times
+ * the largest |V| a row attends to, before the output's own rounding.
  *
  * Device-side contract as for the append: new_start non-decreasing, n_b <=
  * min(c_b, max_new_tokens), rows within num_rows, c_b <= 16 *

@@ -25,9 +25,9 @@
 // (global_load_lds, two steps ahead), both K and V row-major, and used in two
 // halves of 32.
 //
-// Per step and wavefront, with v_mfma_f32_32x32x16_bf16 (A 32x16, B 16x32):
+// Per 32-key half and wavefront, with v_mfma_f32_32x32x16_bf16 (A 32x16, B 16x32):
 //   S^T[key][row]  = sum_d K[key][d] Q[row][d]        8 MFMAs, A = K, B = Q^T
-//   O^T[dim][row] += sum_key V[key][dim] P[row][key]  8 MFMAs, A = V^T, B = P^T
+//   O^T[dim][row] += sum_key V[key][dim] P[row][key]  16 MFMAs, A = V^T, B = P^T (hi, then lo)
 // Lane l of the S^T accumulator holds row l % 32 and keys
 // 8(r/4) + 4(l/32) + r%4 for registers r = 0..15, which is exactly how the
 // B operand of the second product wants P^T, provided both products agree
@@ -36,8 +36,10 @@
 // online, in base 2 with scale*log2(e) folded in (one FMA and one v_exp_f32
 // per score), against a running maximum that moves only when the weights
 // grow large; the two lanes (l, l ^ 32) that share a row combine their
-// maxima and sums with v_permlane32_swap.  P is rounded to bf16 for the
-// matrix cores; the running sum uses the fp32 values.
+// maxima and sums with v_permlane32_swap.  The matrix cores take each fp32
+// weight as two bf16 parts, hi and lo (two P.V products into the same
+// accumulators), so the weights they apply agree with the fp32 ones that the
+// running sum adds up to 2^-16 relative.
 #include "hipdecode.h"
 #include "internal.h"
 
@@ -382,10 +384,18 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
             }
         }
         l_run += psum;
-        uint32_t pp[8];
+        // Each weight goes to the matrix cores as two bf16 parts, hi = the
+        // nearest bf16 and lo = the nearest bf16 of the remainder (exact in
+        // fp32), so hi + lo is within 2^-16 of it (relative) and the weights
+        // in P.V agree with the fp32 ones in l_run.
+        uint32_t pp[8], pl[8];
 #pragma unroll
-        for (int r = 0; r < 16; r += 2)
+        for (int r = 0; r < 16; r += 2) {
             pp[r / 2] = pack2_bf16(pw[r], pw[r + 1]);
+            const float h0 = __uint_as_float(pp[r / 2] << 16);
+            const float h1 = __uint_as_float(pp[r / 2] & 0xFFFF0000u);
+            pl[r / 2] = pack2_bf16(pw[r] - h0, pw[r + 1] - h1);
+        }
 
         // O^T += V^T P^T, two k-steps of 16 keys.  P^T: lane l holds keys
         // 16 kh + 4 half + e and 16 kh + 8 + 4 half + e (e < 4) of this half,
@@ -404,12 +414,16 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
-            const uint4 u = make_uint4(pp[4 * kh], pp[4 * kh + 1], pp[4 * kh + 2], pp[4 * kh + 3]);
-            const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, u);
+            const bf16x8_t phi = __builtin_bit_cast(
+                bf16x8_t, make_uint4(pp[4 * kh], pp[4 * kh + 1], pp[4 * kh + 2], pp[4 * kh + 3]));
+            const bf16x8_t plo = __builtin_bit_cast(
+                bf16x8_t, make_uint4(pl[4 * kh], pl[4 * kh + 1], pl[4 * kh + 2], pl[4 * kh + 3]));
 #pragma unroll
-            for (int db = 0; db < kDimBlocks; ++db)
-                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vv[kh][db]), pop,
-                                                                  acc[db], 0, 0, 0);
+            for (int db = 0; db < kDimBlocks; ++db) {
+                const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, vv[kh][db]);
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, plo, acc[db], 0, 0, 0);
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, phi, acc[db], 0, 0, 0);
+            }
         }
     };
     // Both halves' scores are issued first: the matrix cores work on the

@@ -1,21 +1,22 @@
 """GPU parity of chunked-prefill attention against the fp64 oracle, through the
 C ABI.
 
-Tolerances, derived from the arithmetic (the decode bar of 1e-2 assumes fp32
-softmax weights, which the matrix cores do not take).  Each weight enters the
-P.V product rounded to bf16: 8 significant bits, a relative error of at most
-u = 2^-8.  So |sum p~ v / l - sum p v / l| <= u max|V|, and a bf16 output
-adds its own rounding, at most u |out|.  Per element:
+The bar is the decode one: |out - oracle| <= 1e-2, and |lse - oracle| <=
+1e-4 * max(1, |oracle|).  On bf16 outputs 1e-2 is within reach of a
+correctly rounded result only below 4 in magnitude (half the bf16 spacing is
+at most 2^-7 there, 2^-5 from 4 to 8), so it binds every element with
+|oracle| < 4; every element, those above 4 included, must also meet a
+rounding-level bound derived from the kernel's arithmetic.  The matrix
+cores take every softmax weight p as two bf16 parts, hi (nearest bf16 of p)
+and lo (nearest bf16 of p - hi), so |hi + lo - p| <= 2^-16 p; the running sum
+l is the fp32 sum of the weights themselves.  The weighted mean of V is
+therefore off by at most 2^-16 * max|V| (under 1e-4 for every pool here, all
+|V| < 6.5), and a bf16 output adds its own rounding, at most 2^-8 |out|:
 
-    |out - oracle| <= u (1 + u) Vmax + u |oracle| (bf16 out only) + 1e-5
+    |out - oracle| <= 2^-8 |oracle| (bf16 out) + 2^-16 Vmax + 2e-5
 
-with Vmax the largest |V| in the pool.  With N(0,1) values Vmax is about 5,
-so the bound is about 2e-2, plus the output's share.  Spread-out attention
-stays near 1e-2 (the weights' roundings partly cancel); where one key
-dominates, the error approaches u (Vmax + |out|).  The scores,
-running sums and lse stay in fp32: |lse - oracle| <= 1e-4 * max(1, |oracle|).
-The tests also report the mean error.  Rows that no request names must be
-left exactly as they were.
+with 2e-5 for the fp32 scores, sums and accumulation.  Rows that no request
+names must be left exactly as they were.
 """
 from __future__ import annotations
 
@@ -34,6 +35,9 @@ from workloads import (bf16_bits_to_f32, f32_to_bf16_bits, make_append_inputs, m
 pytestmark = pytest.mark.gpu
 
 BF16_EPS = 2.0 ** -8      # unit roundoff of bf16 (8 significant bits, nearest even)
+SPLIT_EPS = 2.0 ** -16    # relative error of a weight given as hi + lo bf16 parts
+OUT_ATOL = 1e-2           # max |out - oracle|, as for decode
+BF16_REACH = 4.0          # below this magnitude a correctly rounded bf16 is within 2^-7 of any value
 LSE_RTOL = 1e-4
 SENTINEL = 7.0
 
@@ -65,19 +69,24 @@ def v_max(v_pool):
     return float(np.nanmax(np.abs(bf16_bits_to_f32(v_pool))))
 
 
-def out_bound(ref_o, vmax, bf16_out=True):
-    return BF16_EPS * (1 + BF16_EPS) * vmax + (BF16_EPS * np.abs(ref_o) if bf16_out else 0.0) + 1e-5
+def rounding_bound(ref_o, vmax, bf16_out=True):
+    return (BF16_EPS * np.abs(ref_o) if bf16_out else 0.0) + SPLIT_EPS * vmax + 2e-5
 
 
 def check_rows(o, l, ref_o, ref_l, what, vmax, bf16_out=True):
     err = np.abs(o - ref_o)
     assert np.all(np.isfinite(o)), f"{what}: non-finite output"
     max_err = float(err.max()) if err.size else 0.0
-    over = err - out_bound(ref_o, vmax, bf16_out)
-    assert not np.any(over > 0), f"{what}: max |out err| {max_err}, worst excess {float(over.max())}"
+    # 1e-2 binds where a bf16 result can meet it; fp32 outputs everywhere
+    bar = np.abs(ref_o) < BF16_REACH if bf16_out else np.ones(err.shape, dtype=bool)
+    max_bar = float(err[bar].max()) if bar.any() else 0.0
+    assert max_bar <= OUT_ATOL, f"{what}: max |out err| {max_bar} > {OUT_ATOL}"
+    over = err - rounding_bound(ref_o, vmax, bf16_out)
+    assert not np.any(over > 0), f"{what}: error above rounding level by {float(over.max())}"
     lerr = np.abs(l - ref_l) / np.maximum(1.0, np.abs(ref_l))
     assert np.all(lerr <= LSE_RTOL), f"{what}: lse err {float(lerr.max())}"
-    log(f"[prefill] {what}: max|dout|={max_err:.2e} mean|dout|={float(err.mean()):.2e} "
+    log(f"[prefill] {what}: max|dout|={max_err:.2e} (|oracle|<4: {max_bar:.2e}; {int((~bar).sum())} above) "
+        f"mean|dout|={float(err.mean()):.2e} max|out|={float(np.abs(ref_o).max()) if ref_o.size else 0.0:.2f} "
         f"max rel dlse={float(lerr.max()):.2e} (Vmax {vmax:.2f})")
     return max_err
 
@@ -135,9 +144,12 @@ def test_prefill_group_shapes(hq, hkv):
     check_full(case, inp, o, l, f"{hq}/{hkv}")
 
 
-def test_prefill_rising_scores():
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_prefill_rising_scores(out_dtype):
     # Keys grow with their position, so a row's maximum keeps rising past the
-    # running reference: the rescale path runs on many halves, not only the first.
+    # running reference: the rescale path runs on many halves, not only the
+    # first, and the last few keys carry most of the weight (outputs reach
+    # past 4 in magnitude).
     ctx, new = [3000, 700], [512, 700]
     case, inp = make_prefill_case(ctx, new, seed=45)
     k = bf16_bits_to_f32(case.k_pool).astype(np.float32)
@@ -146,8 +158,43 @@ def test_prefill_rising_scores():
             page, slot = case.block_table[b, t // 16], t % 16
             k[page, slot] *= np.float32(1.0 + 7.0 * (t / n) ** 2)
     case = replace(case, k_pool=f32_to_bf16_bits(k))
+    o, l = run_gpu(case, inp, out_dtype=out_dtype)
+    f32 = out_dtype == torch.float32
+    check_full(case, inp, o, l, "rising scores" + (", fp32 out" if f32 else ""), bf16_out=not f32)
+
+
+def test_prefill_dominant_key():
+    """One key per request takes about 88% of the weight of every row of one
+    query head per KV head, and its V holds values of 2.5 to 3.9 in
+    magnitude, so those rows' outputs sit in [2, 4), where bf16 rounding alone
+    is up to 7.8e-3: the weights' own error must stay far below the rest of the
+    1e-2 bar.  The key sits past the first 64, so the running reference is not
+    its own score and its weight is not exactly 1."""
+    ctx, new = [3000, 1500], [256, 128]
+    case, inp = make_prefill_case(ctx, new, seed=48)
+    rng = np.random.default_rng(480)
+    G = case.Hq // case.Hkv
+    q = bf16_bits_to_f32(inp.q).astype(np.float32)
+    k = bf16_bits_to_f32(case.k_pool).astype(np.float32)
+    v = bf16_bits_to_f32(case.v_pool).astype(np.float32)
+    j = 100
+    for b, c in enumerate(ctx):
+        r0, r1 = int(inp.new_start[b]), int(inp.new_start[b + 1])
+        q[r0:r1] = q[r0]                      # every chunk row asks the same question
+        page, slot = case.block_table[b, j // 16], j % 16
+        target = np.log(1.65 * c) + 2.0       # E exp(z) = e^0.5 for the N(0,1) scores of the other keys
+        for g in range(case.Hkv):
+            qh = q[r0, g * G].astype(np.float64)
+            k[page, slot, g] = (qh * (target / (case.scale * np.dot(qh, qh)))).astype(np.float32)
+            v[page, slot, g] = (rng.uniform(2.5, 3.9, case.D) * rng.choice([-1.0, 1.0], case.D)).astype(np.float32)
+    case = replace(case, k_pool=f32_to_bf16_bits(k), v_pool=f32_to_bf16_bits(v))
+    inp = replace(inp, q=f32_to_bf16_bits(q))
     o, l = run_gpu(case, inp)
-    check_full(case, inp, o, l, "rising scores")
+    check_full(case, inp, o, l, "dominant key")
+    ref_o, _ = oracle.prefill_attn(inp.q, case.k_pool, case.v_pool, case.block_table, case.context_lens,
+                                   inp.new_start, case.scale)
+    big = np.abs(ref_o) >= 2.0
+    assert big.sum() > 1000, "the dominated rows must put outputs in [2, 4)"
 
 
 def test_prefill_fp32_out():
@@ -156,26 +203,15 @@ def test_prefill_fp32_out():
     check_full(case, inp, o, l, "fp32 out", bf16_out=False)
 
 
-def sampled_pairs(inp, Hq, rng, extra=48):
-    T = inp.rows
-    rows = [0, 1, 31, 32, 63, 64, 127, 128, T // 2, T - 2, T - 1]
-    pairs = [(r, h) for r in rows for h in (0, 1, Hq // 2, Hq - 1)]
-    pairs += [(int(rng.integers(T)), int(rng.integers(Hq))) for _ in range(extra)]
-    return pairs
-
-
-@pytest.mark.parametrize("name", ["p1", "p2"])
-def test_prefill_named_workloads_sampled(name):
+@pytest.mark.parametrize("name", ["p2", "p1"])
+def test_prefill_named_workloads_full(name):
+    """Every (row, query head) of the named 4,096-token chunks against the
+    oracle: p1 (the last chunk of a 28,672-token prompt) and p2 (the first)."""
     case, inp = make_prefill_config(name)
     log(f"[prefill] {name}: {case.name} rows={inp.rows}")
     o, l = run_gpu(case, inp)
-    pairs = sampled_pairs(inp, case.Hq, np.random.default_rng(44))
-    ref_o, ref_l = oracle.prefill_attn_pairs(inp.q, case.k_pool, case.v_pool, case.block_table,
-                                             case.context_lens, inp.new_start, case.scale, pairs)
-    idx = np.array(pairs)
-    check_rows(o[idx[:, 0], idx[:, 1]], l[idx[:, 0], idx[:, 1]], ref_o, ref_l, f"{name} sampled",
-               v_max(case.v_pool))
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(l)), f"{name}: non-finite rows"
+    check_full(case, inp, o, l, f"{name} every row")
 
 
 def test_prefill_last_rows_match_decode_kernel():
@@ -189,8 +225,8 @@ def test_prefill_last_rows_match_decode_kernel():
     d_out, d_lse = run_hip(dc)
     d_o = d_out.float().cpu().numpy()
     d_l = d_lse.cpu().numpy()
-    # prefill's bound plus the decode kernel's rounding-level one (fp32 weights, bf16 out)
-    assert np.all(np.abs(o[last] - d_o) <= out_bound(d_o, v_max(case.v_pool)) + 2.0 ** -8 * np.abs(d_o) + 2e-5)
+    # both rounding-level bounds: prefill's and the decode kernel's (fp32 weights, bf16 out)
+    assert np.all(np.abs(o[last] - d_o) <= rounding_bound(d_o, v_max(case.v_pool)) + 2.0 ** -8 * np.abs(d_o) + 2e-5)
     assert np.all(np.abs(l[last] - d_l) <= 2 * LSE_RTOL * np.maximum(1.0, np.abs(d_l)))
 
 
@@ -240,7 +276,7 @@ def test_chunked_prefill_pipeline_with_append():
 def test_prefill_graph_replays():
     """A captured prefill call replayed three times, with eager work and a
     changed query in between: each replay equals an eager call on the same
-    inputs bit for bit, and the oracle to the derived bound."""
+    inputs bit for bit, and the oracle at the prefill bars."""
     case, inp = make_prefill_case([2500, 700, 64], [600, 700, 64], seed=47)
     dc = DeviceCase(case)
     T = inp.rows
