@@ -19,6 +19,9 @@ roofline.achieved = algorithmic bytes per call / average call duration,
           timed with HIP events on the stream the kernel runs on.
 cpu_baseline = the fp64 oracle, unmodified, on this host's cores, over one
           layer's worth of (request, head) pairs, scaled to tokens/s.
+configs = the default run (c4, 16 x 28,672 tokens) also times c3 (1 x 28,672),
+          c3b (1 x 65,536) and c5 (32 mixed lengths up to 67,500) the same
+          way, so that one line covers the metric's 28k-64k range.
 
 ``--op append`` measures the KV-cache append instead (``hipdecode_kv_append``
 with RoPE on K and q): a step is 28 calls, one per layer, each writing the new
@@ -62,9 +65,10 @@ DECODE_SOURCES = ["paged_kv_decode_gqa_amd/csrc/paged_decode.hip",
 APPEND_SOURCES = ["paged_kv_decode_gqa_amd/csrc/kv_append.hip",
                   "paged_kv_decode_gqa_amd/csrc/internal.h"]
 PREFILL_SOURCES = ["paged_kv_decode_gqa_amd/csrc/prefill_attn.hip", "paged_kv_decode_gqa_amd/csrc/internal.h"]
-KERNEL_NAMES = {"split": "paged_decode_kernel", "stream": "paged_decode_stream_kernel"}
-KERNEL_SOURCES = {"paged_decode_kernel": DECODE_SOURCES, "paged_decode_stream_kernel": DECODE_SOURCES,
+KERNEL_NAMES = {"split": "paged_decode_kernel"}
+KERNEL_SOURCES = {"paged_decode_kernel": DECODE_SOURCES,
                   "kv_append_kernel": APPEND_SOURCES, "prefill_attn_kernel": PREFILL_SOURCES}
+DECODE_WORKLOADS = ("c1", "c2", "c3", "c4", "c5", "c3b")
 APPEND_METRIC = "kv-cache append new tokens/s (RoPE on K and q) and achieved HBM GB/s"
 PREFILL_METRIC = "chunked-prefill attention tokens/s and achieved bf16 TFLOP/s"
 PEAK_BF16_TFLOPS = 2500.0
@@ -191,7 +195,7 @@ def main(argv=None) -> int:
                          "N(0,1) bf16) instead of a named workload; for sweeps of the per-call fixed cost")
     ap.add_argument("--partition", type=int, default=0, help="split-K partition tokens (0 = planner)")
     ap.add_argument("--waves", type=int, default=0, help="wavefronts per workgroup, 4 or 16 (0 = planner)")
-    ap.add_argument("--schedule", type=int, default=0, help="1 = split, 2 = stream (0 = planner)")
+    ap.add_argument("--schedule", type=int, default=0, help="1 = split (0 = planner; split is the only one)")
     ap.add_argument("--rotate", type=int, default=0, help="distinct KV pool copies (0 = auto)")
     ap.add_argument("--v-offset", type=int, default=None, metavar="BYTES",
                     help="decode: place each V pool BYTES after the end of its K pool in one allocation "
@@ -200,6 +204,9 @@ def main(argv=None) -> int:
                     help="replay one captured HIP graph per step (the default: the decode step of the "
                          "MOSS-TD article runs from captured graphs)")
     ap.add_argument("--eager", dest="graph", action="store_false", help="issue the 28 launches of a step eagerly")
+    ap.add_argument("--configs", default="c3,c3b,c5",
+                    help="decode, default workload only: further workloads timed the same way after c4 and "
+                         "reported under \"configs\" (comma-separated; \"none\" to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for the traffic counters)")
@@ -246,6 +253,7 @@ def main(argv=None) -> int:
         return run_prefill(args, dev)
     if args.op == "step":
         return run_step(args, dev)
+    named = False
     if args.context > 0:
         from workloads import make_case
         t0 = time.time()
@@ -253,13 +261,105 @@ def main(argv=None) -> int:
         case = make_case([args.context], seed=3, name=args.workload)
         t_gen = time.time() - t0
     else:
+        named = args.workload is not None
         args.workload = args.workload or "c4"
-        if args.workload not in ("c1", "c2", "c3", "c4", "c5", "c3b"):
+        if args.workload not in DECODE_WORKLOADS:
             print(f"unknown decode workload {args.workload}", file=sys.stderr)
             return 2
         t0 = time.time()
         case = make_config(args.workload)
         t_gen = time.time() - t0
+    m = measure_decode(case, args.workload, args, dev)
+    out, m = m.pop("_out"), m
+    result = {
+        "metric": METRIC,
+        "value": m["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": m["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 KV pages, shuffled pools; no dataset)",
+        "config": m["config"],
+        "us_per_layer": m["us_per_layer"],
+        "us_per_layer_p10_p50_p90": m["us_per_layer_p10_p50_p90"],
+        "kv_tokens_per_s": m["kv_tokens_per_s"],
+        "wall_s_timed": m["wall_s_timed"],
+        "roofline": m["roofline"],
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        import oracle
+        o_gpu = out.float().cpu().numpy().astype(np.float64)
+        reps, t_cpu = 0, 0.0
+        ref_out = None
+        while reps < 50 and (t_cpu < 10.0 or reps == 0):
+            c0 = time.perf_counter()
+            ref_out, _ = oracle.run_case(case)
+            t_cpu += time.perf_counter() - c0
+            reps += 1
+        t_layer = t_cpu / reps
+        result["cpu_baseline"] = {
+            "value": round(case.B / (LAYERS * t_layer), 4),
+            "unit": "tokens/s",
+            "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "cpu_model": host_cpu_model(),
+            "sample": f"fp64 oracle over all {case.B * case.Hq} (request, head) pairs of one layer call, "
+                      f"{reps} run(s), {t_layer:.3f} s per layer, scaled to {LAYERS} layers per token",
+            "parity_max_abs_err": float(np.abs(o_gpu - ref_out).max()),
+        }
+    del out, case
+    torch.cuda.empty_cache()
+
+    # the rest of the metric's 28k-64k range, each timed the same way
+    extra = [] if args.context > 0 or named or args.configs == "none" else \
+        [w for w in args.configs.split(",") if w and w != args.workload]
+    if extra:
+        result["configs"] = {}
+    for w in extra:
+        if w not in DECODE_WORKLOADS:
+            print(f"unknown decode workload {w}", file=sys.stderr)
+            return 2
+        c = make_config(w)
+        mw = measure_decode(c, w, args, dev)
+        mw.pop("_out")
+        r = mw["roofline"]
+        result["configs"][w] = {
+            "workload": c.name,
+            "batch": c.B,
+            "max_context": c.max_context_len,
+            "tokens_per_s": mw["tokens_per_s"],
+            "us_per_layer": mw["us_per_layer"],
+            "us_per_layer_p10_p50_p90": mw["us_per_layer_p10_p50_p90"],
+            "achieved_GBps": r["achieved"],
+            "frac": r["frac"],
+            "traffic": r["traffic"],
+            "algorithmic_bytes_per_launch": r["algorithmic_bytes_per_launch"],
+            "partition_tokens": mw["config"]["partition_tokens"],
+            "kv_pool_copies": mw["config"]["kv_pool_copies"],
+        }
+        del c, mw
+        torch.cuda.empty_cache()
+    result["setup_s"] = round(t_gen, 2)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def measure_decode(case, workload: str, args, dev) -> dict:
+    """Time `case` as bench's decode step does (28 calls per step over rotated
+    pool copies, graph replay unless --eager) and return the figures; the
+    last call's output tensor is under "_out"."""
+    import numpy as np
+    import torch
+
+    import paged_kv_decode_gqa_amd as hd
+
     out_dtype = torch.float32 if case.out_dtype == "f32" else torch.bfloat16
     out_bytes = 4 if case.out_dtype == "f32" else 2
     alg_bytes = algorithmic_bytes(case, out_bytes)
@@ -268,7 +368,6 @@ def main(argv=None) -> int:
     def bf(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    pool_bytes = 2 * case.k_pool.nbytes
     R = args.rotate or max(2, min(LAYERS, math.ceil(ROTATE_MIN_BYTES / max(1, kv_bytes_call))))
     q = bf(case.q)
     k0, v0 = bf(case.k_pool), bf(case.v_pool)
@@ -290,7 +389,7 @@ def main(argv=None) -> int:
         raise hd.HipDecodeError(st, "params")
     part = hd.hipdecode_partition_tokens(params)
     waves = hd.hipdecode_workgroup_waves(params)
-    schedule = {1: "split", 2: "stream"}[hd.hipdecode_schedule(params)]
+    schedule = {1: "split"}[hd.hipdecode_schedule(params)]
     ws = torch.zeros(hd.hipdecode_workspace_bytes(params) // 4 + 4, dtype=torch.int32, device=dev)
     out = torch.empty((case.B, case.Hq, case.D), dtype=out_dtype, device=dev)
     lse = torch.empty((case.B, case.Hq), dtype=torch.float32, device=dev)
@@ -329,26 +428,14 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms = ev0.elapsed_time(ev1)
-    n_calls = args.steps * LAYERS
-    call_s = ms * 1e-3 / n_calls
-    value = case.B * args.steps / (ms * 1e-3)
+    call_s = ms * 1e-3 / (args.steps * LAYERS)
     achieved = alg_bytes / call_s / 1e9
     spread = per_step_spread(run, stream, args.steps)
-
-    # parity of the last call against the oracle, and the oracle's own speed
-    result = {
-        "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+    kernel = KERNEL_NAMES[schedule]
+    traffic = read_traffic(kernel, workload)
+    m = {
+        "tokens_per_s": round(case.B * args.steps / (ms * 1e-3), 2),
         "ms_per_step": round(ms / args.steps, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) bf16 KV pages, shuffled pools; no dataset)",
         "config": {
             "workload": case.name,
             "batch": case.B,
@@ -373,45 +460,19 @@ def main(argv=None) -> int:
         "wall_s_timed": round(wall, 4),
         "roofline": {
             "bound": "hbm",
-            "kernel": KERNEL_NAMES[schedule],
+            "kernel": kernel,
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": None,
+            "traffic": None if traffic is None else round(traffic),
             "algorithmic_bytes_per_launch": alg_bytes,
             "avg_launch_us": round(call_s * 1e6, 3),
         },
-        "cpu_baseline": None,
+        "_out": out,
     }
-    traffic = read_traffic(KERNEL_NAMES[schedule], args.workload)
-    if traffic is not None:
-        result["roofline"]["traffic"] = round(traffic)
-
-    if not args.no_cpu_baseline:
-        import oracle
-        o_gpu = out.float().cpu().numpy().astype(np.float64)
-        reps, t_cpu = 0, 0.0
-        ref_out = None
-        while reps < 50 and (t_cpu < 10.0 or reps == 0):
-            c0 = time.perf_counter()
-            ref_out, _ = oracle.run_case(case)
-            t_cpu += time.perf_counter() - c0
-            reps += 1
-        t_layer = t_cpu / reps
-        result["cpu_baseline"] = {
-            "value": round(case.B / (LAYERS * t_layer), 4),
-            "unit": "tokens/s",
-            "cores": oracle.max_threads(),
-            "kind": "oracle",
-            "cpu_model": host_cpu_model(),
-            "sample": f"fp64 oracle over all {case.B * case.Hq} (request, head) pairs of one layer call, "
-                      f"{reps} run(s), {t_layer:.3f} s per layer, scaled to {LAYERS} layers per token",
-            "parity_max_abs_err": float(np.abs(o_gpu - ref_out).max()),
-        }
-    result["setup_s"] = round(t_gen, 2)
-    print(json.dumps(result), flush=True)
-    return 0
+    del graph, calls, pools, q, table, ctx, ws, lse
+    return m
 
 
 def run_append(args, dev) -> int:

@@ -98,7 +98,7 @@ typedef struct {
     int32_t max_context_len;       /* host upper bound of context_lens[]; sizes the grid */
     int32_t partition_tokens;      /* split-K partition: 0 = planner's choice, else a multiple of 64 */
     int32_t workgroup_waves;       /* wavefronts per workgroup: 0 = planner's choice, else 4 or 16 */
-    int32_t schedule;              /* 0 = planner's choice, 1 = split by partition, 2 = stream */
+    int32_t schedule;              /* 0 = planner's choice, 1 = split by partition (the only one) */
     int32_t out_dtype;             /* hipdecode_dtype */
     float scale;                   /* applied to q.k, e.g. 1/sqrt(128) */
 } hipdecode_params;
@@ -120,11 +120,11 @@ int32_t hipdecode_partition_tokens(const hipdecode_params *params);
  * invalid.  Pure host function. */
 int32_t hipdecode_workgroup_waves(const hipdecode_params *params);
 
-/* Work schedule that a call with these parameters uses (1 = split by
- * partition, 2 = stream); 0 if the parameters are invalid.  Pure host
- * function.  split: one workgroup per (request, KV head, partition).
- * stream: a fixed grid of equal slices of all (request, KV head, page) work,
- * for batches whose context lengths differ widely (at most 1024 requests). */
+/* Work schedule that a call with these parameters uses: 1 = split, one
+ * workgroup per (request, KV head, partition), the grid mapped onto the
+ * real (request, partition) units of a ragged batch inside the kernel; 0 if
+ * the parameters are invalid (any schedule but 0 and 1 is).  Pure host
+ * function. */
 int32_t hipdecode_schedule(const hipdecode_params *params);
 
 /* Bytes of workspace a call with these parameters needs; 0 if they are
@@ -384,9 +384,8 @@ hipdecode_status hipdecode_step_runner_destroy(hipdecode_step_runner *runner);
  * workgroup that folds a request's last page takes the new token's K and V
  * from k_new/v_new [num_seqs][num_kv_heads][128] (bf16, 16-byte aligned),
  * writes them to their slot and folds them from registers; every workgroup
- * rotates its query heads itself.  Split schedule only (schedule 0 or 1):
- * a stream schedule gives HIPDECODE_ERR_UNSUPPORTED; a rope_theta that is
- * negative or not finite gives HIPDECODE_ERR_SCALE.  Same buffers, workspace
+ * rotates its query heads itself.  A rope_theta that is negative or not
+ * finite gives HIPDECODE_ERR_SCALE.  Same buffers, workspace
  * and contract as hipdecode_paged_attn otherwise; the pools are written.  A
  * request whose context_lens[b] exceeds max_context_len (a broken contract)
  * writes nothing to the pools, as hipdecode_kv_append would not; its out and

@@ -26,7 +26,6 @@ HIPDECODE_ERR_HIP = 7
 HIPDECODE_BF16 = 0
 HIPDECODE_F32 = 1
 HIPDECODE_SCHEDULE_SPLIT = 1
-HIPDECODE_SCHEDULE_STREAM = 2
 HIPDECODE_ROPE_NONE = 0
 HIPDECODE_ROPE_HALF = 1
 

@@ -28,21 +28,12 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// The split schedule is the default.  On MI355X it measured 290 vs 309 us
-// against the stream schedule for 16 equal 28672-token requests and within
-// 1% of it for the ragged 32-request mix; stream runs when asked for.
-int32_t plan_schedule(const hipdecode_params &p)
-{
-    return p.schedule > 0 ? p.schedule : kScheduleSplit;
-}
+// One schedule: split by partition (a ragged batch maps the grid onto its
+// real (request, partition) units inside the kernel).
+int32_t plan_schedule(const hipdecode_params &) { return kScheduleSplit; }
 
-// 4-wave workgroups unless 16 are asked for (the stream kernel is 4-wave only).
-int32_t plan_waves(const hipdecode_params &p)
-{
-    if (plan_schedule(p) == kScheduleStream)
-        return 4;
-    return p.workgroup_waves > 0 ? p.workgroup_waves : 4;
-}
+// 4-wave workgroups unless 16 are asked for.
+int32_t plan_waves(const hipdecode_params &p) { return p.workgroup_waves > 0 ? p.workgroup_waves : 4; }
 
 // Partition size, in multiples of 64 tokens, at most 4096 and at most
 // kMaxMergeSplits partials per request.  Short contexts of many requests are
@@ -75,13 +66,6 @@ int32_t plan_partition(const hipdecode_params &p)
     return (int32_t)part;
 }
 
-// Resident 4-wave workgroups of the stream kernel, which its register count
-// sets: 3 per CU for G <= 2, 2 for G = 4.
-int32_t stream_workgroups(const hipdecode_params &p)
-{
-    return (p.num_q_heads / p.num_kv_heads <= 2 ? 3 : 2) * 256;
-}
-
 int32_t nsplit_max_of(const hipdecode_params &p, int32_t part)
 {
     const int64_t n = ceil_div(p.max_context_len, part);
@@ -104,20 +88,13 @@ WorkspaceLayout layout_with(const hipdecode_params &p, size_t counter_region)
     // one 256-byte line per counter: the tickets of different KV heads never
     // meet on one line (measured 4% at the 32-request mix, 14% at 1 x 3.5k)
     w.part_ml = align256(counter_region);
-    size_t partials;
-    if (plan_schedule(p) == kScheduleStream) {
-        // two per tile; tiles <= W + B * Hkv (a tile is a full block, or a request's last)
-        partials = (size_t)2 * ((size_t)stream_workgroups(p) + (size_t)p.num_seqs * p.num_kv_heads) *
-                   (size_t)(p.num_q_heads / p.num_kv_heads);
-    } else {
-        const int32_t nsplit = nsplit_max_of(p, plan_partition(p));
-        if (nsplit <= 1) {
-            w.part_acc = w.part_ml;
-            w.total = w.part_ml;   // a single partition per request needs only the counters
-            return w;
-        }
-        partials = (size_t)p.num_seqs * (size_t)p.num_q_heads * (size_t)nsplit;
+    const int32_t nsplit = nsplit_max_of(p, plan_partition(p));
+    if (nsplit <= 1) {
+        w.part_acc = w.part_ml;
+        w.total = w.part_ml;   // a single partition per request needs only the counters
+        return w;
     }
+    const size_t partials = (size_t)p.num_seqs * (size_t)p.num_q_heads * (size_t)nsplit;
     w.part_acc = w.part_ml + align256(partials * 2 * sizeof(float));
     w.total = w.part_acc + partials * kHeadDim * sizeof(float);
     return w;
@@ -157,31 +134,18 @@ hipdecode_status check(const hipdecode_params *pp)
         return HIPDECODE_ERR_UNSUPPORTED;
     if (p.workgroup_waves == 16 && group > 2)
         return HIPDECODE_ERR_UNSUPPORTED;
-    if (p.schedule < 0 || p.schedule > kScheduleStream)
-        return HIPDECODE_ERR_UNSUPPORTED;
-    if (p.schedule == kScheduleStream &&
-        (p.num_seqs > kMaxStreamSeqs || p.workgroup_waves == 16 ||
-         // a (request, KV head) merges two partials per block, at most W/Hkv + 1 blocks
-         2 * (stream_workgroups(p) / p.num_kv_heads + 1) > kMaxMergeSplits))
+    if (p.schedule < 0 || p.schedule > kScheduleSplit)
         return HIPDECODE_ERR_UNSUPPORTED;
     // index arithmetic inside the kernel: rows of q/out and the grid stay in 31 bits
     const int64_t rows = (int64_t)p.num_seqs * p.num_q_heads;
     if (rows * kHeadDim > INT32_MAX)
         return HIPDECODE_ERR_SHAPE;
-    if (plan_schedule(p) == kScheduleStream) {
-        // flattened (request, KV head, page) units stay in 31 bits
-        const int64_t units = (int64_t)p.num_seqs * p.num_kv_heads * ceil_div(p.max_context_len, kPageSize);
-        if (units > INT32_MAX)
-            return HIPDECODE_ERR_SHAPE;
-    }
-    if (plan_schedule(p) == kScheduleSplit) {
-        const int32_t nsplit = nsplit_max_of(p, plan_partition(p));
-        if (nsplit > kMaxMergeSplits)
-            return HIPDECODE_ERR_SHAPE;
-        const int64_t grid = (int64_t)p.num_seqs * p.num_kv_heads * nsplit;
-        if (grid > INT32_MAX)
-            return HIPDECODE_ERR_SHAPE;
-    }
+    const int32_t nsplit = nsplit_max_of(p, plan_partition(p));
+    if (nsplit > kMaxMergeSplits)
+        return HIPDECODE_ERR_SHAPE;
+    const int64_t grid = (int64_t)p.num_seqs * p.num_kv_heads * nsplit;
+    if (grid > INT32_MAX)
+        return HIPDECODE_ERR_SHAPE;
     return HIPDECODE_OK;
 }
 
@@ -250,12 +214,8 @@ hipdecode_status check_call(const hipdecode_params *params, const void *q, const
     if (st != HIPDECODE_OK)
         return st;
     const hipdecode_params &p = *params;
-    if (fused) {
-        if (plan_schedule(p) != kScheduleSplit)
-            return HIPDECODE_ERR_UNSUPPORTED;
-        if (!(rope_theta >= 0.0) || !isfinite(rope_theta))
-            return HIPDECODE_ERR_SCALE;
-    }
+    if (fused && (!(rope_theta >= 0.0) || !isfinite(rope_theta)))
+        return HIPDECODE_ERR_SCALE;
     if (p.num_seqs == 0)
         return HIPDECODE_OK;
     if (q == nullptr || out == nullptr || context_lens == nullptr || block_table == nullptr ||
@@ -324,7 +284,6 @@ hipdecode_status run_decode(const hipdecode_params *params, const void *q, const
     a.max_context_len = p.max_context_len;
     a.partition_pages = part / kPageSize;
     a.nsplit_max = nsplit;
-    a.stream_workgroups = stream_workgroups(p);
     a.scale_log2 = p.scale * 1.44269504088896340736f;
     a.k_new = static_cast<const uint16_t *>(k_new);
     a.v_new = static_cast<const uint16_t *>(v_new);
@@ -332,7 +291,7 @@ hipdecode_status run_decode(const hipdecode_params *params, const void *q, const
     a.v_pool_w = fused ? static_cast<uint16_t *>(const_cast<void *>(v_pool)) : nullptr;
     a.rope_theta = fused ? rope_theta : 0.0;
 
-    const hipError_t e = launch_paged_decode(a, p.num_q_heads / p.num_kv_heads, plan_waves(p), plan_schedule(p),
+    const hipError_t e = launch_paged_decode(a, p.num_q_heads / p.num_kv_heads, plan_waves(p),
                                              p.out_dtype == HIPDECODE_F32, static_cast<hipStream_t>(stream), fused);
     return e == hipSuccess ? HIPDECODE_OK : HIPDECODE_ERR_HIP;
 }

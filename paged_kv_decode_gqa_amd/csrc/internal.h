@@ -15,13 +15,11 @@ constexpr int kPageSize = 16;   // tokens per page
 constexpr int kMinPartition = 64;     // split-K partitions are multiples of this many tokens
 constexpr int kMaxPartition = 4096;   // at most 256 pages, so at most 64 per wavefront: one table entry per lane
 constexpr int kMaxMergeSplits = 1024; // partitions per request the final merge can weigh in LDS
-constexpr int kMaxStreamSeqs = 1024;  // stream schedule: requests whose page counts fit the LDS prefix sum
 constexpr int kCounterStride = 64;   // int32 per arrival counter: each on its own 256-byte line
 constexpr int kScheduleSplit = 1;
-constexpr int kScheduleStream = 2;
 
 // Byte offsets inside the caller's workspace.  Partials are indexed
-// [B][Hq][nsplit] by the split schedule and [2W][G] by the stream schedule.
+// [B][Hq][nsplit].
 struct WorkspaceLayout {
     size_t counters;   // int32 [B][Hkv][kCounterStride]: arrivals per (request, KV head) in element 0; zero between calls
     size_t part_ml;    // fp32  [partials][2]: (running max, running sum) in log2 units
@@ -47,8 +45,7 @@ struct DecodeArgs {
     int32_t max_blocks;
     int32_t max_context_len;
     int32_t partition_pages;
-    int32_t nsplit_max;          // split schedule: partitions of the longest context
-    int32_t stream_workgroups;   // stream schedule: grid size
+    int32_t nsplit_max;          // partitions of the longest context
     float scale_log2;   // scale * log2(e): scores are kept in base-2 units
     // Fused append (hipdecode_paged_attn_append) only: each request's new
     // token, written to its slot and folded from registers, and RoPE.
@@ -59,10 +56,10 @@ struct DecodeArgs {
     double rope_theta;       // > 0: q and the new key are rotated at position ctx - 1
 };
 
-// waves: 4 or 16 wavefronts per workgroup (split schedule); schedule: kSchedule*;
-// fused: the split kernel that also appends each request's new token
-hipError_t launch_paged_decode(const DecodeArgs &a, int group, int waves, int schedule, bool out_f32,
-                               hipStream_t stream, bool fused = false);
+// waves: 4 or 16 wavefronts per workgroup; fused: the kernel that also
+// appends each request's new token
+hipError_t launch_paged_decode(const DecodeArgs &a, int group, int waves, bool out_f32, hipStream_t stream,
+                               bool fused = false);
 hipError_t launch_zero_fill(void *p, size_t bytes, hipStream_t stream);
 
 }  // namespace hipdecode

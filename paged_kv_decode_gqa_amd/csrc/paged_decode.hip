@@ -7,18 +7,11 @@
 // multiply-adds against 256 bytes of K and 256 bytes of V shared by the G
 // heads.  Page-level work is in page_fold.h.
 //
-// Two schedules share everything below the workgroup level.
-//
-//  * split: one workgroup per (request b, KV head g, partition of the
-//    context).  The grid is sized by the host's max_context_len.  In a
-//    ragged batch the workgroups map onto the real (request, partition)
-//    units in order, so the slots past the last one, not slots scattered
-//    through the grid, are the ones that exit at once.
-//  * stream: a fixed number W of workgroups (the resident count) take equal
-//    contiguous slices of the flattened (request, KV head, page) sequence,
-//    so a batch of very different context lengths still keeps every CU busy
-//    until the end.  Segment boundaries come from a prefix sum of the
-//    context lengths done in the kernel, so the grid does not depend on them.
+// One workgroup per (request b, KV head g, partition of the context).  The
+// grid is sized by the host's max_context_len.  In a ragged batch the
+// workgroups map onto the real (request, partition) units in order, so the
+// slots past the last one, not slots scattered through the grid, are the
+// ones that exit at once.
 //
 // Inside a workgroup the wavefronts take pages round-robin, each with one page
 // in flight while it folds the previous one; their streams are merged with
@@ -648,156 +641,6 @@ void paged_decode_kernel(DecodeArgs a)
                                       [&](int i, int h) { return (row0 + h) * nsm + i; }, ticket, ln);
 }
 
-// ---------------------------------------------------------------------------
-// stream schedule: W = gridDim.x workgroups take equal contiguous slices of
-// all work units, one unit being one page of one KV head of one request.  The
-// units are ordered request, then block j of S pages, then KV head, then page,
-// with S = ceil(total / W): a tile (request b, block j, KV head g) is at most
-// as long as a slice, so consecutive workgroups read the same pages of
-// neighbouring heads, and every tile is cut into at most two pieces.  Tile t
-// owns partial slots 2t (its first piece) and 2t+1 (its second piece, or an
-// empty partial when one workgroup holds the whole tile), so a (request, KV
-// head) with J blocks always merges exactly 2J partials.
-// ---------------------------------------------------------------------------
-// Slices of `total` units over W workgroups: the first `rem` slices hold
-// base + 1 units, the others base (base = total / W >= 1).
-struct Slices {
-    int base, rem;
-    __device__ __forceinline__ int start(int w) const { return w * base + min(w, rem); }
-};
-
-// Exclusive prefix sum by one wavefront of f(i), i < n, into out[0..n].
-template <class F>
-__device__ __forceinline__ void wave_prefix(int *out, int n, F f, int lane)
-{
-    int carry = 0;
-    for (int c0 = 0; c0 < n; c0 += 64) {
-        const int i = c0 + lane;
-        int v = i < n ? f(i) : 0;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int t = __shfl_up(v, o);
-            if (lane >= o)
-                v += t;
-        }
-        if (i < n)
-            out[i + 1] = carry + v;
-        carry += __shfl(v, 63);
-    }
-    if (lane == 0)
-        out[0] = 0;
-}
-
-template <int G, bool OUT_F32>
-__global__ __launch_bounds__(256) void paged_decode_stream_kernel(DecodeArgs a)
-{
-    constexpr int WAVES = 4;
-    __shared__ Smem<G, WAVES> sm;
-    __shared__ int s_pages[kMaxStreamSeqs + 1];    // pages of the requests before b
-    __shared__ int s_blocks[kMaxStreamSeqs + 1];   // blocks of the requests before b
-    __shared__ int s_tile_pages;
-    const Lane ln;
-    const int B = a.num_seqs;
-    const int Hkv = a.num_kv_heads;
-    const int Wg = (int)gridDim.x;
-
-    // per-request page counts, then (once the tile size is known) block counts
-    if (ln.wave == 0) {
-        wave_prefix(s_pages, B, [&](int i) {
-            return (clamp_ctx(a.context_lens[i], a.max_context_len) + kPageSize - 1) / kPageSize;
-        }, ln.lane);
-        const int tot = __shfl(s_pages[B], 0) * Hkv;
-        const int Wt = tot < Wg ? tot : Wg;
-        const int S = Wt > 0 ? (tot + Wt - 1) / Wt : 1;
-        wave_prefix(s_blocks, B, [&](int i) { return (s_pages[i + 1] - s_pages[i] + S - 1) / S; }, ln.lane);
-        if (ln.lane == 0)
-            s_tile_pages = S;
-    }
-    __syncthreads();
-
-    // LDS values are the same in every lane: keep them in scalar registers
-    auto pages_before = [&](int i) { return __builtin_amdgcn_readfirstlane(s_pages[i]); };
-    auto blocks_before = [&](int i) { return __builtin_amdgcn_readfirstlane(s_blocks[i]); };
-
-    // requests with no context: zero output, written by one workgroup each
-    for (int bb = blockIdx.x; bb < B; bb += Wg)
-        if (pages_before(bb + 1) == pages_before(bb))
-            write_empty<OUT_F32>(a, (size_t)bb * a.num_q_heads, a.num_q_heads, ln.tid, 256);
-
-    const int total = pages_before(B) * Hkv;   // below 2^31: checked on the host
-    const int W = total < Wg ? total : Wg;
-    const int w = blockIdx.x;
-    if (w >= W)
-        return;
-    const int S = __builtin_amdgcn_readfirstlane(s_tile_pages);
-    const Slices sl{total / W, total % W};
-    const int x1 = sl.start(w + 1);
-
-    for (int x = sl.start(w); x < x1;) {
-        // the request whose units hold x: the last b with Hkv * pages_before(b) <= x
-        int lo = 0, hi = B - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (pages_before(mid) * Hkv <= x)
-                lo = mid;
-            else
-                hi = mid - 1;
-        }
-        const int b = lo;
-        const int nb = pages_before(b + 1) - pages_before(b);
-        const int J = (nb + S - 1) / S;
-        const int off = x - pages_before(b) * Hkv;
-        const int j = min(off / (Hkv * S), J - 1);
-        const int len = min(S, nb - j * S);               // pages of block j
-        const int off_j = off - j * Hkv * S;
-        const int g = off_j / len;
-        const int pin = off_j - g * len;                   // page inside the tile
-        const int tile_end = x - pin + len;
-        const int seg_end = tile_end < x1 ? tile_end : x1;
-        const bool first_piece = (pin == 0);
-        const bool whole = first_piece && seg_end == tile_end;
-        const int p = j * S + pin;
-        const int p_hi = p + (seg_end - x);
-        const int ctx = clamp_ctx(a.context_lens[b], a.max_context_len);
-        const size_t row0 = (size_t)b * a.num_q_heads + (size_t)g * G;
-        const int32_t *trow = a.block_table + (size_t)b * a.max_blocks;
-        const int tile0 = blocks_before(b) * Hkv + g;     // tile of block 0; block j adds j * Hkv
-
-        u32x4 qv[G];
-        load_q<G>(qv, a, row0, ln.sub);
-        Stream<G> st;
-        st.init();
-        for (int c0 = p; c0 < p_hi; c0 += 64 * WAVES) {   // at most 64 pages per wavefront at a time
-            const int c1 = min(c0 + 64 * WAVES, p_hi);
-            const int idx = c0 + ln.wave + WAVES * ln.lane;
-            const int entry = idx < c1 ? trow[idx] : -1;
-            fold_range<G, WAVES>(st, a, qv, trow, g, c0, c1, nb, ctx, entry, ln);
-        }
-        __syncthreads();   // the previous piece's readers of sm are done
-        publish_streams<G, WAVES>(st, sm, ln);
-        __syncthreads();
-
-        if (J == 1 && whole) {
-            emit<G, WAVES, OUT_F32>(a, sm, row0, true, [&](int) { return (size_t)0; }, ln);
-        } else {
-            const int tile = tile0 + j * Hkv;
-            const size_t slot = (size_t)2 * tile + (first_piece ? 0 : 1);
-            emit<G, WAVES, OUT_F32>(a, sm, row0, false, [&](int h) { return slot * G + h; }, ln);
-            if (whole)
-                emit_empty<G, WAVES>(a, (slot + 1) * G, ln);
-            int32_t *ticket = a.counters + ((size_t)b * Hkv + g) * kCounterStride;
-            if (arrive<G, WAVES>(ticket, 2 * J, sm, ln, whole ? 2 : 1)) {
-                merge_partials<G, WAVES, OUT_F32>(
-                    a, sm, row0, 2 * J,
-                    [&](int i, int h) { return ((size_t)2 * (tile0 + (i >> 1) * Hkv) + (i & 1)) * G + h; },
-                    ticket, ln);
-            }
-        }
-        __syncthreads();
-        x = seg_end;
-    }
-}
-
 __global__ void zero_fill_kernel(uint8_t *p, size_t bytes)
 {
     const size_t n16 = bytes / 16;
@@ -825,18 +668,8 @@ hipError_t launch_split(const DecodeArgs &a, bool out_f32, unsigned grid, hipStr
 }
 
 template <int G>
-hipError_t launch_g(const DecodeArgs &a, int waves, int schedule, bool out_f32, hipStream_t stream, bool fused)
+hipError_t launch_g(const DecodeArgs &a, int waves, bool out_f32, hipStream_t stream, bool fused)
 {
-    if (schedule == kScheduleStream) {
-        if (fused)
-            return hipErrorInvalidValue;
-        const unsigned grid = (unsigned)a.stream_workgroups;
-        if (out_f32)
-            hipLaunchKernelGGL((paged_decode_stream_kernel<G, true>), dim3(grid), dim3(256), 0, stream, a);
-        else
-            hipLaunchKernelGGL((paged_decode_stream_kernel<G, false>), dim3(grid), dim3(256), 0, stream, a);
-        return hipGetLastError();
-    }
     const unsigned grid = (unsigned)((size_t)a.num_seqs * a.nsplit_max * a.num_kv_heads);
     if constexpr (G <= 2) {   // G = 4 at 16 wavefronts would not fit 128 VGPRs without spilling
         if (waves == 16)
@@ -847,15 +680,15 @@ hipError_t launch_g(const DecodeArgs &a, int waves, int schedule, bool out_f32, 
 
 }  // namespace
 
-hipError_t launch_paged_decode(const DecodeArgs &a, int group, int waves, int schedule, bool out_f32,
-                               hipStream_t stream, bool fused)
+hipError_t launch_paged_decode(const DecodeArgs &a, int group, int waves, bool out_f32, hipStream_t stream,
+                               bool fused)
 {
     if (a.num_seqs == 0)
         return hipSuccess;
     switch (group) {
-    case 1: return launch_g<1>(a, waves, schedule, out_f32, stream, fused);
-    case 2: return launch_g<2>(a, waves, schedule, out_f32, stream, fused);
-    case 4: return launch_g<4>(a, waves, schedule, out_f32, stream, fused);
+    case 1: return launch_g<1>(a, waves, out_f32, stream, fused);
+    case 2: return launch_g<2>(a, waves, out_f32, stream, fused);
+    case 4: return launch_g<4>(a, waves, out_f32, stream, fused);
     default: return hipErrorInvalidValue;
     }
 }

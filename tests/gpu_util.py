@@ -10,6 +10,7 @@ import torch
 import paged_kv_decode_gqa_amd as hd
 
 OUT_ATOL = 1e-2      # max |out - oracle| on bf16 (and fp32) outputs
+BF16_REACH = 4.0     # below this magnitude the nearest bf16 is within 2^-7 of any value; from 4 to 8, 2^-6
 LSE_RTOL = 1e-4      # |lse - oracle| <= 1e-4 * max(1, |oracle|)
 
 
@@ -52,7 +53,10 @@ def compare(out, lse, ref_out, ref_lse, ctx=None, *, what=""):
     assert np.all(np.isfinite(o)), f"{what}: non-finite output"
     err = np.abs(o - ref_out)
     max_err = float(err.max()) if err.size else 0.0
-    assert max_err <= OUT_ATOL, f"{what}: max |out err| {max_err} > {OUT_ATOL}"
+    # 1e-2 binds where a bf16 result can meet it (|oracle| < 4); fp32 outputs everywhere
+    bar = np.abs(ref_out) < BF16_REACH if out.dtype == torch.bfloat16 else np.ones(err.shape, dtype=bool)
+    max_bar = float(err[bar].max()) if bar.any() else 0.0
+    assert max_bar <= OUT_ATOL, f"{what}: max |out err| {max_bar} > {OUT_ATOL}"
     # rounding level: within one bf16 half-ulp of the exact value plus fp32 noise
     if out.dtype == torch.bfloat16:
         bound = np.abs(ref_out) * 2.0 ** -8 + 2e-5

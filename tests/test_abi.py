@@ -68,9 +68,6 @@ GOOD = [
     dict(workgroup_waves=16),
     dict(num_q_heads=16, num_kv_heads=4, workgroup_waves=4),
     dict(schedule=1),
-    dict(schedule=2),
-    dict(schedule=2, num_seqs=1),
-    dict(schedule=2, num_seqs=1024, max_context_len=4096, max_blocks_per_seq=256),
 ]
 
 BAD = [
@@ -96,11 +93,9 @@ BAD = [
     (dict(workgroup_waves=8), hd.HIPDECODE_ERR_UNSUPPORTED),
     (dict(workgroup_waves=-4), hd.HIPDECODE_ERR_UNSUPPORTED),
     (dict(num_q_heads=16, num_kv_heads=4, workgroup_waves=16), hd.HIPDECODE_ERR_UNSUPPORTED),
+    (dict(schedule=2), hd.HIPDECODE_ERR_UNSUPPORTED),
     (dict(schedule=3), hd.HIPDECODE_ERR_UNSUPPORTED),
     (dict(schedule=-1), hd.HIPDECODE_ERR_UNSUPPORTED),
-    (dict(schedule=2, num_seqs=1025, max_context_len=4096, max_blocks_per_seq=256), hd.HIPDECODE_ERR_UNSUPPORTED),
-    (dict(schedule=2, workgroup_waves=16), hd.HIPDECODE_ERR_UNSUPPORTED),
-    (dict(schedule=2, num_q_heads=2, num_kv_heads=1), hd.HIPDECODE_ERR_UNSUPPORTED),
 ]
 
 
@@ -179,7 +174,6 @@ def test_planner_wave_choice():
     assert hd.hipdecode_workgroup_waves(base(num_seqs=1, num_pages=2048)) == 4
     assert hd.hipdecode_workgroup_waves(base(num_seqs=1, max_context_len=512)) == 4
     assert hd.hipdecode_workgroup_waves(base(workgroup_waves=16, num_seqs=1)) == 16
-    assert hd.hipdecode_workgroup_waves(base(schedule=2, workgroup_waves=0)) == 4
 
 
 def test_planner_partitions():
@@ -196,11 +190,11 @@ def test_planner_partitions():
 
 
 def test_planner_schedule_choice():
-    # split unless the stream schedule is asked for
+    # one schedule, split by partition; invalid parameters give 0
     assert hd.hipdecode_schedule(base()) == hd.HIPDECODE_SCHEDULE_SPLIT
     assert hd.hipdecode_schedule(base(num_seqs=32, max_context_len=67500, max_blocks_per_seq=4219)) == 1
-    assert hd.hipdecode_schedule(base(schedule=2)) == hd.HIPDECODE_SCHEDULE_STREAM
     assert hd.hipdecode_schedule(base(schedule=1)) == 1
+    assert hd.hipdecode_schedule(base(schedule=2)) == 0
 
 
 def test_planner_and_workspace_sizes():
@@ -214,10 +208,6 @@ def test_planner_and_workspace_sizes():
     counters = 16 * 8 * 256   # one 256-byte line per (request, KV head)
     expect = counters + ((rows * nsplit * 8 + 255) // 256) * 256 + rows * nsplit * 128 * 4
     assert hd.hipdecode_workspace_bytes(p) == expect
-    # stream: counters plus two partial slots per tile, tiles <= W + B * Hkv (768 workgroups, G = 2)
-    ps = base(schedule=2)
-    slots = 2 * (768 + 16 * 8) * 2
-    assert hd.hipdecode_workspace_bytes(ps) == counters + ((slots * 8 + 255) // 256) * 256 + slots * 128 * 4
     # B=1 at 28672: 8 KV heads x 32 partitions = one workgroup per CU
     p1 = base(num_seqs=1, num_pages=2048)
     part1 = hd.hipdecode_partition_tokens(p1)
@@ -449,8 +439,8 @@ def test_fused_call_rejects_before_any_launch():
     lib = hd.library()
     fake = ctypes.c_void_p(1 << 20)
     call = lib.hipdecode_paged_attn_append
-    stream_sched = base(schedule=2)
-    assert call(ctypes.byref(stream_sched), 1e6, fake, fake, fake, fake, fake, fake, fake, fake, fake, fake,
+    bad_sched = base(schedule=2)
+    assert call(ctypes.byref(bad_sched), 1e6, fake, fake, fake, fake, fake, fake, fake, fake, fake, fake,
                 1 << 30, None) == hd.HIPDECODE_ERR_UNSUPPORTED
     for theta in (float("nan"), -1.0, float("inf")):
         assert call(ctypes.byref(base()), theta, fake, fake, fake, fake, fake, fake, fake, fake, fake, fake,

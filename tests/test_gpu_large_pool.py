@@ -54,7 +54,7 @@ def on_big_pools(case, dc: DeviceCase) -> int:
     return off
 
 
-@pytest.mark.parametrize("waves,schedule", [(4, 0), (16, 0), (4, 2)])
+@pytest.mark.parametrize("waves,schedule", [(4, 0), (16, 0), (4, 1)])
 def test_decode_past_4gib(waves, schedule):
     case = make_case([3000, 17, 5000, 1, 0, 2048], seed=51, poison=True)
     dc = DeviceCase(case)
