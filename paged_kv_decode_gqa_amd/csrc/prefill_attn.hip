@@ -333,12 +333,52 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qop[ks], s, 0, 0, 0);
         return s;
     };
-    auto softmax_pv = [&](auto masked, int kb, int stage, int hh, f32x16_t s) __attribute__((always_inline)) {
-        // Online softmax in base 2 (row j; keys 8(r/4) + 4 half + r%4).  With
-        // c = |scale| log2(e) > 0, the row maximum of c s is c max(s) and
-        // p = 2^(c s - m) is one FMA and one v_exp_f32 (weights below 2^-126
-        // of the row maximum may flush to zero); a masked score is -inf, so
-        // its weight is exactly 0.
+    // The softmax weights of one 32-key half, and their bf16 parts.
+    struct Half {
+        float pw[16];      // 2^(c s - m) per key of this lane
+        float psum;        // their sum
+        uint32_t pp[8];    // hi parts, packed pairs (keys in the S^T accumulator's order)
+        uint32_t pl[8];    // lo parts
+    };
+    // Online softmax in base 2 (row j; keys 8(r/4) + 4 half + r%4).  With
+    // c = |scale| log2(e) > 0, the row maximum of c s is c max(s) and
+    // p = 2^(c s - m) is one FMA and one v_exp_f32 (weights below 2^-126 of
+    // the row maximum may flush to zero); a masked score is -inf, so its
+    // weight is exactly 0.
+    //
+    // The running max m is not brought up to date on every half.  weights()
+    // computes p = 2^(c s - m) against the m in hand, with no branch; only
+    // when some lane's half sums past kPsumMax -- a row maximum well above m,
+    // or m still at its start value on a row's first half -- does settle()
+    // find the row maxima, move m, rescale l and the accumulators, and
+    // recompute the weights.  Every weight is then at most kPsumMax, which
+    // fp32 sums and bf16 operands carry with unchanged relative rounding; out
+    // and lse share the reference m.
+    //
+    // Each weight goes to the matrix cores as two bf16 parts, hi = the
+    // nearest bf16 and lo = the nearest bf16 of the remainder (exact in
+    // fp32), so hi + lo is within 2^-16 of it (relative) and the weights in
+    // P.V agree with the fp32 ones in l_run.
+    auto split = [&](Half &w) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+            w.pp[r / 2] = pack2_bf16(w.pw[r], w.pw[r + 1]);
+            const float h0 = __uint_as_float(w.pp[r / 2] << 16);
+            const float h1 = __uint_as_float(w.pp[r / 2] & 0xFFFF0000u);
+            w.pl[r / 2] = pack2_bf16(w.pw[r] - h0, w.pw[r + 1] - h1);
+        }
+    };
+    auto exps = [&](Half &w, const f32x16_t &s, float m) __attribute__((always_inline)) {
+        const float c = a.scale_log2;
+        w.psum = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+            w.pw[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c, -m));   // masked: 2^-inf = 0
+            w.pw[r + 1] = __builtin_amdgcn_exp2f(fmaf(s[r + 1], c, -m));
+            w.psum += w.pw[r] + w.pw[r + 1];
+        }
+    };
+    auto weights = [&](auto masked, int kb, int hh, f32x16_t &s, Half &w) __attribute__((always_inline)) {
         if constexpr (decltype(masked)::value) {  // only steps reaching past the tile's first position
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -346,62 +386,33 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
                 s[r] = key > pos ? -INFINITY : s[r];
             }
         }
-        // The running max m is not brought up to date on every half.  The
-        // weights p = 2^(c s - m) are computed against the m in hand; only
-        // when some lane's half sums past kPsumMax -- a row maximum well
-        // above m, or m still at its start value on a row's first half --
-        // does the wavefront find the row maxima, move m, rescale l and the
-        // accumulators, and recompute the weights.  Every weight is then at
-        // most kPsumMax, which fp32 sums and bf16 operands carry with
-        // unchanged relative rounding; out and lse share the reference m.
-        const float c = a.scale_log2;
-        float pw[16];
-        float psum = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-            pw[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c, -m_run));   // masked: 2^-inf = 0
-            pw[r + 1] = __builtin_amdgcn_exp2f(fmaf(s[r + 1], c, -m_run));
-            psum += pw[r] + pw[r + 1];
-        }
-        if (__any(!(psum <= kPsumMax))) {
+        exps(w, s, m_run);
+        split(w);
+    };
+    auto settle = [&](const f32x16_t &s, Half &w) __attribute__((always_inline)) {
+        if (__any(!(w.psum <= kPsumMax))) {
             float mx = -INFINITY;
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 mx = fmaxf(mx, s[r]);
-            const float m_new = fmaxf(m_run, pair_max(mx) * c);
+            const float m_new = fmaxf(m_run, pair_max(mx) * a.scale_log2);
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
             m_run = m_new;
             l_run *= alpha;
 #pragma unroll
             for (int db = 0; db < kDimBlocks; ++db)
                 acc[db] *= alpha;
-            psum = 0.f;
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                pw[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c, -m_new));
-                pw[r + 1] = __builtin_amdgcn_exp2f(fmaf(s[r + 1], c, -m_new));
-                psum += pw[r] + pw[r + 1];
-            }
+            exps(w, s, m_new);
+            split(w);
         }
-        l_run += psum;
-        // Each weight goes to the matrix cores as two bf16 parts, hi = the
-        // nearest bf16 and lo = the nearest bf16 of the remainder (exact in
-        // fp32), so hi + lo is within 2^-16 of it (relative) and the weights
-        // in P.V agree with the fp32 ones in l_run.
-        uint32_t pp[8], pl[8];
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-            pp[r / 2] = pack2_bf16(pw[r], pw[r + 1]);
-            const float h0 = __uint_as_float(pp[r / 2] << 16);
-            const float h1 = __uint_as_float(pp[r / 2] & 0xFFFF0000u);
-            pl[r / 2] = pack2_bf16(pw[r] - h0, pw[r + 1] - h1);
-        }
-
-        // O^T += V^T P^T, two k-steps of 16 keys.  P^T: lane l holds keys
-        // 16 kh + 4 half + e and 16 kh + 8 + 4 half + e (e < 4) of this half,
-        // in the S^T accumulator's own order; the V^T reads take the same keys.
+        l_run += w.psum;
+    };
+    // V^T operands of one half: O^T += V^T P^T in two k-steps of 16 keys.
+    // P^T: lane l holds keys 16 kh + 4 half + e and 16 kh + 8 + 4 half + e
+    // (e < 4) of the half, in the S^T accumulator's own order; the V^T reads
+    // take the same keys.
+    auto read_vt = [&](int stage, int hh, i16x8_t (&vv)[2][kDimBlocks]) __attribute__((always_inline)) {
         const lds_u8_t *vl = (const lds_u8_t *)&v_lds[stage][32 * hh * kRowBytes];
-        i16x8_t vv[2][kDimBlocks];
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
@@ -411,13 +422,14 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
                 const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(p + 8 * kRowBytes));
                 vv[kh][db] = i16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             }
-        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto pv = [&](const i16x8_t (&vv)[2][kDimBlocks], const Half &w) __attribute__((always_inline)) {
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
             const bf16x8_t phi = __builtin_bit_cast(
-                bf16x8_t, make_uint4(pp[4 * kh], pp[4 * kh + 1], pp[4 * kh + 2], pp[4 * kh + 3]));
+                bf16x8_t, make_uint4(w.pp[4 * kh], w.pp[4 * kh + 1], w.pp[4 * kh + 2], w.pp[4 * kh + 3]));
             const bf16x8_t plo = __builtin_bit_cast(
-                bf16x8_t, make_uint4(pl[4 * kh], pl[4 * kh + 1], pl[4 * kh + 2], pl[4 * kh + 3]));
+                bf16x8_t, make_uint4(w.pl[4 * kh], w.pl[4 * kh + 1], w.pl[4 * kh + 2], w.pl[4 * kh + 3]));
 #pragma unroll
             for (int db = 0; db < kDimBlocks; ++db) {
                 const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, vv[kh][db]);
@@ -426,9 +438,23 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
             }
         }
     };
-    // Both halves' scores are issued first: the matrix cores work on the
-    // second half's S while the first half's softmax runs on the VALU, and on
-    // the first half's P.V while the second softmax runs.
+    // One half alone (the late rows' steps, each wavefront on one half).
+    auto softmax_pv = [&](auto masked, int kb, int stage, int hh, f32x16_t s) __attribute__((always_inline)) {
+        Half w;
+        weights(masked, kb, hh, s, w);
+        settle(s, w);
+        i16x8_t vv[2][kDimBlocks];
+        read_vt(stage, hh, vv);
+        __builtin_amdgcn_sched_barrier(0);
+        pv(vv, w);
+    };
+    // Both halves: the scores of both are issued first, so the matrix cores
+    // work on the second half's S while the first half's weights are formed;
+    // the second half's weights and their parts (branch-free) are formed
+    // beside the first half's P.V products, whose V^T operands, and the second
+    // half's, are read before them; only then can the second half's rare
+    // rescale (which needs the first half's products in the accumulators)
+    // run, followed by its P.V.
     auto compute_step = [&](auto masked, int kb, int stage) __attribute__((always_inline)) {
         // all sixteen K operands of the step are read before the first MFMA
         bf16x8_t k0[kHeadDim / 16], k1[kHeadDim / 16];
@@ -447,8 +473,17 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
 #pragma unroll
         for (int ks = 0; ks < kHeadDim / 16; ++ks)
             s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1[ks], qop[ks], s1, 0, 0, 0);
-        softmax_pv(masked, kb, stage, 0, s0);
-        softmax_pv(masked, kb, stage, 1, s1);
+        Half w0, w1;
+        weights(masked, kb, 0, s0, w0);
+        settle(s0, w0);
+        i16x8_t vv0[2][kDimBlocks], vv1[2][kDimBlocks];
+        read_vt(stage, 0, vv0);
+        read_vt(stage, 1, vv1);
+        __builtin_amdgcn_sched_barrier(0);
+        pv(vv0, w0);
+        weights(masked, kb, 1, s1, w1);
+        settle(s1, w1);
+        pv(vv1, w1);
     };
 
     // Pipeline: step kb + 2 is copied into LDS while step kb is computed.
