@@ -142,6 +142,24 @@ def test_fp32_output_long():
     _check(case, "fp32 out")
 
 
+@pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
+def test_small_lse_meets_the_relative_bar(out_dtype):
+    """Two-token contexts at a small scale put every lse near ln 2 (|lse| < 1),
+    where the bar 1e-4 * max(1, |lse|) is absolute; here each lse must also
+    meet the relative bar 1e-4 * |lse| itself.  (The floor of 1 stays in the
+    shared check for lse near 0, where the fp32 sum m + ln l of two terms of
+    opposite sign can cancel and no relative bound holds.)"""
+    case = make_case([2] * 12 + [3, 2, 2, 2], seed=19, out_dtype=out_dtype, scale=0.01)
+    out, lse = _check(case, f"small lse, {out_dtype} out")
+    _, ref_lse = oracle.run_case(case)
+    l = lse.cpu().numpy().astype(np.float64)
+    small = np.abs(ref_lse) < 1.0
+    assert small.sum() >= 16 * 12, "the case must put most lse below 1"
+    rel = np.abs(l - ref_lse)[small] / np.abs(ref_lse[small])
+    assert float(rel.max()) <= 1e-4, f"relative lse error {float(rel.max())}"
+    log(f"[parity] small lse: {int(small.sum())} values in (-1, 1), max relative error {float(rel.max()):.2e}")
+
+
 def test_batch_zero_is_noop():
     q = torch.zeros((0, 16, 128), dtype=torch.bfloat16, device="cuda")
     k = torch.zeros((4, 16, 8, 128), dtype=torch.bfloat16, device="cuda")
