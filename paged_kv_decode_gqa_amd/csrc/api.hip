@@ -284,6 +284,7 @@ hipdecode_status run_decode(const hipdecode_params *params, const void *q, const
     a.max_context_len = p.max_context_len;
     a.partition_pages = part / kPageSize;
     a.nsplit_max = nsplit;
+    a.head_mix = p.num_kv_heads % 8 == 0 ? 8 : p.num_kv_heads % 4 == 0 ? 4 : p.num_kv_heads % 2 == 0 ? 2 : 1;
     a.scale_log2 = p.scale * 1.44269504088896340736f;
     a.k_new = static_cast<const uint16_t *>(k_new);
     a.v_new = static_cast<const uint16_t *>(v_new);

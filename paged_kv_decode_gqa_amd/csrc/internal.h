@@ -46,6 +46,7 @@ struct DecodeArgs {
     int32_t max_context_len;
     int32_t partition_pages;
     int32_t nsplit_max;          // partitions of the longest context
+    int32_t head_mix;            // largest power of two <= 8 dividing num_kv_heads: KV heads XOR-ed by dispatch round
     float scale_log2;   // scale * log2(e): scores are kept in base-2 units
     // Fused append (hipdecode_paged_attn_append) only: each request's new
     // token, written to its slot and folded from registers, and RoPE.

@@ -531,8 +531,18 @@ void paged_decode_kernel(DecodeArgs a)
     __shared__ Smem<G, WAVES> sm;
     const Lane ln;
     const int Hkv = a.num_kv_heads;
-    const int g = blockIdx.x % Hkv;
     const int rest = blockIdx.x / Hkv;
+    // The dispatcher hands out workgroups in rounds of one per CU (256 on
+    // MI355X), so one CU holds workgroups r * 256 + i of successive rounds r.
+    // XOR-ing the KV head with the round gives each CU rows of several heads,
+    // whose addresses differ in bits 8-10 of the token row; measured 1.4%
+    // faster at 16 x 28,672 tokens and 1.8% at the 32-request mix, unchanged
+    // when the grid is a single round.  The XOR value is taken from the first
+    // workgroup of the unit's Hkv consecutive ones, and acts within groups of
+    // head_mix heads (a power of two dividing Hkv), so every unit still maps
+    // its Hkv workgroups onto its Hkv heads one to one.
+    const int round = (int)(((unsigned)rest * (unsigned)Hkv) >> 8);
+    const int g = (int)(blockIdx.x % Hkv) ^ (round & (a.head_mix - 1));
     const int pp = a.partition_pages;
     // Unit `rest` in the full grid: request rest / nsplit_max, partition rest % nsplit_max.
     const int b_full = rest / a.nsplit_max;

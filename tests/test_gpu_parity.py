@@ -142,6 +142,15 @@ def test_fp32_output_long():
     _check(case, "fp32 out")
 
 
+@pytest.mark.parametrize("hq,hkv", [(12, 12), (24, 12), (12, 6), (16, 8), (4, 1)])
+def test_heads_mixed_across_dispatch_rounds(hq, hkv):
+    """Grids of many 256-workgroup rounds, where the kernel XORs each unit's
+    KV head with its round: with Hkv 12 or 6 a unit's Hkv workgroups straddle
+    round boundaries, and every head must still be computed exactly once."""
+    case = make_case([20000, 9000, 1], seed=23, Hq=hq, Hkv=hkv, poison=True)
+    _check(case, f"heads mixed by round, {hq}/{hkv}", partition_tokens=256)
+
+
 @pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
 def test_small_lse_meets_the_relative_bar(out_dtype):
     """Two-token contexts at a small scale put every lse near ln 2 (|lse| < 1),
