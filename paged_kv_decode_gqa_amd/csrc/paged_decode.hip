@@ -479,7 +479,7 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane)
     return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
 }
 
-// The split schedule's work list.  The grid has a slot for every partition
+// The work list.  The grid has a slot for every partition
 // the longest context could need, but a ragged batch has far fewer real
 // (request, partition) units.  Unit u is the u-th real unit in request order,
 // partitions ascending; an empty request counts one unit, which writes its
@@ -518,8 +518,9 @@ __device__ __forceinline__ RealUnit real_unit(const DecodeArgs &a, int u)
 }
 
 // ---------------------------------------------------------------------------
-// split schedule: workgroup = (real unit, KV head), KV head fastest so
-// consecutive workgroups read neighbouring head rows of the same pages.  A
+// workgroup = (real unit, KV head), KV head fastest so consecutive
+// workgroups read neighbouring head rows of the same pages (the heads are
+// XOR-ed by dispatch round below).  A
 // single request, or a batch with one partition per request, maps the grid
 // directly (unit = request * nsplit_max + partition; units past a request's
 // partition count exit); any other batch goes through real_unit().
