@@ -14,7 +14,7 @@ constexpr int kHeadDim = 128;   // dims per head; a K or V row is 256 bytes
 constexpr int kPageSize = 16;   // tokens per page
 constexpr int kMinPartition = 64;     // split-K partitions are multiples of this many tokens
 constexpr int kMaxPartition = 4096;   // at most 256 pages, so at most 64 per wavefront: one table entry per lane
-constexpr int kMaxMergeSplits = 1024; // partitions per request the final merge can weigh in LDS
+constexpr int kMaxMergeSplits = 1024; // partitions per request: bounds the partials one workgroup merges
 constexpr int kCounterStride = 64;   // int32 per arrival counter: each on its own 256-byte line
 constexpr int kScheduleSplit = 1;
 

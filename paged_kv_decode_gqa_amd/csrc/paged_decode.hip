@@ -30,8 +30,6 @@ namespace {
 
 using namespace dev;
 
-constexpr int kRegPartials = 8;   // final merge: partial sums per thread loaded up front
-
 // Reductions over a wavefront: four DPP steps inside each row of 16 lanes
 // (as row_sum16 does), then the four rows' results through v_readlane, so no
 // step waits on an LDS-based lane shuffle.
@@ -114,21 +112,20 @@ __device__ __forceinline__ void merge_row_groups(Stream<G> &st)
     merge_pairs<G, 32>(st);
 }
 
-// LDS shared by both kernels.
+// LDS of the decode kernel.  With four wavefronts the 16 row-group streams
+// go to LDS as they are and are merged there in one step; sixteen
+// wavefronts first merge their row-groups in registers, so LDS holds one
+// stream per wavefront.  The final merge uses acc as scratch when several
+// threads share a dim.
 template <int G, int WAVES>
 struct Smem {
     static constexpr int kThreadsWG = 64 * WAVES;
-    static constexpr int kChunks = G * kHeadDim / 4;   // float4 chunks of G heads
-    static constexpr int kSets = kThreadsWG / kChunks;  // final merge: partial subsets
-    static constexpr int kScratch4 =
-        (WAVES * G * kHeadDim / 4 > kThreadsWG) ? WAVES * G * kHeadDim / 4 : kThreadsWG;
-    f32x4 acc4[kScratch4];          // [WAVES][G][kHeadDim] floats, or final-merge scratch
-    float m[WAVES][G];
-    float l[WAVES][G];
-    float w[G][kMaxMergeSplits];    // final merge: partial maxima, then weights
-    float lw[G][kMaxMergeSplits];   // final merge: partial sums
-    float head_m[G];
-    float head_l[G];
+    static constexpr int kRowGroups = WAVES == 4 ? 4 : 1;   // streams per wavefront kept apart
+    static constexpr int kStreams = WAVES * kRowGroups;
+    static_assert(kStreams <= 64, "one stream per lane when weighing them");
+    float acc[kStreams][G][kHeadDim];   // unnormalised sums of V per stream
+    float m[kStreams][G];
+    float l[kStreams][G];
     int last;
 };
 
@@ -262,59 +259,73 @@ __device__ __forceinline__ void fold_range(Stream<G> &st, const DecodeArgs &a, c
     }
 }
 
-// Row-groups inside each wavefront, then the wavefronts' totals into LDS.
-// The caller syncs the workgroup afterwards.
+// The workgroup's streams into LDS (row-groups merged first only with
+// sixteen wavefronts).  The caller syncs the workgroup afterwards.
 template <int G, int WAVES>
 __device__ __forceinline__ void publish_streams(Stream<G> &st, Smem<G, WAVES> &sm, const Lane &ln)
 {
-    merge_row_groups<G>(st);
-    if (ln.row == 0) {
+    using S = Smem<G, WAVES>;
+    if constexpr (S::kRowGroups == 1)
+        merge_row_groups<G>(st);
+    if (S::kRowGroups == 4 || ln.row == 0) {
+        const int s = ln.wave * S::kRowGroups + (S::kRowGroups == 4 ? ln.row : 0);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            f32x4 *dst = sm.acc4 + ((ln.wave * G + h) * kHeadDim + ln.sub * 8) / 4;
+            f32x4 *dst = reinterpret_cast<f32x4 *>(&sm.acc[s][h][ln.sub * 8]);
             dst[0] = f32x4{st.acc[h][0], st.acc[h][1], st.acc[h][2], st.acc[h][3]};
             dst[1] = f32x4{st.acc[h][4], st.acc[h][5], st.acc[h][6], st.acc[h][7]};
             if (ln.sub == 0) {
-                sm.m[ln.wave][h] = st.m[h];
-                sm.l[ln.wave][h] = st.l[h];
+                sm.m[s][h] = st.m[h];
+                sm.l[s][h] = st.l[h];
             }
         }
     }
 }
 
-// Combine the workgroup's wavefronts for query head h, dim d: (M, L, A).
-template <int G, int WAVES>
-__device__ __forceinline__ void combine_waves(const Smem<G, WAVES> &sm, int h, int d, float &M, float &L,
-                                              float &A)
+// Max and sum over the first N lanes of a wavefront, handed to every lane
+// (lanes past N must hold -inf and 0).
+template <int N>
+__device__ __forceinline__ float lanes_max(float x)
 {
-    const float *s_acc = reinterpret_cast<const float *>(sm.acc4);
-    M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w)
-        M = fmaxf(M, sm.m[w][h]);
-    const float M_use = (M == -INFINITY) ? 0.f : M;
-    L = 0.f;
-    A = 0.f;
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w) {
-        const float wt = merge_weight(sm.m[w][h], M_use);
-        L = fmaf(sm.l[w][h], wt, L);
-        A = fmaf(s_acc[(w * G + h) * kHeadDim + d], wt, A);
-    }
+    if constexpr (N <= 16)
+        return lane_value(row_max16(x), 0);
+    else
+        return wave_max(x);
+}
+
+template <int N>
+__device__ __forceinline__ float lanes_sum(float x)
+{
+    if constexpr (N <= 16)
+        return lane_value(row_sum16(x), 0);
+    else
+        return wave_sum(x);
 }
 
 // Write the workgroup's result for G query heads: final output when one
 // workgroup covers the (request, KV head), else a partial at partial index
-// part_index(h).  The caller syncs before and after.
+// part_index(h).  Each thread takes dims of one head at a time (uniform
+// across its wavefront); lane j weighs stream j, so the streams' weights
+// reach the sums as scalars.  The caller syncs before and after.
 template <int G, int WAVES, bool OUT_F32, class PartIndex>
 __device__ __forceinline__ void emit(const DecodeArgs &a, const Smem<G, WAVES> &sm, size_t row0, bool final,
                                      PartIndex part_index, const Lane &ln)
 {
-    for (int idx = ln.tid; idx < G * kHeadDim; idx += Smem<G, WAVES>::kThreadsWG) {
-        const int h = idx / kHeadDim;
+    using S = Smem<G, WAVES>;
+    constexpr int NS = S::kStreams;
+    for (int idx = ln.tid; idx < G * kHeadDim; idx += S::kThreadsWG) {
+        const int h = __builtin_amdgcn_readfirstlane(idx / kHeadDim);
         const int d = idx % kHeadDim;
-        float M, L, A;
-        combine_waves<G, WAVES>(sm, h, d, M, L, A);
+        const float ms = ln.lane < NS ? sm.m[ln.lane][h] : -INFINITY;
+        const float ls = ln.lane < NS ? sm.l[ln.lane][h] : 0.f;
+        const float M = lanes_max<NS>(ms);
+        const float M_use = (M == -INFINITY) ? 0.f : M;
+        const float w = merge_weight(ms, M_use);   // 0 past the streams
+        const float L = lanes_sum<NS>(ls * w);
+        float A = 0.f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+            A = fmaf(lane_value(w, s), sm.acc[s][h][d], A);
         if (final) {
             store_out<OUT_F32>(a.out, (row0 + h) * kHeadDim + d, A / L);
             if (d == 0 && a.lse != nullptr)
@@ -345,105 +356,137 @@ __device__ __forceinline__ bool arrive(int32_t *ticket, int count, Smem<G, WAVES
     return __builtin_amdgcn_readfirstlane(sm.last) != 0;
 }
 
-// An empty partial (no tokens): weight 0 in any merge.
-template <int G, int WAVES>
-__device__ __forceinline__ void emit_empty(const DecodeArgs &a, size_t part_base, const Lane &ln)
+// K consecutive floats (K = 1 or 2) of a partial, coherently.
+template <int K>
+__device__ __forceinline__ void load_dims(float (&v)[K], const float *p)
 {
-    for (int idx = ln.tid; idx < G * kHeadDim; idx += Smem<G, WAVES>::kThreadsWG) {
-        const size_t pi = part_base + idx / kHeadDim;
-        coherent_store(a.part_acc + pi * kHeadDim + idx % kHeadDim, 0.f);
-        if (idx % kHeadDim == 0) {
-            coherent_store(a.part_ml + pi * 2 + 0, -INFINITY);
-            coherent_store(a.part_ml + pi * 2 + 1, 0.f);
-        }
+    if constexpr (K == 1) {
+        v[0] = coherent_load(p);
+    } else {
+        static_assert(K == 2, "one or two dims per thread");
+        const uint64_t u = coherent_load8(p);
+        v[0] = __uint_as_float((uint32_t)u);
+        v[1] = __uint_as_float((uint32_t)(u >> 32));
     }
 }
 
-// Merge `count` partials of G query heads (partial i of head h at index
-// part_index(i, h)), write out and lse, and reset the ticket.
+// The final merge of `count` partials of G query heads (partial i of head h
+// at index part_index(i, h)).  Thread t owns K dims of one head; when the
+// workgroup has more threads than dims, the threads of a dim split the
+// partials into S sets and add their sums through LDS at the end.  Every
+// wavefront finds its head's maximum and sum itself, lane j weighing
+// partials j, j + 64, ..., so the weights reach the sums as scalars and no
+// workgroup barrier separates the loads from the sums.  A thread's first
+// PRE partials are loaded in one batch right after the (m, l) pairs.
+template <int G, int WAVES, int PRE, bool OUT_F32, class PartIndex>
+__device__ __forceinline__ void merge_partials_pre(const DecodeArgs &a, Smem<G, WAVES> &sm, size_t row0,
+                                                   int count, PartIndex part_index, const Lane &ln)
+{
+    constexpr int D = G * kHeadDim;
+    constexpr int NT = 64 * WAVES;
+    constexpr int K = D > NT ? D / NT : 1;          // dims per thread
+    constexpr int S = NT > D ? NT / D : 1;          // sets of partials
+    constexpr int TPS = D / K;                      // threads per set
+    static_assert(K <= 2 && TPS % 64 == 0, "whole wavefronts per set and head");
+    const int t = ln.tid % TPS;
+    const int set = __builtin_amdgcn_readfirstlane(ln.tid / TPS);
+    const int h = __builtin_amdgcn_readfirstlane(t * K / kHeadDim);
+    const int d = (t * K) % kHeadDim;
+    const float *acc_base = a.part_acc + d;
+    auto acc_ptr = [&](int i) { return acc_base + part_index(i, h) * kHeadDim; };
+
+    // (m, l) of partials lane, lane + 64, ... : the first 64 stay in registers
+    const int i0 = min(ln.lane, count - 1);
+    const uint64_t ml0 = coherent_load8(a.part_ml + part_index(i0, h) * 2);
+    float pre[PRE][K];
+#pragma unroll
+    for (int r = 0; r < PRE; ++r)
+        load_dims<K>(pre[r], acc_ptr(min(set + r * S, count - 1)));
+    const float m0 = ln.lane < count ? __uint_as_float((uint32_t)ml0) : -INFINITY;
+    const float l0 = ln.lane < count ? __uint_as_float((uint32_t)(ml0 >> 32)) : 0.f;
+    float mx = m0;
+    for (int c0 = 64; c0 < count; c0 += 64) {
+        const int i = c0 + ln.lane;
+        if (i < count)
+            mx = fmaxf(mx, __uint_as_float((uint32_t)coherent_load8(a.part_ml + part_index(i, h) * 2)));
+    }
+    const float M = wave_max(mx);
+    const float M_use = (M == -INFINITY) ? 0.f : M;
+    const float w0 = merge_weight(m0, M_use);
+    float lsum = l0 * w0;
+    float A[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+        A[k] = 0.f;
+    const int n0 = min(count, 64);
+#pragma unroll
+    for (int r = 0; r < PRE; ++r) {
+        const int i = set + r * S;
+        if (i < n0) {
+            const float wi = lane_value(w0, i);
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+                A[k] = fmaf(wi, pre[r][k], A[k]);
+        }
+    }
+    for (int i = set + PRE * S; i < n0; i += S) {
+        float v[K];
+        load_dims<K>(v, acc_ptr(i));
+        const float wi = lane_value(w0, i);
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            A[k] = fmaf(wi, v[k], A[k]);
+    }
+    for (int c0 = 64; c0 < count; c0 += 64) {   // partials past the first 64
+        const int j = c0 + ln.lane;
+        const uint64_t ml = coherent_load8(a.part_ml + part_index(min(j, count - 1), h) * 2);
+        const float wj = j < count ? merge_weight(__uint_as_float((uint32_t)ml), M_use) : 0.f;
+        lsum = fmaf(j < count ? __uint_as_float((uint32_t)(ml >> 32)) : 0.f, wj, lsum);
+        const int first = c0 + (set - c0 % S + S) % S;   // the set's first partial of this chunk
+        for (int i = first; i < min(count, c0 + 64); i += S) {
+            float v[K];
+            load_dims<K>(v, acc_ptr(i));
+            const float wi = lane_value(wj, i - c0);
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+                A[k] = fmaf(wi, v[k], A[k]);
+        }
+    }
+    const float L = wave_sum(lsum);
+    if constexpr (S > 1) {
+        float *scratch = &sm.acc[0][0][0];
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            scratch[set * D + t * K + k] = A[k];
+        __syncthreads();
+        if (set != 0)
+            return;
+#pragma unroll
+        for (int s = 1; s < S; ++s)
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+                A[k] += scratch[s * D + t * K + k];
+    }
+    const size_t o = (row0 + h) * kHeadDim + d;
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+        store_out<OUT_F32>(a.out, o + k, A[k] / L);
+    if (d == 0 && a.lse != nullptr)
+        a.lse[row0 + h] = (M + log2f(L)) * kLn2;
+}
+
+// The final merge, with as many partials loaded up front as a set needs
+// (8 or 32), and the ticket reset for the next call.
 template <int G, int WAVES, bool OUT_F32, class PartIndex>
 __device__ __forceinline__ void merge_partials(const DecodeArgs &a, Smem<G, WAVES> &sm, size_t row0, int count,
                                                PartIndex part_index, int32_t *ticket, const Lane &ln)
 {
-    using S = Smem<G, WAVES>;
-    // Every thread owns 4 dims of one head and a 1/kSets share of the
-    // partials.  Its first kRegPartials partial sums and the (m, l) pair of
-    // partial tid are loaded in one batch, without branches (indices past the
-    // end are clamped and their values dropped), so the merge waits on
-    // memory once; (m, l) pairs past the first kThreadsWG follow in a loop.
-    const int chunk = ln.tid % S::kChunks;
-    const int set = ln.tid / S::kChunks;
-    const int h = chunk / (kHeadDim / 4);
-    const int c = chunk % (kHeadDim / 4);
-    const int n_ml = G * count;
-    const int idx0 = min(ln.tid, n_ml - 1);
-    const int hh0 = idx0 / count;
-    const uint64_t ml0 = coherent_load8(a.part_ml + part_index(idx0 - hh0 * count, hh0) * 2);
-    f32x4 pre[kRegPartials];
-#pragma unroll
-    for (int r = 0; r < kRegPartials; ++r) {
-        const int i = min(set + r * S::kSets, count - 1);
-        pre[r] = coherent_load4(a.part_acc + part_index(i, h) * kHeadDim + 4 * c);
-    }
-    if (ln.tid < n_ml) {
-        sm.w[hh0][idx0 - hh0 * count] = __uint_as_float((uint32_t)ml0);
-        sm.lw[hh0][idx0 - hh0 * count] = __uint_as_float((uint32_t)(ml0 >> 32));
-    }
-    for (int idx = ln.tid + S::kThreadsWG; idx < n_ml; idx += S::kThreadsWG) {
-        const int hh = idx / count;
-        const int i = idx - hh * count;
-        const uint64_t ml = coherent_load8(a.part_ml + part_index(i, hh) * 2);
-        sm.w[hh][i] = __uint_as_float((uint32_t)ml);
-        sm.lw[hh][i] = __uint_as_float((uint32_t)(ml >> 32));
-    }
-    __syncthreads();
-    // wavefront hw turns head hw's maxima into weights and sums L
-    if (ln.wave < G) {
-        const int hw = ln.wave;
-        float mx = -INFINITY;
-        for (int i = ln.lane; i < count; i += 64)
-            mx = fmaxf(mx, sm.w[hw][i]);
-        mx = wave_max(mx);
-        const float M_use = (mx == -INFINITY) ? 0.f : mx;
-        float ls = 0.f;
-        for (int i = ln.lane; i < count; i += 64) {
-            const float w = merge_weight(sm.w[hw][i], M_use);
-            sm.w[hw][i] = w;
-            ls = fmaf(sm.lw[hw][i], w, ls);
-        }
-        ls = wave_sum(ls);
-        if (ln.lane == 0) {
-            sm.head_m[hw] = mx;
-            sm.head_l[hw] = ls;
-        }
-    }
-    __syncthreads();
-
-    f32x4 A = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int r = 0; r < kRegPartials; ++r) {
-        const int i = set + r * S::kSets;
-        if (i < count)
-            A += sm.w[h][i] * pre[r];
-    }
-#pragma unroll 8
-    for (int i = set + kRegPartials * S::kSets; i < count; i += S::kSets)
-        A += sm.w[h][i] * coherent_load4(a.part_acc + part_index(i, h) * kHeadDim + 4 * c);
-    sm.acc4[set * S::kChunks + chunk] = A;
-    __syncthreads();
-    if (set == 0) {
-#pragma unroll
-        for (int s = 1; s < S::kSets; ++s)
-            A += sm.acc4[s * S::kChunks + chunk];
-        const float hl = sm.head_l[h];
-        const size_t o = (row0 + h) * kHeadDim + 4 * c;
-        store_out<OUT_F32>(a.out, o + 0, A[0] / hl);
-        store_out<OUT_F32>(a.out, o + 1, A[1] / hl);
-        store_out<OUT_F32>(a.out, o + 2, A[2] / hl);
-        store_out<OUT_F32>(a.out, o + 3, A[3] / hl);
-        if (c == 0 && a.lse != nullptr)
-            a.lse[row0 + h] = (sm.head_m[h] + log2f(hl)) * kLn2;
-    }
+    constexpr int D = G * kHeadDim;
+    constexpr int S = 64 * WAVES > D ? 64 * WAVES / D : 1;
+    if (count <= 8 * S)
+        merge_partials_pre<G, WAVES, 8, OUT_F32>(a, sm, row0, count, part_index, ln);
+    else
+        merge_partials_pre<G, WAVES, 32, OUT_F32>(a, sm, row0, count, part_index, ln);
     if (ln.tid == 0)
         __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -525,8 +568,10 @@ __device__ __forceinline__ RealUnit real_unit(const DecodeArgs &a, int u)
 // directly (unit = request * nsplit_max + partition; units past a request's
 // partition count exit); any other batch goes through real_unit().
 // ---------------------------------------------------------------------------
+// Four wavefronts per SIMD fit in 128 VGPRs for G <= 2; G = 4 holds twice the
+// softmax state and runs two per SIMD (about 172 VGPRs) rather than spill.
 template <int G, int WAVES, bool OUT_F32, bool FUSED>
-__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(G == 4 ? 2 : 4)))
 void paged_decode_kernel(DecodeArgs a)
 {
     __shared__ Smem<G, WAVES> sm;
