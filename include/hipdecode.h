@@ -442,6 +442,36 @@ hipdecode_status hipdecode_paged_attn_noalloc(const hipdecode_params *params,
                                               float *lse,
                                               void *stream);
 
+/* ------------------------------------------------------------------------
+ * Contract violations met on the device.
+ *
+ * The kernels never read or write outside the buffers the sizes describe,
+ * even when device-side contents break the contract; they clamp or skip
+ * instead (see each entry point).  Each time they do, they also set a bit in
+ * a flag word of the library, one word per GPU, so that a caller can find out
+ * afterwards that a result it holds is unspecified.  Setting a bit costs
+ * nothing on the normal path.
+ *   HIPDECODE_VIOLATION_CONTEXT: a context length below 0 or above
+ *       max_context_len (decode), or past 16 * max_blocks_per_seq tokens
+ *       (append, prefill);
+ *   HIPDECODE_VIOLATION_PAGE: a block-table entry that a request uses names
+ *       no page of the pool;
+ *   HIPDECODE_VIOLATION_ROWS: append or prefill: a request with more new
+ *       tokens than its context or than max_new_tokens, or rows outside
+ *       [0, num_rows) (new_start decreasing included).
+ * ------------------------------------------------------------------------ */
+
+#define HIPDECODE_VIOLATION_CONTEXT 1u
+#define HIPDECODE_VIOLATION_PAGE 2u
+#define HIPDECODE_VIOLATION_ROWS 4u
+
+/* Waits for all work on the current device (hipDeviceSynchronize), then
+ * stores in *flags the OR of the HIPDECODE_VIOLATION_* bits that kernels of
+ * this library have set on it since the previous call, and clears them.  Not
+ * for use under graph capture; calls from several host threads, or while
+ * another thread launches work on the device, may lose bits. */
+hipdecode_status hipdecode_contract_violations(uint32_t *flags);
+
 /* Static English text for a status code; never NULL. */
 const char *hipdecode_status_string(hipdecode_status status);
 

@@ -48,8 +48,15 @@ EXPORTED = (
     "hipdecode_step_runner_step",
     "hipdecode_step_runner_destroy",
     "hipdecode_paged_attn_noalloc",
+    "hipdecode_contract_violations",
     "hipdecode_status_string",
 )
+
+# Bits of hipdecode_contract_violations: device-side contents that broke the
+# contract (the kernels clamped or skipped them; the results are unspecified).
+HIPDECODE_VIOLATION_CONTEXT = 1
+HIPDECODE_VIOLATION_PAGE = 2
+HIPDECODE_VIOLATION_ROWS = 4
 
 # Bytes of the library's static scratch behind hipdecode_paged_attn_noalloc.
 HIPDECODE_NOALLOC_SCRATCH_BYTES = 16 << 20
@@ -195,6 +202,8 @@ def library() -> ctypes.CDLL:
     lib.hipdecode_step_runner_destroy.restype = ctypes.c_int
     lib.hipdecode_paged_attn_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.hipdecode_paged_attn_noalloc.restype = ctypes.c_int
+    lib.hipdecode_contract_violations.argtypes = [ctypes.POINTER(ctypes.c_uint32)]
+    lib.hipdecode_contract_violations.restype = ctypes.c_int
     lib.hipdecode_status_string.argtypes = [ctypes.c_int]
     lib.hipdecode_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -303,6 +312,16 @@ def hipdecode_paged_attn_noalloc(params: hipdecode_params, q, k_pool, v_pool, bl
                                                 _stream_handle(stream))
     if st != HIPDECODE_OK:
         raise HipDecodeError(st, "hipdecode_paged_attn_noalloc")
+
+
+def hipdecode_contract_violations() -> int:
+    """Wait for the current device, return the HIPDECODE_VIOLATION_* bits the
+    library's kernels set there since the last call, and clear them."""
+    flags = ctypes.c_uint32(0)
+    st = library().hipdecode_contract_violations(ctypes.byref(flags))
+    if st != HIPDECODE_OK:
+        raise HipDecodeError(st, "hipdecode_contract_violations")
+    return int(flags.value)
 
 
 class PreparedCall:

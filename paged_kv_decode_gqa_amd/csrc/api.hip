@@ -5,6 +5,7 @@
 
 #include <math.h>
 
+#include <atomic>
 #include <mutex>
 
 namespace hipdecode {
@@ -291,6 +292,7 @@ hipdecode_status run_decode(const hipdecode_params *params, const void *q, const
     a.k_pool_w = fused ? static_cast<uint16_t *>(const_cast<void *>(k_pool)) : nullptr;
     a.v_pool_w = fused ? static_cast<uint16_t *>(const_cast<void *>(v_pool)) : nullptr;
     a.rope_theta = fused ? rope_theta : 0.0;
+    a.violations = violation_word();
 
     const hipError_t e = launch_paged_decode(a, p.num_q_heads / p.num_kv_heads, plan_waves(p),
                                              p.out_dtype == HIPDECODE_F32, static_cast<hipStream_t>(stream), fused);
@@ -384,6 +386,57 @@ HIPDECODE_API hipdecode_status hipdecode_paged_attn_noalloc(const hipdecode_para
         return sst;
     return run_decode(params, q, k_pool, v_pool, block_table, context_lens, out, lse, ws, kNoallocBytes, stream,
                       false, nullptr, nullptr, 0.0, true);
+}
+
+// ---------------------------------------------------------------------------
+// Contract violations.  One flag word per device, in this file-scope device
+// array; host code uses only the address hipGetSymbolAddress gives for the
+// current device, looked up once per device.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint32_t violation_flags[64];
+
+namespace hipdecode {
+namespace {
+
+std::mutex g_violation_mutex;
+std::atomic<uint32_t *> g_violation_ptr[kNoallocMaxDevices];
+
+}  // namespace
+
+uint32_t *violation_word()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kNoallocMaxDevices)
+        return nullptr;
+    uint32_t *w = g_violation_ptr[dev].load(std::memory_order_acquire);
+    if (w != nullptr)
+        return w;
+    std::lock_guard<std::mutex> lock(g_violation_mutex);
+    w = g_violation_ptr[dev].load(std::memory_order_relaxed);
+    if (w == nullptr) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(violation_flags)) != hipSuccess || p == nullptr)
+            return nullptr;
+        w = static_cast<uint32_t *>(p);
+        g_violation_ptr[dev].store(w, std::memory_order_release);
+    }
+    return w;
+}
+
+}  // namespace hipdecode
+
+HIPDECODE_API hipdecode_status hipdecode_contract_violations(uint32_t *flags)
+{
+    if (flags == nullptr)
+        return HIPDECODE_ERR_NULL;
+    uint32_t *w = violation_word();
+    if (w == nullptr)
+        return HIPDECODE_ERR_HIP;
+    const uint32_t zero = 0;
+    if (hipDeviceSynchronize() != hipSuccess || hipMemcpy(flags, w, sizeof(uint32_t), hipMemcpyDeviceToHost) != hipSuccess ||
+        hipMemcpy(w, &zero, sizeof(uint32_t), hipMemcpyHostToDevice) != hipSuccess)
+        return HIPDECODE_ERR_HIP;
+    return HIPDECODE_OK;
 }
 
 HIPDECODE_API const char *hipdecode_status_string(hipdecode_status status)

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "hipdecode.h"
+
 // Exported entry points of the C ABI; everything else has hidden visibility.
 #define HIPDECODE_API extern "C" __attribute__((visibility("default")))
 
@@ -55,7 +57,22 @@ struct DecodeArgs {
     uint16_t *k_pool_w;      // the pools, writable
     uint16_t *v_pool_w;
     double rope_theta;       // > 0: q and the new key are rotated at position ctx - 1
+    uint32_t *violations;    // contract-violation flag word of this device
 };
+
+// The contract-violation flag word of the current device (the
+// HIPDECODE_VIOLATION_* bits), looked up once per device; nullptr if the
+// runtime cannot name it.
+uint32_t *violation_word();
+
+// Sets a contract-violation bit: a device-scope atomic OR through the vector
+// memory path, taken only where a kernel has already found the contract
+// broken.
+__device__ __forceinline__ void report_violation(uint32_t *word, uint32_t bit)
+{
+    if (word != nullptr)
+        __hip_atomic_fetch_or(word, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // waves: 4 or 16 wavefronts per workgroup; fused: the kernel that also
 // appends each request's new token

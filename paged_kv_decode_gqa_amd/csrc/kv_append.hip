@@ -55,6 +55,7 @@ struct AppendArgs {
     int32_t max_new;
     int32_t token_groups;   // workgroups per request: ceil(max_new / tokens per workgroup)
     double theta;
+    uint32_t *violations;   // contract-violation flag word of this device
 };
 
 using rope::bf16x2_t;
@@ -147,8 +148,13 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(AppendArgs a)
     // the host bound, rows outside the inputs) writes nothing at all.  All of
     // this is uniform across the wavefront, and nothing below waits for the
     // other wavefronts, so a wavefront may leave on its own.
-    if (j >= n || n > ctx || n > a.max_new || start < 0 || (int64_t)start + n > a.num_rows)
+    const bool rows_bad = n < 0 || n > max(ctx, 0) || n > a.max_new || start < 0 || (int64_t)start + n > a.num_rows;
+    if (j >= n || rows_bad) {
+        if (lane == 0 && (rows_bad || ctx < 0))
+            report_violation(a.violations, (rows_bad ? HIPDECODE_VIOLATION_ROWS : 0u) |
+                                               (ctx < 0 ? HIPDECODE_VIOLATION_CONTEXT : 0u));
         return;
+    }
     const int pos = ctx - n + j;
     const size_t row = (size_t)start + j;
     const size_t kv_row = (size_t)a.num_kv_heads * kHeadDim;
@@ -191,11 +197,17 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(AppendArgs a)
     }
 
     const int blk = pos / kPageSize;
-    if (blk >= a.max_blocks)
+    if (blk >= a.max_blocks) {
+        if (lane == 0)
+            report_violation(a.violations, HIPDECODE_VIOLATION_CONTEXT);
         return;
+    }
     const int page = a.block_table[(size_t)b * a.max_blocks + blk];
-    if ((unsigned)page >= (unsigned)a.num_pages)
+    if ((unsigned)page >= (unsigned)a.num_pages) {
+        if (lane == 0)
+            report_violation(a.violations, HIPDECODE_VIOLATION_PAGE);
         return;
+    }
     const size_t slot = (size_t)page * kPageSize + pos % kPageSize;
     uint16_t *kd = a.k_pool + slot * kv_row;
     uint16_t *vd = a.v_pool + slot * kv_row;
@@ -332,6 +344,7 @@ HIPDECODE_API hipdecode_status hipdecode_kv_append(const hipdecode_append_params
     a.num_rows = p.num_rows;
     a.max_new = max_new;
     a.theta = p.rope_theta;
+    a.violations = violation_word();
 
     // Few tokens (a decode step): four wavefronts per token, for latency.
     const bool few = (int64_t)p.num_seqs * max_new <= kFewTokens;

@@ -161,13 +161,14 @@ __device__ __forceinline__ void load_q(u32x4 (&qv)[G], const DecodeArgs &a, size
 // from registers; no other workgroup reads that page.  With append_new false
 // (a context length past the host bound, so ctx was clamped and slot ctx - 1
 // holds a real cached token) nothing is written and the page is folded as
-// the pool holds it.
+// the pool holds it.  Returns HIPDECODE_VIOLATION_PAGE if a page id the
+// range uses lies outside the pool (that page was skipped), else 0.
 struct NoHook {
     __device__ __forceinline__ void operator()() const {}
 };
 
 template <int G, int WAVES, bool FUSED = false, class Hook = NoHook>
-__device__ __forceinline__ void fold_range(Stream<G> &st, const DecodeArgs &a, const u32x4 (&qv)[G],
+__device__ __forceinline__ uint32_t fold_range(Stream<G> &st, const DecodeArgs &a, const u32x4 (&qv)[G],
                                            const int32_t *trow, int g, int p_begin, int p_end,
                                            int n_pages, int ctx, int entry, const Lane &ln, int b = 0,
                                            const double2 *angles = nullptr, Hook before_fold = Hook(),
@@ -223,6 +224,8 @@ __device__ __forceinline__ void fold_range(Stream<G> &st, const DecodeArgs &a, c
             fold(ra, i);
         }
     }
+    // pages outside the pool were skipped above
+    uint32_t viol = __ballot(ln.lane < npw && (unsigned)entry >= num_pages) != 0ull ? HIPDECODE_VIOLATION_PAGE : 0u;
     if (tail_partial && ln.wave == WAVES - 1) {
         const int phys = trow[full_end];
         if ((unsigned)phys < num_pages) {
@@ -255,8 +258,11 @@ __device__ __forceinline__ void fold_range(Stream<G> &st, const DecodeArgs &a, c
                 }
             }
             fold_page<G, true>(st, ra, qv, a.scale_log2, full_end * kPageSize + ln.row, ctx);
+        } else {
+            viol = HIPDECODE_VIOLATION_PAGE;
         }
     }
+    return viol;
 }
 
 // The workgroup's streams into LDS (row-groups merged first only with
@@ -531,13 +537,14 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane)
 struct RealUnit {
     int b, split, ctx;
     bool over;   // the request's context length exceeds the host bound (ctx is clamped)
+    bool bad;    // the request's context length is negative or exceeds the host bound
 };
 
 __device__ __forceinline__ RealUnit real_unit(const DecodeArgs &a, int u)
 {
     const int lane = (int)(threadIdx.x & 63);
     const int span = kPageSize * a.partition_pages;
-    RealUnit r{-1, 0, 0, false};
+    RealUnit r{-1, 0, 0, false, false};
     int carry = 0;
     for (int c0 = 0; c0 < a.num_seqs; c0 += 64) {
         const int j = c0 + lane;
@@ -552,7 +559,9 @@ __device__ __forceinline__ RealUnit real_unit(const DecodeArgs &a, int u)
             r.b = c0 + l;
             r.split = u - carry - __builtin_amdgcn_readlane(excl, l);
             r.ctx = __builtin_amdgcn_readlane(cj, l);
-            r.over = __builtin_amdgcn_readlane(raw, l) > a.max_context_len;
+            const int raw_l = __builtin_amdgcn_readlane(raw, l);
+            r.over = raw_l > a.max_context_len;
+            r.bad = raw_l < 0 || r.over;
             break;
         }
         carry += __builtin_amdgcn_readlane(incl, 63);
@@ -603,6 +612,9 @@ void paged_decode_kernel(DecodeArgs a)
 
     int b, split, ctx, spec_entry;
     [[maybe_unused]] bool over;   // context length past the host bound: the fused kernel appends nothing
+    // Contract violations met here, reported once no load of the call is in
+    // flight, so that the branch leaves the waits on the main path alone.
+    uint32_t viol = 0;
     if (a.num_seqs == 1 || a.nsplit_max == 1) {
         // Every unit of the full grid up to a request's partition count is real.
         b = b_full;
@@ -610,6 +622,8 @@ void paged_decode_kernel(DecodeArgs a)
         const int raw = a.context_lens[b];
         ctx = clamp_ctx(raw, a.max_context_len);
         over = raw > a.max_context_len;
+        if (split == 0 && (raw < 0 || over))
+            viol = HIPDECODE_VIOLATION_CONTEXT;
         spec_entry = spec_full;
         const int nsplit_b = (ctx + kPageSize * pp - 1) / (kPageSize * pp);
         if (ctx == 0 ? split != 0 : split >= nsplit_b)
@@ -623,6 +637,8 @@ void paged_decode_kernel(DecodeArgs a)
         split = u.split;
         ctx = u.ctx;
         over = u.over;
+        if (split == 0 && u.bad)
+            viol = HIPDECODE_VIOLATION_CONTEXT;
         spec_entry = spec_full;
         if (b != b_full || split != split_full) {   // ragged batch: fetch this partition's entries
             const int idx = split * pp + ln.wave + WAVES * ln.lane;
@@ -638,6 +654,8 @@ void paged_decode_kernel(DecodeArgs a)
 
     if (ctx == 0) {
         write_empty<OUT_F32>(a, row0, G, ln.tid, 64 * WAVES);
+        if (viol != 0 && ln.tid == 0)
+            report_violation(a.violations, viol);
         return;
     }
 
@@ -677,11 +695,14 @@ void paged_decode_kernel(DecodeArgs a)
     Stream<G> st;
     st.init();
     if constexpr (FUSED)
-        fold_range<G, WAVES, FUSED>(st, a, qv, trow, g, p_begin, min(p_begin + a.partition_pages, n_pages),
-                                    n_pages, ctx, spec_entry, ln, b, rope_on ? angles : nullptr, rotate_q, !over);
+        viol |= fold_range<G, WAVES, FUSED>(st, a, qv, trow, g, p_begin, min(p_begin + a.partition_pages, n_pages),
+                                            n_pages, ctx, spec_entry, ln, b, rope_on ? angles : nullptr, rotate_q,
+                                            !over);
     else
-        fold_range<G, WAVES, FUSED>(st, a, qv, trow, g, p_begin, min(p_begin + a.partition_pages, n_pages),
-                                    n_pages, ctx, spec_entry, ln, b);
+        viol |= fold_range<G, WAVES, FUSED>(st, a, qv, trow, g, p_begin, min(p_begin + a.partition_pages, n_pages),
+                                            n_pages, ctx, spec_entry, ln, b);
+    if (viol != 0 && ln.lane == 0)
+        report_violation(a.violations, viol);
     publish_streams<G, WAVES>(st, sm, ln);
     __syncthreads();
 

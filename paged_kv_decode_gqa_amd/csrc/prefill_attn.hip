@@ -85,6 +85,7 @@ struct PrefillArgs {
     int32_t pairs;          // workgroups (pairs of half-tiles) per request and KV head
     float scale_log2;       // max(|scale| * log2(e), 2^-100): positive, see the launch
     uint32_t q_sign;        // 0x80008000 when scale < 0: q is negated on load instead
+    uint32_t *violations;   // contract-violation flag word of this device
 };
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
@@ -195,9 +196,14 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
     const int n = a.new_start[b + 1] - start;
     // Uniform across the workgroup: a request that breaks the contract, or a
     // pair past its chunk, does nothing.
-    if (n <= 0 || n > ctx || n > a.max_new || start < 0 || (int64_t)start + n > a.num_rows ||
-        (int64_t)ctx > (int64_t)a.max_blocks * kPageSize)
+    const bool rows_bad = n < 0 || n > max(ctx, 0) || n > a.max_new || start < 0 || (int64_t)start + n > a.num_rows;
+    const bool ctx_bad = ctx < 0 || (int64_t)ctx > (int64_t)a.max_blocks * kPageSize;
+    if (n <= 0 || rows_bad || ctx_bad) {
+        if (threadIdx.x == 0 && (rows_bad || ctx_bad))
+            report_violation(a.violations, (rows_bad ? HIPDECODE_VIOLATION_ROWS : 0u) |
+                                               (ctx_bad ? HIPDECODE_VIOLATION_CONTEXT : 0u));
         return;
+    }
     const int halves = (n + kHalfTokens - 1) / kHalfTokens;
     if (pair >= (halves + 1) / 2)
         return;
@@ -274,8 +280,8 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
     auto issue = [&](int kb, int stage) __attribute__((always_inline)) {
         const int key_w = kb * kKeys + 8 * w;                // first of this wavefront's eight keys
         const int pidx = min(key_w, kv_end - 1) / kPageSize;
-        int page = scalar_load(table + pidx);
-        page = (unsigned)page < (unsigned)a.num_pages ? page : 0;
+        const int raw_page = scalar_load(table + pidx);
+        const int page = (unsigned)raw_page < (unsigned)a.num_pages ? raw_page : 0;
         const size_t pbase = (size_t)page * page_bytes;
         const bool full = key_w + 8 <= kv_end;   // uniform
 #pragma unroll
@@ -492,6 +498,17 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
     issue(0, 0);
     if (nblk > 1)
         issue(1, 1);
+    // Page ids outside the pool are read as page 0 above; they are found here
+    // once, from the workgroup's table entries, while the first copies fly,
+    // and reported at the end.
+    bool bad_page;
+    {
+        const int npages = (kv_end + kPageSize - 1) / kPageSize;
+        bool bad = false;
+        for (int i = tid; i < npages; i += kPfThreads)
+            bad |= (unsigned)table[i] >= (unsigned)a.num_pages;
+        bad_page = __ballot(bad) != 0ull;
+    }
     wait_vm<0>();   // q and the first copies: nothing older than a step's copies stays in flight in the loop
     int stage = 0;
     auto sync_step = [&](int kb) __attribute__((always_inline)) {
@@ -626,6 +643,8 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
     }
     if (upper)
         write_rows();
+    if (bad_page && lane == 0)
+        report_violation(a.violations, HIPDECODE_VIOLATION_PAGE);
 }
 
 hipdecode_status check_prefill(const hipdecode_prefill_params *pp)
@@ -717,6 +736,7 @@ HIPDECODE_API hipdecode_status hipdecode_prefill_attn(const hipdecode_prefill_pa
     // far below 2^70), so scale 0 still gives the mean of V and ln(n).
     a.scale_log2 = fmaxf(fabsf(p.scale) * 1.44269504088896340736f, 0x1p-100f);
     a.q_sign = p.scale < 0.f ? 0x80008000u : 0u;
+    a.violations = violation_word();
     const unsigned grid = (unsigned)((int64_t)p.num_seqs * a.pairs * p.num_kv_heads);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool f32 = p.out_dtype == HIPDECODE_F32;

@@ -453,3 +453,16 @@ def test_fused_call_rejects_before_any_launch():
                 fake, fake, ws, None) == hd.HIPDECODE_ERR_ALIGN
     assert call(ctypes.byref(base(num_seqs=0)), 1e6, None, None, None, None, None, None, None, None, None, None, 0,
                 None) == hd.HIPDECODE_OK
+
+
+def test_header_constants_match_the_binding():
+    text = open(HEADER).read()
+    defines = {k: v for k, v in re.findall(r"#define (HIPDECODE_\w+) \(?\(?(?:size_t\))?\s*([0-9]+)u?", text)}
+    for name in ("HIPDECODE_VIOLATION_CONTEXT", "HIPDECODE_VIOLATION_PAGE", "HIPDECODE_VIOLATION_ROWS"):
+        assert int(defines[name]) == getattr(hd, name), name
+    bits = [hd.HIPDECODE_VIOLATION_CONTEXT, hd.HIPDECODE_VIOLATION_PAGE, hd.HIPDECODE_VIOLATION_ROWS]
+    assert sorted(bits) == [1, 2, 4]
+
+
+def test_contract_violations_rejects_null_before_any_hip_call():
+    assert hd.library().hipdecode_contract_violations(None) == hd.HIPDECODE_ERR_NULL

@@ -162,7 +162,12 @@ def test_append_skips_what_breaks_the_contract():
     ctx_bad = case.context_lens.copy()
     ctx_bad[3] = 3                                       # request 3: 5 new tokens, context 3
     broken = replace(case, block_table=bad, context_lens=ctx_bad)
+    hd.hipdecode_contract_violations()   # clear what earlier calls left
+    run_gpu_append(case, inputs)
+    assert hd.hipdecode_contract_violations() == 0, "a call within the contract reported a violation"
     gk, gv, gq = run_gpu_append(broken, inputs)
+    # an unmapped block and a page outside the pool, and more new tokens than the context
+    assert hd.hipdecode_contract_violations() == hd.HIPDECODE_VIOLATION_PAGE | hd.HIPDECODE_VIOLATION_ROWS
     # expected: only requests 0 and 4, appended one at a time by the oracle
     ek, ev, eq = case.k_pool, case.v_pool, inputs.q
     for b in (0, 4):

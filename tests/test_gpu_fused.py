@@ -97,9 +97,11 @@ def test_fused_context_past_bound_writes_nothing(theta):
     dc = DeviceCase(case)
     bound = 800                     # request 1 (1000 tokens) is past it
     k_before, v_before = to_bits(dc.k).copy(), to_bits(dc.v).copy()
+    hd.hipdecode_contract_violations()   # clear what earlier calls left
     hd.paged_attn_append(bits_to_bf16(inputs.q), bits_to_bf16(inputs.k_new), bits_to_bf16(inputs.v_new), dc.k, dc.v,
                          dc.table, dc.ctx, case.scale, max_context_len=bound, rope_theta=theta)
     torch.cuda.synchronize()
+    assert hd.hipdecode_contract_violations() == hd.HIPDECODE_VIOLATION_CONTEXT
     gk, gv = to_bits(dc.k), to_bits(dc.v)
     pages_1 = {int(p) for p in case.block_table[1, :(1000 + 15) // 16]}
     for p in pages_1:

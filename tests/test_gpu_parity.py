@@ -283,6 +283,58 @@ def test_maximum_split_count():
     _check(case, "1024 splits", partition_tokens=64)
 
 
+def _violations():
+    return hd.hipdecode_contract_violations()
+
+
+@pytest.mark.parametrize("ctx", [[3000, 1201, 700], [3001]], ids=["batch", "single"])
+def test_contract_violations_are_reported(ctx):
+    """Device-side contents that break the contract are clamped or skipped,
+    and reported: a clean call leaves the flags at 0; a context length past
+    the bound, a negative one, and a page id outside the pool (in a full page
+    and in the partly filled last page) each set their bit; the requests that
+    keep the contract still match the oracle."""
+    case = make_case(ctx, seed=47, pool_pages=sum((n + 15) // 16 for n in ctx) + 9)
+    ref_out, ref_lse = oracle.run_case(case)
+    dc = DeviceCase(case)
+    _violations()   # clear what earlier calls left
+    log(f"[parity] contract violations, {len(ctx)} requests: clean call")
+    out, lse = run_hip(dc)
+    compare(out, lse, ref_out, ref_lse, what="clean")
+    assert _violations() == 0
+
+    log("[parity] contract violations: context past the bound")
+    run_hip(dc, max_context_len=2000)
+    assert _violations() == hd.HIPDECODE_VIOLATION_CONTEXT
+
+    bad_b = len(ctx) - 1
+    keep = [b for b in range(len(ctx)) if b != bad_b]
+    ctx_neg = case.context_lens.copy()
+    ctx_neg[bad_b] = -5
+    dc.ctx = torch.from_numpy(ctx_neg).cuda()
+    log("[parity] contract violations: negative context length")
+    out, lse = run_hip(dc)
+    assert _violations() == hd.HIPDECODE_VIOLATION_CONTEXT
+    if keep:
+        compare(out[keep], lse[keep], ref_out[keep], ref_lse[keep], what="negative length beside")
+    dc.ctx = torch.from_numpy(case.context_lens).cuda()
+
+    b = 1 if len(ctx) > 1 else 0
+    others = [x for x in range(len(ctx)) if x != b]
+    for blk in (10, (ctx[b] - 1) // 16):   # a full page, then the partly filled last page
+        bad = case.block_table.copy()
+        bad[b, blk] = case.num_pages + 5
+        dc.table = torch.from_numpy(bad).cuda()
+        log(f"[parity] contract violations: page outside the pool at block {blk}")
+        out, lse = run_hip(dc)
+        assert _violations() == hd.HIPDECODE_VIOLATION_PAGE
+        if others:
+            compare(out[others], lse[others], ref_out[others], ref_lse[others], what="bad page beside")
+    dc.table = torch.from_numpy(case.block_table).cuda()
+    out, lse = run_hip(dc)
+    assert _violations() == 0
+
+
 WORK_LIST_CASES = {
     # more requests than one wavefront's lanes, so the unit scan runs over several chunks
     "65 mixed with empties": [0 if i % 9 == 4 else int(x) for i, x in

@@ -235,7 +235,11 @@ def test_prefill_skips_what_breaks_the_contract():
     ctx_bad = case.context_lens.copy()
     ctx_bad[1] = 5                                   # 10 chunk tokens, context 5
     broken = replace(case, context_lens=ctx_bad)
+    hd.hipdecode_contract_violations()   # clear what earlier calls left
+    run_gpu(case, inp)
+    assert hd.hipdecode_contract_violations() == 0, "a call within the contract reported a violation"
     o, l = run_gpu(broken, inp)
+    assert hd.hipdecode_contract_violations() == hd.HIPDECODE_VIOLATION_ROWS
     ok_rows = np.r_[0:20, 30:70]
     ref_o, ref_l = oracle.prefill_attn(inp.q, case.k_pool, case.v_pool, case.block_table, case.context_lens,
                                        inp.new_start, case.scale)
