@@ -381,9 +381,11 @@ __device__ __forceinline__ void load_dims(float (&v)[K], const float *p)
 // workgroup has more threads than dims, the threads of a dim split the
 // partials into S sets and add their sums through LDS at the end.  Every
 // wavefront finds its head's maximum and sum itself, lane j weighing
-// partials j, j + 64, ..., so the weights reach the sums as scalars and no
-// workgroup barrier separates the loads from the sums.  A thread's first
-// PRE partials are loaded in one batch right after the (m, l) pairs.
+// partials j, j + 64, ... (one round of 64 at a time), so the weights reach
+// the sums as scalars and no workgroup barrier separates the loads from the
+// sums.  A thread's first PRE partials are loaded in one batch right after
+// the (m, l) pairs; the rest go in batches of NB, each batch's loads issued
+// before any of them is used, so that each batch costs one memory round trip.
 template <int G, int WAVES, int PRE, bool OUT_F32, class PartIndex>
 __device__ __forceinline__ void merge_partials_pre(const DecodeArgs &a, Smem<G, WAVES> &sm, size_t row0,
                                                    int count, PartIndex part_index, const Lane &ln)
@@ -393,6 +395,8 @@ __device__ __forceinline__ void merge_partials_pre(const DecodeArgs &a, Smem<G, 
     constexpr int K = D > NT ? D / NT : 1;          // dims per thread
     constexpr int S = NT > D ? NT / D : 1;          // sets of partials
     constexpr int TPS = D / K;                      // threads per set
+    constexpr int NB = 32 / K;                      // partials per batch after the first
+    constexpr int kRounds = kMaxMergeSplits / 64;   // rounds of 64 (m, l) pairs at most
     static_assert(K <= 2 && TPS % 64 == 0, "whole wavefronts per set and head");
     const int t = ln.tid % TPS;
     const int set = __builtin_amdgcn_readfirstlane(ln.tid / TPS);
@@ -400,10 +404,33 @@ __device__ __forceinline__ void merge_partials_pre(const DecodeArgs &a, Smem<G, 
     const int d = (t * K) % kHeadDim;
     const float *acc_base = a.part_acc + d;
     auto acc_ptr = [&](int i) { return acc_base + part_index(i, h) * kHeadDim; };
+    auto ml_of = [&](int i) { return coherent_load8(a.part_ml + part_index(min(i, count - 1), h) * 2); };
+    float A[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+        A[k] = 0.f;
+    // partials [i_begin, i_end) of this set, i = set (mod S), weights w of the round starting at c0
+    auto add_batches = [&](int i_begin, int i_end, float w, int c0) {
+        for (int i0 = i_begin; i0 < i_end; i0 += NB * S) {
+            float v[NB][K];
+#pragma unroll
+            for (int r = 0; r < NB; ++r)
+                load_dims<K>(v[r], acc_ptr(min(i0 + r * S, count - 1)));
+#pragma unroll
+            for (int r = 0; r < NB; ++r) {
+                const int i = i0 + r * S;
+                if (i < i_end) {
+                    const float wi = lane_value(w, i - c0);
+#pragma unroll
+                    for (int k = 0; k < K; ++k)
+                        A[k] = fmaf(wi, v[r][k], A[k]);
+                }
+            }
+        }
+    };
 
-    // (m, l) of partials lane, lane + 64, ... : the first 64 stay in registers
-    const int i0 = min(ln.lane, count - 1);
-    const uint64_t ml0 = coherent_load8(a.part_ml + part_index(i0, h) * 2);
+    // round 0: (m, l) of partial `lane`, then this set's first PRE partials
+    const uint64_t ml0 = ml_of(ln.lane);
     float pre[PRE][K];
 #pragma unroll
     for (int r = 0; r < PRE; ++r)
@@ -411,19 +438,21 @@ __device__ __forceinline__ void merge_partials_pre(const DecodeArgs &a, Smem<G, 
     const float m0 = ln.lane < count ? __uint_as_float((uint32_t)ml0) : -INFINITY;
     const float l0 = ln.lane < count ? __uint_as_float((uint32_t)(ml0 >> 32)) : 0.f;
     float mx = m0;
-    for (int c0 = 64; c0 < count; c0 += 64) {
-        const int i = c0 + ln.lane;
-        if (i < count)
-            mx = fmaxf(mx, __uint_as_float((uint32_t)coherent_load8(a.part_ml + part_index(i, h) * 2)));
+    if (count > 64) {
+        // the maxima of the later rounds, in one batch (indices past the end clamped, values dropped)
+        uint64_t mlr[kRounds - 1];
+#pragma unroll
+        for (int c = 1; c < kRounds; ++c)
+            mlr[c - 1] = ml_of(64 * c + ln.lane);
+#pragma unroll
+        for (int c = 1; c < kRounds; ++c)
+            if (64 * c + ln.lane < count)
+                mx = fmaxf(mx, __uint_as_float((uint32_t)mlr[c - 1]));
     }
     const float M = wave_max(mx);
     const float M_use = (M == -INFINITY) ? 0.f : M;
     const float w0 = merge_weight(m0, M_use);
     float lsum = l0 * w0;
-    float A[K];
-#pragma unroll
-    for (int k = 0; k < K; ++k)
-        A[k] = 0.f;
     const int n0 = min(count, 64);
 #pragma unroll
     for (int r = 0; r < PRE; ++r) {
@@ -435,28 +464,13 @@ __device__ __forceinline__ void merge_partials_pre(const DecodeArgs &a, Smem<G, 
                 A[k] = fmaf(wi, pre[r][k], A[k]);
         }
     }
-    for (int i = set + PRE * S; i < n0; i += S) {
-        float v[K];
-        load_dims<K>(v, acc_ptr(i));
-        const float wi = lane_value(w0, i);
-#pragma unroll
-        for (int k = 0; k < K; ++k)
-            A[k] = fmaf(wi, v[k], A[k]);
-    }
-    for (int c0 = 64; c0 < count; c0 += 64) {   // partials past the first 64
+    add_batches(set + PRE * S, n0, w0, 0);
+    for (int c0 = 64; c0 < count; c0 += 64) {   // the later rounds of 64 partials
         const int j = c0 + ln.lane;
-        const uint64_t ml = coherent_load8(a.part_ml + part_index(min(j, count - 1), h) * 2);
+        const uint64_t ml = ml_of(j);
         const float wj = j < count ? merge_weight(__uint_as_float((uint32_t)ml), M_use) : 0.f;
         lsum = fmaf(j < count ? __uint_as_float((uint32_t)(ml >> 32)) : 0.f, wj, lsum);
-        const int first = c0 + (set - c0 % S + S) % S;   // the set's first partial of this chunk
-        for (int i = first; i < min(count, c0 + 64); i += S) {
-            float v[K];
-            load_dims<K>(v, acc_ptr(i));
-            const float wi = lane_value(wj, i - c0);
-#pragma unroll
-            for (int k = 0; k < K; ++k)
-                A[k] = fmaf(wi, v[k], A[k]);
-        }
+        add_batches(c0 + (set - c0 % S + S) % S, min(count, c0 + 64), wj, c0);
     }
     const float L = wave_sum(lsum);
     if constexpr (S > 1) {
