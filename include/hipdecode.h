@@ -30,6 +30,11 @@
  *   workspace     hipdecode_workspace_bytes(params) bytes, zero-filled before
  *                 its first use (hipdecode_workspace_init or any zero fill);
  *                 every completed call leaves its counters at zero again.
+ *                 The counters lead the workspace (num_seqs * num_kv_heads *
+ *                 256 bytes) and the split partials follow them, so calls
+ *                 that share a workspace must have the same num_seqs *
+ *                 num_kv_heads; zero-fill it again before a call that
+ *                 changes that product.
  * q, k_pool, v_pool, out and workspace must be 16-byte aligned; all of them are
  * device memory.  Supported shapes: head_dim 128, page size 16, G in {1, 2, 4}
  * (16-wavefront workgroups for G <= 2 only).
@@ -322,8 +327,9 @@ hipdecode_status hipdecode_prefill_attn(const hipdecode_prefill_params *params,
  * block_table [max_bucket][max_blocks_per_seq] and context_lens [max_bucket]
  * int32, device memory.  The caller updates q, k_new, v_new and block_table
  * between steps with work ordered on the same stream.  The runner allocates
- * its attention workspace, two pinned staging buffers, two events, a capture
- * stream and the graphs, and frees them in hipdecode_step_runner_destroy.
+ * an attention workspace with one slice per bucket, two pinned staging
+ * buffers, two events, a capture stream and the graphs, and frees them in
+ * hipdecode_step_runner_destroy.
  * A runner is used from one thread, its steps on one stream.
  * ------------------------------------------------------------------------ */
 

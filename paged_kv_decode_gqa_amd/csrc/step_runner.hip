@@ -32,8 +32,9 @@ struct hipdecode_step_runner {
     int32_t *block_table;
     int32_t *context_lens;
     // owned resources
-    void *workspace;
+    void *workspace;              // one slice per bucket, at ws_offset[log2(bucket)]
     size_t workspace_bytes;
+    size_t ws_offset[33];         // slice k spans [ws_offset[k], ws_offset[k + 1])
     int32_t *staging[2];          // pinned, max_bucket int32 each
     hipEvent_t staged[2];         // recorded after the copy out of staging[i]
     bool staged_pending[2];
@@ -154,14 +155,16 @@ void release(hipdecode_step_runner *r)
 hipdecode_status capture(hipdecode_step_runner *r, int32_t bucket, hipGraphExec_t *exec)
 {
     const hipdecode_params p = attn_params(r->cfg, bucket);
+    const int32_t k = log2_of(bucket);
+    void *ws = static_cast<uint8_t *>(r->workspace) + r->ws_offset[k];
+    const size_t ws_bytes = r->ws_offset[k + 1] - r->ws_offset[k];
     if (hipStreamBeginCapture(r->capture, hipStreamCaptureModeThreadLocal) != hipSuccess)
         return HIPDECODE_ERR_HIP;
     hipdecode_status st = HIPDECODE_OK;
     for (int32_t l = 0; l < r->cfg.num_layers && st == HIPDECODE_OK; ++l)
         st = hipdecode_paged_attn_append(&p, r->cfg.rope_theta, r->q[l], r->k_new[l], r->v_new[l], r->k_pool[l],
                                          r->v_pool[l], r->block_table, r->context_lens, r->out[l],
-                                         r->lse != nullptr ? r->lse[l] : nullptr, r->workspace, r->workspace_bytes,
-                                         r->capture);
+                                         r->lse != nullptr ? r->lse[l] : nullptr, ws, ws_bytes, r->capture);
     hipGraph_t graph = nullptr;
     const hipError_t end = hipStreamEndCapture(r->capture, &graph);
     if (st != HIPDECODE_OK || end != hipSuccess || graph == nullptr) {
@@ -225,14 +228,19 @@ HIPDECODE_API hipdecode_status hipdecode_step_runner_create(const hipdecode_step
     r->block_table = buffers->block_table;
     r->context_lens = buffers->context_lens;
 
-    // one workspace, large enough for the biggest bucket's plan (calls are ordered)
+    // One slice of the workspace per bucket.  A workspace keeps its arrival
+    // counters at zero between calls only for calls of one layout (the
+    // counters lead it, sized by the batch), so buckets must not share one:
+    // a smaller bucket's partials would land on a larger one's counters.
     size_t ws = 0;
-    for (int32_t b = 1; b <= r->max_bucket; b <<= 1) {
-        const hipdecode_params p = attn_params(r->cfg, b);
+    for (int32_t k = 0; k < r->num_buckets; ++k) {
+        const hipdecode_params p = attn_params(r->cfg, (int32_t)1 << k);
         const size_t need = hipdecode_workspace_bytes(&p);
-        ws = need > ws ? need : ws;
+        r->ws_offset[k] = ws;
+        ws += (need < 256 ? 256 : need + 255) & ~(size_t)255;
     }
-    r->workspace_bytes = ws < 256 ? 256 : ws;
+    r->ws_offset[r->num_buckets] = ws;
+    r->workspace_bytes = ws;
     bool ok = hipStreamCreateWithFlags(&r->capture, hipStreamNonBlocking) == hipSuccess &&
               hipMalloc(&r->workspace, r->workspace_bytes) == hipSuccess;
     for (int i = 0; i < 2 && ok; ++i)

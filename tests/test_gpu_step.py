@@ -33,11 +33,12 @@ def rows_bits(rng, shape):
 class Setup:
     """Per-layer pools and step buffers for ``bucket`` rows."""
 
-    def __init__(self, final_ctx, layers, max_seqs, seed):
+    def __init__(self, final_ctx, layers, max_seqs, seed, Hq=16, Hkv=8):
         self.max_seqs = max_seqs
         self.bucket = hd.hipdecode_step_bucket(max_seqs, max_seqs)
         ctx_rows = list(final_ctx) + [0] * (self.bucket - len(final_ctx))
-        self.cases = [make_case(ctx_rows, seed=seed + 10 * l, pool_pages=sum((c + 15) // 16 for c in ctx_rows) + 4)
+        self.cases = [make_case(ctx_rows, seed=seed + 10 * l, Hq=Hq, Hkv=Hkv,
+                                pool_pages=sum((c + 15) // 16 for c in ctx_rows) + 4)
                       for l in range(layers)]
         # every layer shares one table: same pages per request, different pools
         self.table = self.cases[0].block_table
@@ -99,14 +100,28 @@ def test_step_runner_one_step_with_padding():
 def test_step_runner_pipelined_steps():
     """Five steps, batch 3, 3, 5, 1, 12 (buckets 4, 4, 8, 1, 16), enqueued
     back to back with their inputs copied in on the stream."""
-    base = [700, 33, 1500, 16, 90, 1, 250, 64, 511, 1024, 7, 300]
-    batches = [3, 3, 5, 1, 12]
+    run_pipelined([700, 33, 1500, 16, 90, 1, 250, 64, 511, 1024, 7, 300], [3, 3, 5, 1, 12], max_seqs=12, seed=63)
+
+
+@pytest.mark.parametrize("hq,hkv", [(16, 8), (16, 4)])
+def test_step_runner_long_contexts_split(hq, hkv):
+    """Long contexts in small buckets: the planner splits every request over
+    many partitions, so each replayed layer runs the cross-workgroup merge
+    (tickets and partials shared by the layers' launches) inside the graph."""
+    base = [9000, 4000]
+    params = hd.make_params(num_seqs=2, num_q_heads=hq, num_kv_heads=hkv, num_pages=1000, max_blocks_per_seq=600,
+                            max_context_len=9004, scale=0.088)
+    assert hd.hipdecode_partition_tokens(params) < 4000, "the requests must be split"
+    run_pipelined(base, [2, 1, 2, 2], max_seqs=2, seed=65, Hq=hq, Hkv=hkv)
+
+
+def run_pipelined(base, batches, *, max_seqs, seed, Hq=16, Hkv=8):
     final = list(base)
     for B in batches:
         for b in range(B):
             final[b] += 1
-    s = Setup(final, layers=2, max_seqs=12, seed=63)
-    rng = np.random.default_rng(64)
+    s = Setup(final, layers=2, max_seqs=max_seqs, seed=seed, Hq=Hq, Hkv=Hkv)
+    rng = np.random.default_rng(seed + 1)
     grown = list(base)
     plan = []
     for B in batches:
