@@ -283,6 +283,28 @@ def test_maximum_split_count():
     _check(case, "1024 splits", partition_tokens=64)
 
 
+@pytest.mark.parametrize("ctx,partition", [([3000, 700], 0), ([300, 200, 17], 4096)], ids=["split", "unsplit"])
+def test_without_lse(ctx, partition):
+    """lse may be NULL: out is then bit-identical to the call that writes lse,
+    through the workspace and the allocation-free entry points alike."""
+    case = make_case(ctx, seed=48)
+    dc = DeviceCase(case)
+    p = hd.make_params(num_seqs=case.B, num_q_heads=16, num_kv_heads=8, num_pages=case.num_pages,
+                       max_blocks_per_seq=case.max_blocks, max_context_len=case.max_context_len, scale=case.scale,
+                       partition_tokens=partition)
+    ws = torch.zeros(hd.hipdecode_workspace_bytes(p) // 4 + 4, dtype=torch.int32, device="cuda")
+    outs = [torch.empty((case.B, 16, 128), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+    lse = torch.empty((case.B, 16), dtype=torch.float32, device="cuda")
+    log(f"[parity] without lse, {len(ctx)} requests, partition {partition}")
+    hd.hipdecode_paged_attn(p, dc.q, dc.k, dc.v, dc.table, dc.ctx, outs[0], lse, ws)
+    hd.hipdecode_paged_attn(p, dc.q, dc.k, dc.v, dc.table, dc.ctx, outs[1], None, ws)
+    hd.hipdecode_paged_attn_noalloc(p, dc.q, dc.k, dc.v, dc.table, dc.ctx, outs[2], None)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    ref_out, ref_lse = oracle.run_case(case)
+    compare(outs[0], lse, ref_out, ref_lse, what="with lse")
+
+
 def _violations():
     return hd.hipdecode_contract_violations()
 

@@ -230,6 +230,23 @@ def test_prefill_last_rows_match_decode_kernel():
     assert np.all(np.abs(l[last] - d_l) <= 2 * LSE_RTOL * np.maximum(1.0, np.abs(d_l)))
 
 
+def test_prefill_without_lse():
+    """lse may be NULL: out is then bit-identical to the call that writes lse."""
+    case, inp = make_prefill_case([900, 300], [300, 100], seed=49)
+    dc = DeviceCase(case)
+    q = bits_to_bf16(inp.q)
+    p = hd.make_prefill_params(num_seqs=case.B, num_q_heads=case.Hq, num_kv_heads=case.Hkv,
+                               num_pages=case.num_pages, max_blocks_per_seq=case.max_blocks,
+                               num_rows=q.shape[0], max_new_tokens=inp.max_new_tokens, scale=case.scale)
+    starts = i32(inp.new_start)
+    outs = [torch.empty((q.shape[0], case.Hq, case.D), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    lse = torch.empty((q.shape[0], case.Hq), dtype=torch.float32, device="cuda")
+    hd.hipdecode_prefill_attn(p, q, dc.k, dc.v, starts, dc.table, dc.ctx, outs[0], lse)
+    hd.hipdecode_prefill_attn(p, q, dc.k, dc.v, starts, dc.table, dc.ctx, outs[1], None)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+
+
 def test_prefill_skips_what_breaks_the_contract():
     case, inp = make_prefill_case([100, 50, 40], [20, 10, 40], seed=46)
     ctx_bad = case.context_lens.copy()
