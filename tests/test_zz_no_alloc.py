@@ -88,3 +88,51 @@ def test_noalloc_refuses_past_its_limits():
         hd.hipdecode_paged_attn_noalloc(p, dc.q, dc.k, dc.v, dc.table, dc.ctx, out, lse)
     assert ei.value.status == hd.HIPDECODE_ERR_WORKSPACE
     log("[noalloc] calls past the static scratch refused")
+
+
+def test_noalloc_graph_replays_between_other_calls():
+    """The allocation-free call captured in a HIP graph and replayed three times
+    with new context lengths, an eager allocation-free call of another shape
+    between the replays (it shares the static array); every replay bit-equal to
+    the same call made eagerly, and within the decode bars of the oracle."""
+    case = make_case([9000, 9000, 9000], seed=94, pool_pages=1800)
+    other = make_case([5000, 300, 12000, 64, 7000], seed=95, pool_pages=1600)
+    dc, do = DeviceCase(case), DeviceCase(other)
+    p = params_of(case, 9000)
+    po = params_of(other, other.max_context_len)
+    out = torch.empty((case.B, case.Hq, case.D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((case.B, case.Hq), dtype=torch.float32, device="cuda")
+    ctx_dev = dc.ctx.clone()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):   # warm-up outside the graph
+        hd.hipdecode_paged_attn_noalloc(p, dc.q, dc.k, dc.v, dc.table, ctx_dev, out, lse)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        hd.hipdecode_paged_attn_noalloc(p, dc.q, dc.k, dc.v, dc.table, ctx_dev, out, lse)
+    torch.cuda.synchronize()
+    o_other = torch.empty((other.B, other.Hq, other.D), dtype=torch.bfloat16, device="cuda")
+    l_other = torch.empty((other.B, other.Hq), dtype=torch.float32, device="cuda")
+    ref_other = oracle.run_case(other)
+    for it, lens in enumerate([[4000, 9000, 100], [8191, 17, 0], [9000, 2500, 4096]]):
+        log(f"[noalloc] graph replay {it}: {lens}")
+        ctx_dev.copy_(torch.tensor(lens, dtype=torch.int32))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref_case = make_case([9000, 9000, 9000], seed=94, pool_pages=1800)
+        ref_case.context_lens = np.array(lens, dtype=np.int32)
+        ref_out, ref_lse = oracle.run_case(ref_case)
+        compare(out, lse, ref_out, ref_lse, what=f"noalloc graph replay {it}")
+        eager_out = torch.empty_like(out)
+        eager_lse = torch.empty_like(lse)
+        hd.hipdecode_paged_attn_noalloc(p, dc.q, dc.k, dc.v, dc.table, ctx_dev, eager_out, eager_lse)
+        torch.cuda.synchronize()
+        assert torch.equal(eager_out, out) and torch.equal(eager_lse, lse), "replay differs from eager"
+        # another shape on the same static array between the replays
+        hd.hipdecode_paged_attn_noalloc(po, do.q, do.k, do.v, do.table, do.ctx, o_other, l_other)
+        torch.cuda.synchronize()
+        compare(o_other, l_other, *ref_other, what=f"noalloc other shape after replay {it}")
