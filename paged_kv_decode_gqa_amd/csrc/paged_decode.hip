@@ -9,9 +9,9 @@
 //
 // One workgroup per (request b, KV head g, partition of the context).  The
 // grid is sized by the host's max_context_len.  In a ragged batch the
-// workgroups map onto the real (request, partition) units in order, so the
-// slots past the last one, not slots scattered through the grid, are the
-// ones that exit at once.
+// workgroups map onto the real (request, partition) units, full partitions
+// first, so the slots past the last one, not slots scattered through the
+// grid, are the ones that exit at once.
 //
 // Inside a workgroup the wavefronts take pages round-robin, each with one page
 // in flight while it folds the previous one; their streams are merged with
@@ -542,12 +542,16 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane)
     return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
 }
 
-// The work list.  The grid has a slot for every partition
-// the longest context could need, but a ragged batch has far fewer real
-// (request, partition) units.  Unit u is the u-th real unit in request order,
-// partitions ascending; an empty request counts one unit, which writes its
-// empty output.  Slots past the last real unit get b = -1 and exit, so every
-// workgroup the dispatcher places early carries work.
+// The work list.  The grid has a slot for every partition the longest
+// context could need, but a ragged batch has far fewer real (request,
+// partition) units.  Unit u is the u-th real unit: first every full
+// partition, in request order, partitions ascending; then each request's
+// partly filled last partition, in request order (an empty request counts
+// one such unit, which writes its empty output).  Slots past the last real
+// unit get b = -1 and exit, so every workgroup the dispatcher places early
+// carries work, and the short units come last: the workgroups resident on a
+// CU run close to one after another in dispatch order, so the last ones set
+// the tail of the call.
 struct RealUnit {
     int b, split, ctx;
     bool over;   // the request's context length exceeds the host bound (ctx is clamped)
@@ -559,26 +563,29 @@ __device__ __forceinline__ RealUnit real_unit(const DecodeArgs &a, int u)
     const int lane = (int)(threadIdx.x & 63);
     const int span = kPageSize * a.partition_pages;
     RealUnit r{-1, 0, 0, false, false};
-    int carry = 0;
-    for (int c0 = 0; c0 < a.num_seqs; c0 += 64) {
-        const int j = c0 + lane;
-        const int raw = j < a.num_seqs ? a.context_lens[j] : 0;
-        const int cj = clamp_ctx(raw, a.max_context_len);
-        const int nj = j < a.num_seqs ? max(1, (cj + span - 1) / span) : 0;
-        const int incl = wave_inclusive_scan(nj, lane);
-        const int excl = incl - nj;
-        const unsigned long long hit = __ballot(u >= carry + excl && u < carry + incl);
-        if (hit != 0ull) {
-            const int l = __builtin_amdgcn_readfirstlane(__ffsll(hit) - 1);
-            r.b = c0 + l;
-            r.split = u - carry - __builtin_amdgcn_readlane(excl, l);
-            r.ctx = __builtin_amdgcn_readlane(cj, l);
-            const int raw_l = __builtin_amdgcn_readlane(raw, l);
-            r.over = raw_l > a.max_context_len;
-            r.bad = raw_l < 0 || r.over;
-            break;
+    for (int pass = 0; pass < 2; ++pass) {   // 0: full partitions, 1: partly filled last ones
+        int carry = 0;
+        for (int c0 = 0; c0 < a.num_seqs; c0 += 64) {
+            const int j = c0 + lane;
+            const int raw = j < a.num_seqs ? a.context_lens[j] : 0;
+            const int cj = clamp_ctx(raw, a.max_context_len);
+            const int nj = j >= a.num_seqs ? 0 : pass == 0 ? cj / span : ((cj == 0 || cj % span != 0) ? 1 : 0);
+            const int incl = wave_inclusive_scan(nj, lane);
+            const int excl = incl - nj;
+            const unsigned long long hit = __ballot(u >= carry + excl && u < carry + incl);
+            if (hit != 0ull) {
+                const int l = __builtin_amdgcn_readfirstlane(__ffsll(hit) - 1);
+                r.b = c0 + l;
+                r.ctx = __builtin_amdgcn_readlane(cj, l);
+                r.split = pass == 0 ? u - carry - __builtin_amdgcn_readlane(excl, l) : r.ctx / span;
+                const int raw_l = __builtin_amdgcn_readlane(raw, l);
+                r.over = raw_l > a.max_context_len;
+                r.bad = raw_l < 0 || r.over;
+                return r;
+            }
+            carry += __builtin_amdgcn_readlane(incl, 63);
         }
-        carry += __builtin_amdgcn_readlane(incl, 63);
+        u -= carry;
     }
     return r;
 }
