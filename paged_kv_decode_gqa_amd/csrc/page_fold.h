@@ -232,16 +232,6 @@ __device__ __forceinline__ uint64_t coherent_load8(const float *p)
                              __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Four consecutive floats, 8-byte aligned, as two 64-bit coherent loads.
-__device__ __forceinline__ f32x4 coherent_load4(const float *p)
-{
-    uint64_t *q = reinterpret_cast<uint64_t *>(const_cast<float *>(p));
-    const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return f32x4{__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)),
-                 __uint_as_float((uint32_t)hi), __uint_as_float((uint32_t)(hi >> 32))};
-}
-
 // Weight of a stream with running max m when merged under the overall max M
 // (M_use is M, or 0 when every stream is empty).
 __device__ __forceinline__ float merge_weight(float m, float M_use) { return exp2_fast(m - M_use); }
