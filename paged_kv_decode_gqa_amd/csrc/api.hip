@@ -16,6 +16,7 @@ constexpr int64_t kTargetWorkgroupsFew = 256;     // one per CU, for a few long 
 constexpr int64_t kFewPairs = 32;                 // (request, KV head) pairs counted as few
 constexpr int64_t kSingleSplitMax = 2048;         // contexts up to this long are not split at all
 constexpr int64_t kBalancedPartition = 2048;      // partition when the target would exceed kMaxPartition
+constexpr int64_t kShortPartitionMaxSplits = 8;   // 64-token partitions only for contexts of at most this many
 
 // hipdecode_paged_attn_noalloc: its static scratch and the fixed region of
 // arrival counters at the start of it (4096 (request, KV head) pairs).
@@ -42,9 +43,13 @@ int32_t plan_waves(const hipdecode_params &p) { return p.workgroup_waves > 0 ? p
 // partitions against 8.5 us unsplit; sixteen at 200-420 tokens were fastest
 // unsplit).  A few requests get about one workgroup per CU (fewer, larger partitions
 // merge faster, and a CU holding two workgroups would finish last); larger
-// batches get about four per CU.  A batch that would want partitions past the
-// maximum has work to spare and gets smaller ones, which even out requests of
-// very different lengths.
+// batches get about four per CU.  64-token partitions are kept for contexts
+// of at most eight of them; a longer context gets at least 128 tokens per
+// partition (one request at 1024 tokens: 6.31 us against 6.65 us; two at 768:
+// 6.96 against 7.25), since a wavefront then folds two pages instead of one
+// and half as many partials are merged.  A batch that would want partitions
+// past the maximum has work to spare and gets smaller ones, which even out
+// requests of very different lengths.
 int32_t plan_partition(const hipdecode_params &p)
 {
     if (p.partition_tokens > 0)
@@ -62,6 +67,8 @@ int32_t plan_partition(const hipdecode_params &p)
     if (part < floor_part)
         part = floor_part;
     part = ceil_div(part, kMinPartition) * kMinPartition;
+    if (part == kMinPartition && p.max_context_len > kShortPartitionMaxSplits * kMinPartition)
+        part = 2 * kMinPartition;
     if (part > kMaxPartition)
         part = kBalancedPartition;
     return (int32_t)part;

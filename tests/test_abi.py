@@ -219,6 +219,12 @@ def test_planner_and_workspace_sizes():
     # one short request is split for latency: 512 tokens in 64-token partitions
     p3 = base(num_seqs=1, max_context_len=512, num_pages=64, max_blocks_per_seq=32)
     assert hd.hipdecode_partition_tokens(p3) == 64
+    # past eight 64-token partitions a context gets at least 128 tokens per partition
+    for n, want in ((576, 128), (1024, 128), (2048, 128), (4096, 128)):
+        p4 = base(num_seqs=1, max_context_len=n, num_pages=256, max_blocks_per_seq=256)
+        assert hd.hipdecode_partition_tokens(p4) == want, n
+    p5 = base(num_seqs=2, max_context_len=1024, num_pages=128, max_blocks_per_seq=64)
+    assert hd.hipdecode_partition_tokens(p5) == 128
     # explicit partition is honoured
     assert hd.hipdecode_partition_tokens(base(partition_tokens=128)) == 128
 
