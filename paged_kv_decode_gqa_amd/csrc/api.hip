@@ -299,6 +299,7 @@ hipdecode_status run_decode(const hipdecode_params *params, const void *q, const
     a.k_pool_w = fused ? static_cast<uint16_t *>(const_cast<void *>(k_pool)) : nullptr;
     a.v_pool_w = fused ? static_cast<uint16_t *>(const_cast<void *>(v_pool)) : nullptr;
     a.rope_theta = fused ? rope_theta : 0.0;
+    a.rope_log2_theta = a.rope_theta > 0.0 ? log2(a.rope_theta) : 0.0;
     a.violations = violation_word();
 
     const hipError_t e = launch_paged_decode(a, p.num_q_heads / p.num_kv_heads, plan_waves(p),

@@ -57,6 +57,7 @@ struct DecodeArgs {
     uint16_t *k_pool_w;      // the pools, writable
     uint16_t *v_pool_w;
     double rope_theta;       // > 0: q and the new key are rotated at position ctx - 1
+    double rope_log2_theta;  // log2(rope_theta) when rope_theta > 0
     uint32_t *violations;    // contract-violation flag word of this device
 };
 

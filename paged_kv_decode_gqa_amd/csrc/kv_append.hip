@@ -54,7 +54,7 @@ struct AppendArgs {
     int32_t num_rows;
     int32_t max_new;
     int32_t token_groups;   // workgroups per request: ceil(max_new / tokens per workgroup)
-    double theta;
+    double log2_theta;      // with RoPE: log2 of its theta
     uint32_t *violations;   // contract-violation flag word of this device
 };
 
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(AppendArgs a)
     double2 cs[kPairsPerItem];
     if (ROPE) {
         // lane i: the angle of pair i, evaluated in fp64
-        angles[w][lane] = rope::angle(a.theta, pos, lane);
+        angles[w][lane] = rope::angle_of(rope::frequency(a.log2_theta, lane), pos);
         // LDS operations of one wavefront complete in order; this keeps the
         // compiler from moving the reads above the write.
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -343,7 +343,7 @@ HIPDECODE_API hipdecode_status hipdecode_kv_append(const hipdecode_append_params
     a.max_blocks = p.max_blocks_per_seq;
     a.num_rows = p.num_rows;
     a.max_new = max_new;
-    a.theta = p.rope_theta;
+    a.log2_theta = p.rope != HIPDECODE_ROPE_NONE ? log2(p.rope_theta) : 0.0;
     a.violations = violation_word();
 
     // Few tokens (a decode step): four wavefronts per token, for latency.

@@ -153,26 +153,27 @@ __device__ __forceinline__ void load_q(u32x4 (&qv)[G], const DecodeArgs &a, size
 // Fold pages [p_begin, p_end) (at most 64 per wavefront) of KV head g of a
 // request with ctx tokens and n_pages pages into this wavefront's stream.
 // entry: the block-table entry of page p_begin + wave + WAVES * lane, or
-// anything for lanes past the range.  A partly filled last page of the
-// request is folded by the last wavefront, with masking, after the others.
+// anything for lanes past the range.  Full pages go round-robin over the
+// wavefronts; a partly filled last page of the request goes to the wavefront
+// next in turn, as the last page of its pipeline, and is folded with masking.
 // FUSED: the request's last page always goes that way, and its new token
-// (slot (ctx - 1) % 16, row b of k_new/v_new) is taken from k_new/v_new --
-// K rotated with `angles` when RoPE is on -- written to the pool and folded
-// from registers; no other workgroup reads that page.  With append_new false
-// (a context length past the host bound, so ctx was clamped and slot ctx - 1
-// holds a real cached token) nothing is written and the page is folded as
-// the pool holds it.  Returns HIPDECODE_VIOLATION_PAGE if a page id the
-// range uses lies outside the pool (that page was skipped), else 0.
+// (slot (ctx - 1) % 16, row b of k_new/v_new, loaded together with the page)
+// is taken from k_new/v_new -- K rotated with `angles` when RoPE is on --
+// written to the pool and folded from registers; no other workgroup reads
+// that page.  With append_new false (a context length past the host bound,
+// so ctx was clamped and slot ctx - 1 holds a real cached token) nothing is
+// written and the page is folded as the pool holds it.  Returns
+// HIPDECODE_VIOLATION_PAGE if a page id the range uses lies outside the pool
+// (that page was skipped), else 0.
 struct NoHook {
     __device__ __forceinline__ void operator()() const {}
 };
 
 template <int G, int WAVES, bool FUSED = false, class Hook = NoHook>
 __device__ __forceinline__ uint32_t fold_range(Stream<G> &st, const DecodeArgs &a, const u32x4 (&qv)[G],
-                                           const int32_t *trow, int g, int p_begin, int p_end,
-                                           int n_pages, int ctx, int entry, const Lane &ln, int b = 0,
-                                           const double2 *angles = nullptr, Hook before_fold = Hook(),
-                                           bool append_new = true)
+                                           int g, int p_begin, int p_end, int n_pages, int ctx, int entry,
+                                           const Lane &ln, int b = 0, const double2 *angles = nullptr,
+                                           Hook before_fold = Hook(), bool append_new = true)
 {
     const uint32_t tok_bytes = (uint32_t)a.num_kv_heads * kHeadDim * 2;   // bytes between slots
     const size_t page_elems = (size_t)kPageSize * a.num_kv_heads * kHeadDim;
@@ -183,8 +184,30 @@ __device__ __forceinline__ uint32_t fold_range(Stream<G> &st, const DecodeArgs &
     const int full_end = tail_partial ? p_end - 1 : p_end;
     const int span = full_end - p_begin;
     const int npw = span > ln.wave ? (span - ln.wave + WAVES - 1) / WAVES : 0;
-    const int my_entry = ln.lane < npw ? entry : -1;
+    // The last page, at relative index span, is page span / WAVES of
+    // wavefront span % WAVES, which has exactly that many full pages.
+    const bool my_tail = tail_partial && ln.wave == span % WAVES;
+    const int n = npw + (my_tail ? 1 : 0);
+    const int my_entry = ln.lane < n ? entry : -1;
     const unsigned num_pages = (unsigned)a.num_pages;
+
+    // FUSED: the 16 lanes that hold the new token (register slot / 4) load
+    // its K and V, and K's partner dims for RoPE, before the first page; once
+    // before_fold has the angles they rotate K, write the token to the pool
+    // and park it in LDS, from where the fold of the last page takes it.
+    [[maybe_unused]] const int slot = (ctx - 1) % kPageSize;
+    [[maybe_unused]] const bool new_lanes = FUSED && my_tail && append_new && ln.row == (slot & 3);
+    __shared__ u32x4 new_tok[FUSED ? 2 : 1][FUSED ? 16 : 1];
+    [[maybe_unused]] u32x4 kn, vn, kp;
+    if constexpr (FUSED) {
+        if (new_lanes) {
+            const size_t nrow = ((size_t)b * a.num_kv_heads + g) * kHeadDim;
+            kn = load16(a.k_new + nrow + ln.sub * 8);
+            vn = load16(a.v_new + nrow + ln.sub * 8);
+            if (angles != nullptr)
+                kp = load16(a.k_new + nrow + (ln.sub ^ 8) * 8);
+        }
+    }
 
     // The steady-state loop issues its loads unconditionally so that the
     // compiler's wait counts stay exact and page i+1 really is in flight while
@@ -197,72 +220,79 @@ __device__ __forceinline__ uint32_t fold_range(Stream<G> &st, const DecodeArgs &
         const int safe = (unsigned)phys < num_pages ? phys : 0;
         load_page(r, a.k_pool + (size_t)safe * page_elems, a.v_pool + (size_t)safe * page_elems, lane_off, tok4);
     };
-    auto fold = [&](const PageRegs &r, int i) {
+    auto fold_full = [&](const PageRegs &r, int i) {
         const int phys = __builtin_amdgcn_readlane(my_entry, i);
         if ((unsigned)phys < num_pages)   // a page outside the pool is never folded
             fold_page<G, false>(st, r, qv, a.scale_log2, 0, 0);
     };
+    // The wavefront's last page: the request's partly filled last page when
+    // this wavefront holds it, else a full one.
+    auto fold_last = [&](PageRegs &r, int i) {
+        if (!my_tail) {
+            fold_full(r, i);
+            return;
+        }
+        const int phys = __builtin_amdgcn_readlane(my_entry, i);
+        if ((unsigned)phys >= num_pages)
+            return;
+        if constexpr (FUSED) {
+            if (new_lanes) {
+                const u32x4 k_tok = new_tok[0][ln.sub];
+                const u32x4 v_tok = new_tok[1][ln.sub];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    if (t == (slot >> 2)) {
+                        r.k[t] = k_tok;
+                        r.v[t] = v_tok;
+                    }
+                }
+            }
+        }
+        fold_page<G, true>(st, r, qv, a.scale_log2, full_end * kPageSize + ln.row, ctx);
+    };
 
     // before_fold runs in every wavefront once the first page is in flight
     // (the fused kernel rotates q there); it may hold a workgroup barrier.
-    if (npw > 0)
+    if (n > 0)
         issue(ra, 0);
     before_fold();
-    if (npw > 0) {
-        int i = 0;
-        for (; i + 2 < npw; i += 2) {
-            issue(rb, i + 1);
-            fold(ra, i);
-            issue(ra, i + 2);
-            fold(rb, i + 1);
+    if constexpr (FUSED) {
+        if (new_lanes) {
+            if (angles != nullptr) {
+                const int base = 8 * (ln.sub & 7);
+                const uint4 rot = rope::rotate8(make_uint4(kn.x, kn.y, kn.z, kn.w),
+                                                make_uint4(kp.x, kp.y, kp.z, kp.w), ln.sub >= 8,
+                                                [&](int e) { return angles[base + e]; });
+                kn = u32x4{rot.x, rot.y, rot.z, rot.w};
+            }
+            const int phys = __builtin_amdgcn_readlane(my_entry, npw);
+            if ((unsigned)phys < num_pages) {
+                const size_t off = (size_t)phys * page_elems * 2 + lane_off + (size_t)(slot >> 2) * tok4;
+                *reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(a.k_pool_w) + off) = kn;
+                *reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(a.v_pool_w) + off) = vn;
+            }
+            new_tok[0][ln.sub] = kn;
+            new_tok[1][ln.sub] = vn;
         }
-        if (i + 1 < npw) {
+    }
+    if (n > 0) {
+        int i = 0;
+        for (; i + 2 < n; i += 2) {
             issue(rb, i + 1);
-            fold(ra, i);
-            fold(rb, i + 1);
+            fold_full(ra, i);
+            issue(ra, i + 2);
+            fold_full(rb, i + 1);
+        }
+        if (i + 1 < n) {
+            issue(rb, i + 1);
+            fold_full(ra, i);
+            fold_last(rb, i + 1);
         } else {
-            fold(ra, i);
+            fold_last(ra, i);
         }
     }
     // pages outside the pool were skipped above
-    uint32_t viol = __ballot(ln.lane < npw && (unsigned)entry >= num_pages) != 0ull ? HIPDECODE_VIOLATION_PAGE : 0u;
-    if (tail_partial && ln.wave == WAVES - 1) {
-        const int phys = trow[full_end];
-        if ((unsigned)phys < num_pages) {
-            load_page(ra, a.k_pool + (size_t)phys * page_elems, a.v_pool + (size_t)phys * page_elems,
-                      lane_off, tok4);
-            if constexpr (FUSED) {
-                const int slot = (ctx - 1) % kPageSize;
-                if (append_new && ln.row == (slot & 3)) {   // the 16 lanes holding the new token, in register slot / 4
-                    const size_t nrow = ((size_t)b * a.num_kv_heads + g) * kHeadDim;
-                    u32x4 kn = load16(a.k_new + nrow + ln.sub * 8);
-                    const u32x4 vn = load16(a.v_new + nrow + ln.sub * 8);
-                    if (angles != nullptr) {
-                        const u32x4 kp = load16(a.k_new + nrow + (ln.sub ^ 8) * 8);
-                        const int base = 8 * (ln.sub & 7);
-                        const uint4 r = rope::rotate8(make_uint4(kn.x, kn.y, kn.z, kn.w),
-                                                      make_uint4(kp.x, kp.y, kp.z, kp.w), ln.sub >= 8,
-                                                      [&](int e) { return angles[base + e]; });
-                        kn = u32x4{r.x, r.y, r.z, r.w};
-                    }
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        if (t == (slot >> 2)) {
-                            ra.k[t] = kn;
-                            ra.v[t] = vn;
-                        }
-                    }
-                    const size_t off = (size_t)phys * page_elems * 2 + lane_off + (size_t)(slot >> 2) * tok4;
-                    *reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(a.k_pool_w) + off) = kn;
-                    *reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(a.v_pool_w) + off) = vn;
-                }
-            }
-            fold_page<G, true>(st, ra, qv, a.scale_log2, full_end * kPageSize + ln.row, ctx);
-        } else {
-            viol = HIPDECODE_VIOLATION_PAGE;
-        }
-    }
-    return viol;
+    return __ballot(ln.lane < n && (unsigned)entry >= num_pages) != 0ull ? HIPDECODE_VIOLATION_PAGE : 0u;
 }
 
 // The workgroup's streams into LDS (row-groups merged first only with
@@ -667,7 +697,6 @@ void paged_decode_kernel(DecodeArgs a)
                              ? a.block_table[(size_t)b * a.max_blocks + idx] : -1;
         }
     }
-    const int32_t *trow = a.block_table + (size_t)b * a.max_blocks;
     const int p_begin = split * pp;
     const int n_pages = (ctx + kPageSize - 1) / kPageSize;
     const int nsplit_b = (n_pages + pp - 1) / pp;
@@ -700,7 +729,7 @@ void paged_decode_kernel(DecodeArgs a)
         if constexpr (FUSED) {
             if (rope_on) {
                 if (ln.wave == 0)
-                    angles[ln.lane] = rope::angle(a.rope_theta, ctx - 1, ln.lane);
+                    angles[ln.lane] = rope::angle_of(rope::frequency(a.rope_log2_theta, ln.lane), ctx - 1);
                 __syncthreads();
                 const int base = 8 * (ln.sub & 7);
 #pragma unroll
@@ -716,11 +745,11 @@ void paged_decode_kernel(DecodeArgs a)
     Stream<G> st;
     st.init();
     if constexpr (FUSED)
-        viol |= fold_range<G, WAVES, FUSED>(st, a, qv, trow, g, p_begin, min(p_begin + a.partition_pages, n_pages),
+        viol |= fold_range<G, WAVES, FUSED>(st, a, qv, g, p_begin, min(p_begin + a.partition_pages, n_pages),
                                             n_pages, ctx, spec_entry, ln, b, rope_on ? angles : nullptr, rotate_q,
                                             !over);
     else
-        viol |= fold_range<G, WAVES, FUSED>(st, a, qv, trow, g, p_begin, min(p_begin + a.partition_pages, n_pages),
+        viol |= fold_range<G, WAVES, FUSED>(st, a, qv, g, p_begin, min(p_begin + a.partition_pages, n_pages),
                                             n_pages, ctx, spec_entry, ln, b);
     if (viol != 0 && ln.lane == 0)
         report_violation(a.violations, viol);

@@ -19,10 +19,14 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kHalf = 64;   // rotation pairs of a 128-dimension head
 
-// (cos, sin) of pair i's angle at position pos, in fp64.
-__device__ inline double2 angle(double theta, int pos, int i)
+// Frequency of pair i, theta^(-2i/128) = 2^(-(i/64) log2 theta), in fp64,
+// from log2 theta computed once on the host: one exp2 per lane, which is
+// much shorter than a pow, and within a few units in the last place of it.
+__device__ inline double frequency(double log2_theta, int i) { return exp2(-((double)i / 64.0) * log2_theta); }
+
+// (cos, sin) of the angle pos * freq, in fp64.
+__device__ inline double2 angle_of(double freq, int pos)
 {
-    const double freq = pow(theta, -2.0 * (double)i / 128.0);
     double sn, c;
     sincos((double)pos * freq, &sn, &c);
     return make_double2(c, sn);
