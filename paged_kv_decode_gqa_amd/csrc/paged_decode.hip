@@ -191,22 +191,22 @@ __device__ __forceinline__ uint32_t fold_range(Stream<G> &st, const DecodeArgs &
     const int my_entry = ln.lane < n ? entry : -1;
     const unsigned num_pages = (unsigned)a.num_pages;
 
-    // FUSED: the 16 lanes that hold the new token (register slot / 4) load
-    // its K and V, and K's partner dims for RoPE, before the first page; once
-    // before_fold has the angles they rotate K, write the token to the pool
-    // and park it in LDS, from where the fold of the last page takes it.
+    // FUSED: the 16 lanes that hold the new token (register slot / 4) take
+    // its K and V, and K's partner dims for RoPE, loaded before the first
+    // page; once before_fold has the angles they rotate K, write the token to
+    // the pool and park it in LDS, from where the fold of the last page takes
+    // it.  Every lane loads (the request's row exists whenever ctx > 0), with
+    // no branch, so that the compiler's wait for the table entry before the
+    // first page counts these loads and does not wait for them.
     [[maybe_unused]] const int slot = (ctx - 1) % kPageSize;
     [[maybe_unused]] const bool new_lanes = FUSED && my_tail && append_new && ln.row == (slot & 3);
     __shared__ u32x4 new_tok[FUSED ? 2 : 1][FUSED ? 16 : 1];
     [[maybe_unused]] u32x4 kn, vn, kp;
     if constexpr (FUSED) {
-        if (new_lanes) {
-            const size_t nrow = ((size_t)b * a.num_kv_heads + g) * kHeadDim;
-            kn = load16(a.k_new + nrow + ln.sub * 8);
-            vn = load16(a.v_new + nrow + ln.sub * 8);
-            if (angles != nullptr)
-                kp = load16(a.k_new + nrow + (ln.sub ^ 8) * 8);
-        }
+        const size_t nrow = ((size_t)b * a.num_kv_heads + g) * kHeadDim;
+        kn = load16(a.k_new + nrow + ln.sub * 8);
+        vn = load16(a.v_new + nrow + ln.sub * 8);
+        kp = load16(a.k_new + nrow + (ln.sub ^ 8) * 8);
     }
 
     // The steady-state loop issues its loads unconditionally so that the
@@ -253,7 +253,10 @@ __device__ __forceinline__ uint32_t fold_range(Stream<G> &st, const DecodeArgs &
 
     // before_fold runs in every wavefront once the first page is in flight
     // (the fused kernel rotates q there); it may hold a workgroup barrier.
-    if (n > 0)
+    // The fused kernel issues that page even in a wavefront with no pages (it
+    // fetches page 0 and folds nothing): with the load under a branch, the
+    // compiler's wait for q inside before_fold would also wait for the page.
+    if (FUSED || n > 0)
         issue(ra, 0);
     before_fold();
     if constexpr (FUSED) {
@@ -717,13 +720,14 @@ void paged_decode_kernel(DecodeArgs a)
     // that page is in flight.
     __shared__ double2 angles[FUSED ? rope::kHalf : 1];
     const bool rope_on = FUSED && a.rope_theta > 0.0;
+    // Loaded with RoPE off too: loads under a branch leave the compiler's
+    // wait for the table entry, which the first page needs, counting too few
+    // loads after it, so that wait would also hold for q.
     u32x4 qp[G];
     if constexpr (FUSED) {
-        if (rope_on) {
 #pragma unroll
-            for (int h = 0; h < G; ++h)
-                qp[h] = load16(a.q + (row0 + h) * kHeadDim + (ln.sub ^ 8) * 8);
-        }
+        for (int h = 0; h < G; ++h)
+            qp[h] = load16(a.q + (row0 + h) * kHeadDim + (ln.sub ^ 8) * 8);
     }
     auto rotate_q = [&]() __attribute__((always_inline)) {
         if constexpr (FUSED) {
