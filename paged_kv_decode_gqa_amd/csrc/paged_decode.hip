@@ -150,6 +150,24 @@ __device__ __forceinline__ void load_q(u32x4 (&qv)[G], const DecodeArgs &a, size
         qv[h] = load16(a.q + (row0 + h) * kHeadDim + sub * 8);
 }
 
+// RoPE of the 8 dims [8 sub, 8 sub + 8) of a head that all four row-groups
+// of a wavefront hold alike (q, or the new token's K), given the partner
+// dims: row-group r rotates word r (dims 8 sub + 2r and 8 sub + 2r + 1) and
+// three lane swaps hand every row-group all four words.  cs(e): the angles
+// of pair 8 (sub % 8) + e.  Called with every lane of the wavefront active.
+template <typename CS>
+__device__ __forceinline__ u32x4 rotate_shared(u32x4 own, u32x4 partner, bool second_half, int row, CS cs)
+{
+    const uint32_t o = row == 0 ? own.x : row == 1 ? own.y : row == 2 ? own.z : own.w;
+    const uint32_t p = row == 0 ? partner.x : row == 1 ? partner.y : row == 2 ? partner.z : partner.w;
+    const uint32_t mine = rope::rotate2(o, p, second_half, cs(2 * row), cs(2 * row + 1));
+    float w_even, w_odd, w0, w1, w2, w3;
+    pair_values<16>(__uint_as_float(mine), w_even, w_odd);   // words of rows r & 2 and (r & 2) | 1
+    pair_values<32>(w_even, w0, w2);
+    pair_values<32>(w_odd, w1, w3);
+    return u32x4{__float_as_uint(w0), __float_as_uint(w1), __float_as_uint(w2), __float_as_uint(w3)};
+}
+
 // Fold pages [p_begin, p_end) (at most 64 per wavefront) of KV head g of a
 // request with ctx tokens and n_pages pages into this wavefront's stream.
 // entry: the block-table entry of page p_begin + wave + WAVES * lane, or
@@ -260,14 +278,11 @@ __device__ __forceinline__ uint32_t fold_range(Stream<G> &st, const DecodeArgs &
         issue(ra, 0);
     before_fold();
     if constexpr (FUSED) {
+        if (my_tail && angles != nullptr) {   // the whole wavefront: rotate_shared swaps lanes
+            const int base = 8 * (ln.sub & 7);
+            kn = rotate_shared(kn, kp, ln.sub >= 8, ln.row, [&](int e) { return angles[base + e]; });
+        }
         if (new_lanes) {
-            if (angles != nullptr) {
-                const int base = 8 * (ln.sub & 7);
-                const uint4 rot = rope::rotate8(make_uint4(kn.x, kn.y, kn.z, kn.w),
-                                                make_uint4(kp.x, kp.y, kp.z, kp.w), ln.sub >= 8,
-                                                [&](int e) { return angles[base + e]; });
-                kn = u32x4{rot.x, rot.y, rot.z, rot.w};
-            }
             const int phys = __builtin_amdgcn_readlane(my_entry, npw);
             if ((unsigned)phys < num_pages) {
                 const size_t off = (size_t)phys * page_elems * 2 + lane_off + (size_t)(slot >> 2) * tok4;
@@ -737,12 +752,8 @@ void paged_decode_kernel(DecodeArgs a)
                 __syncthreads();
                 const int base = 8 * (ln.sub & 7);
 #pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    const uint4 r = rope::rotate8(make_uint4(qv[h].x, qv[h].y, qv[h].z, qv[h].w),
-                                                  make_uint4(qp[h].x, qp[h].y, qp[h].z, qp[h].w), ln.sub >= 8,
-                                                  [&](int e) { return angles[base + e]; });
-                    qv[h] = u32x4{r.x, r.y, r.z, r.w};
-                }
+                for (int h = 0; h < G; ++h)
+                    qv[h] = rotate_shared(qv[h], qp[h], ln.sub >= 8, ln.row, [&](int e) { return angles[base + e]; });
             }
         }
     };

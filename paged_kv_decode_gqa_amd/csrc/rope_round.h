@@ -66,53 +66,31 @@ __device__ inline uint32_t pack_bf16(double x, double y)
 __device__ inline double lo_f64(uint32_t w) { return (double)__uint_as_float(w << 16); }
 __device__ inline double hi_f64(uint32_t w) { return (double)__uint_as_float(w & 0xFFFF0000u); }
 
-// Rotates 8 consecutive dimensions [8c, 8c + 8) of a head held in `own`
-// (c = 0..15), given the 8 partner dimensions `partner` (8c + 64 or 8c - 64):
-// pairs 8(c % 8) + e use angles cs(e).  The first half of a head takes
+// Rotates one word of a head: the two dimensions held in `own` (bf16, low
+// half first), given the two partner dimensions `partner` (64 higher or
+// lower) and their angles c0, c1.  The first half of a head takes
 // x cos - partner sin, the second partner sin + x cos.
 //
 // Rounding: t = fp32 nearest of each fp64 value r, then the hardware's bf16
 // nearest even of t.  Every bf16 rounding boundary (a midpoint between bf16
 // neighbours) is an fp32 number and rounding is monotonic, so t lies on the
 // same side of each boundary as r unless t is itself a boundary; the two
-// roundings then agree with the direct one.  When some t is a boundary (low
-// 16 bits 0x8000, probability about 2^-16 per value) or NaN, all eight take
-// the exact path of pack_bf16.
-template <typename CS>
-__device__ inline uint4 rotate8(uint4 own, uint4 partner, bool second_half, CS cs)
+// roundings then agree with the direct one.  When a t is a boundary (low 16
+// bits 0x8000, probability about 2^-16 per value) or NaN, the word takes the
+// exact path of pack_bf16.
+__device__ inline uint32_t rotate2(uint32_t own, uint32_t partner, bool second_half, double2 c0, double2 c1)
 {
-    const uint32_t o[4] = {own.x, own.y, own.z, own.w};
-    const uint32_t p[4] = {partner.x, partner.y, partner.z, partner.w};
-    double r[8];
-    float t[8];
-    bool unsure = false;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        const double2 c0 = cs(2 * w);
-        const double2 c1 = cs(2 * w + 1);
-        const double x0 = lo_f64(o[w]), x1 = hi_f64(o[w]);
-        const double y0 = lo_f64(p[w]), y1 = hi_f64(p[w]);
-        r[2 * w] = second_half ? x0 * c0.x + y0 * c0.y : x0 * c0.x - y0 * c0.y;
-        r[2 * w + 1] = second_half ? x1 * c1.x + y1 * c1.y : x1 * c1.x - y1 * c1.y;
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        t[e] = (float)r[e];
-        unsure |= (__float_as_uint(t[e]) & 0xFFFFu) == 0x8000u || t[e] != t[e];
-    }
-    uint32_t u[4];
-    if (__builtin_expect(unsure, 0)) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-            u[w] = pack_bf16(r[2 * w], r[2 * w + 1]);
-    } else {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const f32x2_t v = {t[2 * w], t[2 * w + 1]};
-            u[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
-        }
-    }
-    return make_uint4(u[0], u[1], u[2], u[3]);
+    const double x0 = lo_f64(own), x1 = hi_f64(own);
+    const double y0 = lo_f64(partner), y1 = hi_f64(partner);
+    const double r0 = second_half ? x0 * c0.x + y0 * c0.y : x0 * c0.x - y0 * c0.y;
+    const double r1 = second_half ? x1 * c1.x + y1 * c1.y : x1 * c1.x - y1 * c1.y;
+    const float t0 = (float)r0, t1 = (float)r1;
+    const bool unsure = (__float_as_uint(t0) & 0xFFFFu) == 0x8000u || t0 != t0 ||
+                        (__float_as_uint(t1) & 0xFFFFu) == 0x8000u || t1 != t1;
+    if (__builtin_expect(unsure, 0))
+        return pack_bf16(r0, r1);
+    const f32x2_t v = {t0, t1};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 }  // namespace rope
