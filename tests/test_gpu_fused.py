@@ -74,6 +74,17 @@ def test_fused_splits_and_waves(waves, partition):
              what=f"waves={waves} part={partition}")
 
 
+@pytest.mark.parametrize("waves", [4, 16])
+def test_fused_last_page_on_every_wavefront(waves):
+    """The page that takes the new token goes to the wavefront next in turn
+    after the full pages: with 256-token partitions, contexts 16k + 9 and
+    16k + 16 put it at every relative index, partly filled or full."""
+    ctx = [16 * k + 9 for k in range(16)] + [16 * k + 16 for k in range(0, 16, 3)]
+    case = make_case(ctx, seed=75, pool_pages=sum((n + 15) // 16 for n in ctx) + 5)
+    run_case(case, make_append_inputs(case, None, seed=75), theta=THETA, waves=waves, partition=256,
+             what=f"last page on every wavefront, {waves} waves")
+
+
 @pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 4), (32, 16)])
 def test_fused_group_sizes(hq, hkv):
     case = make_case([700, 33, 1500, 16], seed=73, Hq=hq, Hkv=hkv, pool_pages=200)

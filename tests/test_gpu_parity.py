@@ -85,6 +85,18 @@ def test_edge_lengths_poisoned(partition, waves):
 
 
 @pytest.mark.parametrize("waves", [4, 16])
+def test_last_page_on_every_wavefront(waves):
+    """A partly filled last page goes to the wavefront next in turn after the
+    full pages.  With 256-token partitions (16 pages), contexts 16k + 9 for
+    k = 0..15 put that page at every relative index, so on every wavefront of
+    a 4- or 16-wavefront workgroup, after 0 to 3 full pages of its own; the
+    unused slots hold NaN."""
+    ctx = [16 * k + 9 for k in range(16)] + [256 * 3 + 16 * k + 9 for k in range(0, 16, 5)]
+    case = make_case(ctx, seed=15, poison=True, pool_pages=sum((n + 15) // 16 for n in ctx) + 5)
+    _check(case, f"last page on every wavefront, {waves} waves", partition_tokens=256, workgroup_waves=waves)
+
+
+@pytest.mark.parametrize("waves", [4, 16])
 def test_split_count_invariance(waves):
     case = make_case([200, 1000, 3333, 8191, 17], seed=12, poison=True)
     dc = DeviceCase(case)
