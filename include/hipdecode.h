@@ -178,7 +178,10 @@ hipdecode_status hipdecode_paged_attn(const hipdecode_params *params,
  *     x'[i]      = x[i] cos(p f_i) - x[i + 64] sin(p f_i)
  *     x'[i + 64] = x[i + 64] cos(p f_i) + x[i] sin(p f_i)
  * evaluated in fp64 from the exactly widened bf16 inputs and rounded once to
- * the nearest bf16, ties to even.
+ * the nearest bf16, ties to even.  f_i itself is evaluated in fp64 as
+ * 2^(-(i/64) log2(rope_theta)), within a few units in the last place of the
+ * power, so a rotated value within about 1e-12 (relative) of a midpoint
+ * between two bf16 numbers may round to either of them.
  *
  * Layouts (row-major, contiguous):
  *   q             [num_rows][num_q_heads][128]   bf16, may be NULL
