@@ -348,6 +348,39 @@ class PreparedCall:
             raise HipDecodeError(st, "hipdecode_paged_attn")
 
 
+def _check_tensor(name, t, shape, dtype, device):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_call_tensors(q, k_pool, v_pool, block_table, context_lens, rows, out, lse, out_dtype):
+    """Host checks of what the C ABI cannot see: shapes, dtypes and devices of
+    the tensors a convenience call passes, so that a mismatched buffer is a
+    ValueError rather than a kernel writing past it."""
+    import torch
+    if q.dim() != 3 or k_pool.dim() != 4:
+        raise ValueError("q must be [rows, Hq, 128] and k_pool [P, 16, Hkv, 128]")
+    dev = q.device
+    _, Hq, D = q.shape
+    _check_tensor("v_pool", v_pool, k_pool.shape, torch.bfloat16, dev)
+    _check_tensor("k_pool", k_pool, k_pool.shape, torch.bfloat16, dev)
+    B = context_lens.shape[0] if context_lens.dim() == 1 else -1
+    _check_tensor("context_lens", context_lens, (B,), torch.int32, dev)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError(f"block_table must be [{B}, max_blocks]")
+    _check_tensor("block_table", block_table, block_table.shape, torch.int32, dev)
+    if out is not None:
+        _check_tensor("out", out, (rows, Hq, D), out_dtype, dev)
+    if lse is not None:
+        _check_tensor("lse", lse, (rows, Hq), torch.float32, dev)
+
+
 def paged_attn(q, k_pool, v_pool, block_table, context_lens, scale, *, max_context_len,
                out_dtype=None, partition_tokens=0, workgroup_waves=0, schedule=0, out=None, lse=None,
                workspace=None):
@@ -364,6 +397,7 @@ def paged_attn(q, k_pool, v_pool, block_table, context_lens, scale, *, max_conte
     P, page, Hkv, Dk = k_pool.shape
     if out_dtype is None:
         out_dtype = out.dtype if out is not None else torch.bfloat16
+    _check_call_tensors(q, k_pool, v_pool, block_table, context_lens, B, out, lse, out_dtype)
     code = HIPDECODE_F32 if out_dtype == torch.float32 else HIPDECODE_BF16
     params = make_params(num_seqs=B, num_q_heads=Hq, num_kv_heads=Hkv, num_pages=P,
                          max_blocks_per_seq=block_table.shape[1], max_context_len=max_context_len,
@@ -470,6 +504,8 @@ def kv_append(k_new, v_new, block_table, context_lens, k_pool, v_pool, *, q=None
         raise ValueError("q must be [T, Hq, head_dim]")
     Hq = q.shape[1] if q is not None else Hkv
     B = context_lens.shape[0]
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError(f"block_table must be [{B}, max_blocks]")
     if new_start is not None and new_start.shape != (B + 1,):
         raise ValueError("new_start must have num_seqs + 1 entries")
     if max_new_tokens is None:
@@ -536,6 +572,7 @@ def prefill_attn(q, k_pool, v_pool, block_table, context_lens, new_start, scale,
         raise ValueError("new_start must have num_seqs + 1 entries")
     if out_dtype is None:
         out_dtype = out.dtype if out is not None else torch.bfloat16
+    _check_call_tensors(q, k_pool, v_pool, block_table, context_lens, T, out, lse, out_dtype)
     params = make_prefill_params(num_seqs=B, num_q_heads=Hq, num_kv_heads=Hkv, num_pages=P,
                                  max_blocks_per_seq=block_table.shape[1], num_rows=T,
                                  max_new_tokens=T if max_new_tokens is None else max_new_tokens, scale=scale,
@@ -652,6 +689,11 @@ def paged_attn_append(q, k_new, v_new, k_pool, v_pool, block_table, context_lens
     P, page, Hkv, _ = k_pool.shape
     if out_dtype is None:
         out_dtype = out.dtype if out is not None else torch.bfloat16
+    if q.dtype != torch.bfloat16:
+        raise ValueError("q must be bfloat16")
+    _check_call_tensors(q, k_pool, v_pool, block_table, context_lens, B, out, lse, out_dtype)
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        _check_tensor(name, t, (B, Hkv, D), torch.bfloat16, q.device)
     params = make_params(num_seqs=B, num_q_heads=Hq, num_kv_heads=Hkv, num_pages=P,
                          max_blocks_per_seq=block_table.shape[1], max_context_len=max_context_len, scale=scale,
                          head_dim=D, page_size=page, partition_tokens=partition_tokens,

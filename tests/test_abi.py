@@ -472,3 +472,73 @@ def test_header_constants_match_the_binding():
 
 def test_contract_violations_rejects_null_before_any_hip_call():
     assert hd.library().hipdecode_contract_violations(None) == hd.HIPDECODE_ERR_NULL
+
+
+# --------------------------------------------------------------------------
+# Convenience wrappers: host checks of tensors the C ABI cannot see
+# --------------------------------------------------------------------------
+def _decode_tensors(B=2, Hq=16, Hkv=8, P=8, blocks=4):
+    import torch
+    q = torch.zeros((B, Hq, 128), dtype=torch.bfloat16)
+    k = torch.zeros((P, 16, Hkv, 128), dtype=torch.bfloat16)
+    v = torch.zeros((P, 16, Hkv, 128), dtype=torch.bfloat16)
+    table = torch.zeros((B, blocks), dtype=torch.int32)
+    ctx = torch.zeros((B,), dtype=torch.int32)
+    return q, k, v, table, ctx
+
+
+@pytest.mark.parametrize("bad", ["out_dtype", "out_shape", "lse_shape", "v_shape", "table_rows", "ctx_dtype"])
+def test_paged_attn_wrapper_rejects_mismatched_tensors(bad):
+    """Every mismatch is a ValueError raised on the host, before any launch
+    (these tensors live on the CPU, where a launch would fail differently)."""
+    import torch
+    q, k, v, table, ctx = _decode_tensors()
+    out, lse = None, None
+    if bad == "out_dtype":
+        out = torch.empty((2, 16, 128), dtype=torch.float32)
+    elif bad == "out_shape":
+        out = torch.empty((1, 16, 128), dtype=torch.bfloat16)
+    elif bad == "lse_shape":
+        lse = torch.empty((2, 8), dtype=torch.float32)
+    elif bad == "v_shape":
+        v = torch.zeros((4, 16, 8, 128), dtype=torch.bfloat16)
+    elif bad == "table_rows":
+        table = torch.zeros((3, 4), dtype=torch.int32)
+    elif bad == "ctx_dtype":
+        ctx = torch.zeros((2,), dtype=torch.int64)
+    with pytest.raises(ValueError):
+        hd.paged_attn(q, k, v, table, ctx, 0.088, max_context_len=64, out_dtype=torch.bfloat16, out=out, lse=lse)
+
+
+@pytest.mark.parametrize("bad", ["k_new_shape", "out_shape"])
+def test_paged_attn_append_wrapper_rejects_mismatched_tensors(bad):
+    import torch
+    q, k, v, table, ctx = _decode_tensors()
+    k_new = torch.zeros((2, 8, 128), dtype=torch.bfloat16)
+    v_new = torch.zeros((2, 8, 128), dtype=torch.bfloat16)
+    out = None
+    if bad == "k_new_shape":
+        k_new = torch.zeros((2, 4, 128), dtype=torch.bfloat16)
+    else:
+        out = torch.empty((2, 8, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        hd.paged_attn_append(q, k_new, v_new, k, v, table, ctx, 0.088, max_context_len=64, rope_theta=1e6,
+                             out=out)
+
+
+def test_prefill_wrapper_rejects_mismatched_output():
+    import torch
+    _, k, v, table, ctx = _decode_tensors()
+    q = torch.zeros((5, 16, 128), dtype=torch.bfloat16)
+    new_start = torch.tensor([0, 3, 5], dtype=torch.int32)
+    out = torch.empty((4, 16, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        hd.prefill_attn(q, k, v, table, ctx, new_start, 0.088, out=out)
+
+
+def test_kv_append_wrapper_rejects_table_rows():
+    import torch
+    _, k, v, _, ctx = _decode_tensors()
+    k_new = torch.zeros((2, 8, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        hd.kv_append(k_new, k_new.clone(), torch.zeros((1, 4), dtype=torch.int32), ctx, k, v, rope_theta=1e6)
