@@ -606,9 +606,32 @@ class StepRunner:
     def __init__(self, layers, block_table, context_lens, *, max_seqs, num_pages, max_context_len, scale,
                  rope_theta=0.0, out_dtype=HIPDECODE_BF16):
         import numpy as np
+        import torch
         first = layers[0]
         L = len(layers)
         self._keep = (layers, block_table, context_lens)
+        # host checks of what the C ABI cannot see: every layer's tensors
+        # shaped for the largest bucket, on one device
+        rows = hipdecode_step_bucket(int(max_seqs), int(max_seqs))
+        if rows <= 0:
+            raise ValueError("max_seqs must be at least 1")
+        dev = first["q"].device
+        Hq, D = first["q"].shape[1], first["q"].shape[2]
+        Hkv = first["k_pool"].shape[2]
+        out_torch = torch.float32 if out_dtype == HIPDECODE_F32 else torch.bfloat16
+        for i, layer in enumerate(layers):
+            _check_tensor(f"layers[{i}].k_pool", layer["k_pool"], (int(num_pages), 16, Hkv, D), torch.bfloat16, dev)
+            _check_tensor(f"layers[{i}].v_pool", layer["v_pool"], (int(num_pages), 16, Hkv, D), torch.bfloat16, dev)
+            _check_tensor(f"layers[{i}].q", layer["q"], (rows, Hq, D), torch.bfloat16, dev)
+            _check_tensor(f"layers[{i}].k_new", layer["k_new"], (rows, Hkv, D), torch.bfloat16, dev)
+            _check_tensor(f"layers[{i}].v_new", layer["v_new"], (rows, Hkv, D), torch.bfloat16, dev)
+            _check_tensor(f"layers[{i}].out", layer["out"], (rows, Hq, D), out_torch, dev)
+            if layer.get("lse") is not None:
+                _check_tensor(f"layers[{i}].lse", layer["lse"], (rows, Hq), torch.float32, dev)
+        if block_table.dim() != 2 or block_table.shape[0] != rows:
+            raise ValueError(f"block_table must be [{rows}, max_blocks]")
+        _check_tensor("block_table", block_table, block_table.shape, torch.int32, dev)
+        _check_tensor("context_lens", context_lens, (rows,), torch.int32, dev)
 
         def ptrs(key):
             if any(layer.get(key) is None for layer in layers):

@@ -542,3 +542,31 @@ def test_kv_append_wrapper_rejects_table_rows():
     k_new = torch.zeros((2, 8, 128), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         hd.kv_append(k_new, k_new.clone(), torch.zeros((1, 4), dtype=torch.int32), ctx, k, v, rope_theta=1e6)
+
+
+@pytest.mark.parametrize("bad", ["q_rows", "pool_pages", "out_dtype", "table_rows"])
+def test_step_runner_wrapper_rejects_mismatched_tensors(bad):
+    import torch
+    rows, Hq, Hkv, P = 4, 16, 8, 10      # max_seqs 3 -> bucket 4
+
+    def layer():
+        return dict(k_pool=torch.zeros((P, 16, Hkv, 128), dtype=torch.bfloat16),
+                    v_pool=torch.zeros((P, 16, Hkv, 128), dtype=torch.bfloat16),
+                    q=torch.zeros((rows, Hq, 128), dtype=torch.bfloat16),
+                    k_new=torch.zeros((rows, Hkv, 128), dtype=torch.bfloat16),
+                    v_new=torch.zeros((rows, Hkv, 128), dtype=torch.bfloat16),
+                    out=torch.zeros((rows, Hq, 128), dtype=torch.bfloat16),
+                    lse=torch.zeros((rows, Hq), dtype=torch.float32))
+    layers = [layer(), layer()]
+    table = torch.zeros((rows, 2), dtype=torch.int32)
+    ctx = torch.zeros((rows,), dtype=torch.int32)
+    if bad == "q_rows":
+        layers[1]["q"] = torch.zeros((3, Hq, 128), dtype=torch.bfloat16)
+    elif bad == "pool_pages":
+        layers[0]["v_pool"] = torch.zeros((P - 1, 16, Hkv, 128), dtype=torch.bfloat16)
+    elif bad == "out_dtype":
+        layers[1]["out"] = torch.zeros((rows, Hq, 128), dtype=torch.float32)
+    elif bad == "table_rows":
+        table = torch.zeros((3, 2), dtype=torch.int32)
+    with pytest.raises(ValueError):
+        hd.StepRunner(layers, table, ctx, max_seqs=3, num_pages=P, max_context_len=32, scale=0.088, rope_theta=1e6)
