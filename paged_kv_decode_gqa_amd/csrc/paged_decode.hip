@@ -370,16 +370,31 @@ __device__ __forceinline__ void emit(const DecodeArgs &a, const Smem<G, WAVES> &
     for (int idx = ln.tid; idx < G * kHeadDim; idx += S::kThreadsWG) {
         const int h = __builtin_amdgcn_readfirstlane(idx / kHeadDim);
         const int d = idx % kHeadDim;
+        // The streams' sums for this dim, read before the weights are formed
+        // so that the LDS reads overlap that work rather than each other's.
+        float sums[NS];
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+            sums[s] = sm.acc[s][h][d];
         const float ms = ln.lane < NS ? sm.m[ln.lane][h] : -INFINITY;
         const float ls = ln.lane < NS ? sm.l[ln.lane][h] : 0.f;
         const float M = lanes_max<NS>(ms);
         const float M_use = (M == -INFINITY) ? 0.f : M;
         const float w = merge_weight(ms, M_use);   // 0 past the streams
         const float L = lanes_sum<NS>(ls * w);
-        float A = 0.f;
+        // four independent chains, so the FMAs do not wait on one another
+        constexpr int kChains = NS >= 4 ? 4 : NS;
+        float part[kChains];
+#pragma unroll
+        for (int c = 0; c < kChains; ++c)
+            part[c] = 0.f;
 #pragma unroll
         for (int s = 0; s < NS; ++s)
-            A = fmaf(lane_value(w, s), sm.acc[s][h][d], A);
+            part[s % kChains] = fmaf(lane_value(w, s), sums[s], part[s % kChains]);
+        float A = part[0];
+#pragma unroll
+        for (int c = 1; c < kChains; ++c)
+            A += part[c];
         if (final) {
             store_out<OUT_F32>(a.out, (row0 + h) * kHeadDim + d, A / L);
             if (d == 0 && a.lse != nullptr)
@@ -502,6 +517,14 @@ __device__ __forceinline__ void merge_partials_pre(const DecodeArgs &a, Smem<G, 
     const float w0 = merge_weight(m0, M_use);
     float lsum = l0 * w0;
     const int n0 = min(count, 64);
+    // four independent chains over the prefetched partials, so the FMAs do
+    // not wait on one another
+    float chain[4][K];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            chain[c][k] = 0.f;
 #pragma unroll
     for (int r = 0; r < PRE; ++r) {
         const int i = set + r * S;
@@ -509,9 +532,12 @@ __device__ __forceinline__ void merge_partials_pre(const DecodeArgs &a, Smem<G, 
             const float wi = lane_value(w0, i);
 #pragma unroll
             for (int k = 0; k < K; ++k)
-                A[k] = fmaf(wi, pre[r][k], A[k]);
+                chain[r % 4][k] = fmaf(wi, pre[r][k], chain[r % 4][k]);
         }
     }
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+        A[k] += (chain[0][k] + chain[1][k]) + (chain[2][k] + chain[3][k]);
     add_batches(set + PRE * S, n0, w0, 0);
     for (int c0 = 64; c0 < count; c0 += 64) {   // the later rounds of 64 partials
         const int j = c0 + ln.lane;
