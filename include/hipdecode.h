@@ -261,16 +261,22 @@ hipdecode_status hipdecode_kv_append(const hipdecode_append_params *params,
  * G = num_q_heads / num_kv_heads in {1, 2, 4}.  No workspace; asynchronous on
  * `stream`, graph-capturable.
  *
- * Scores, softmax weights, the running sums and lse are fp32.  The matrix
- * cores take each weight as the sum of two bf16 parts (within 2^-16 of it,
- * relative), so the weighted mean of V is off by at most about 2^-16 times
- * the largest |V| a row attends to, before the output's own rounding.
+ * Scores, softmax weights, the running sums and lse are fp32.  The weighted
+ * sum of V runs on the matrix cores in fp16: each weight is rounded to its
+ * nearest fp16 (within 2^-11, relative; the weights are kept in fp16's normal
+ * range), and V enters exactly (every bf16 value below 2^16 in magnitude has
+ * an fp16 form; below 2^-17 it is kept to within 2^-25).  The output is then
+ * off by at most 2^-11 times the softmax-weighted mean of |V| over the row's
+ * keys, before its own rounding.  V entries of magnitude 2^16 or more are
+ * outside the contract.
  *
  * Device-side contract as for the append: new_start non-decreasing, n_b <=
  * min(c_b, max_new_tokens), rows within num_rows, c_b <= 16 *
- * max_blocks_per_seq, blocks in the pool.  A request that breaks the first
- * conditions writes nothing; pages outside the pool read as page 0, so memory
- * outside the buffers is never touched.
+ * max_blocks_per_seq, blocks in the pool; and |V| < 2^16 for the entries
+ * read.  A request that breaks the first conditions writes nothing; pages
+ * outside the pool read as page 0, so memory outside the buffers is never
+ * touched; V past the range turns into inf in the products of the rows that
+ * attend to it.
  * ------------------------------------------------------------------------ */
 
 typedef struct {
@@ -467,12 +473,16 @@ hipdecode_status hipdecode_paged_attn_noalloc(const hipdecode_params *params,
  *       no page of the pool;
  *   HIPDECODE_VIOLATION_ROWS: append or prefill: a request with more new
  *       tokens than its context or than max_new_tokens, or rows outside
- *       [0, num_rows) (new_start decreasing included).
+ *       [0, num_rows) (new_start decreasing included);
+ *   HIPDECODE_VIOLATION_VALUE: prefill: a V entry that a workgroup read
+ *       has magnitude 2^16 or more (inf included), past the range its
+ *       fp16 products carry exactly.
  * ------------------------------------------------------------------------ */
 
 #define HIPDECODE_VIOLATION_CONTEXT 1u
 #define HIPDECODE_VIOLATION_PAGE 2u
 #define HIPDECODE_VIOLATION_ROWS 4u
+#define HIPDECODE_VIOLATION_VALUE 8u
 
 /* Waits for all work on the current device (hipDeviceSynchronize), then
  * stores in *flags the OR of the HIPDECODE_VIOLATION_* bits that kernels of

@@ -57,6 +57,7 @@ EXPORTED = (
 HIPDECODE_VIOLATION_CONTEXT = 1
 HIPDECODE_VIOLATION_PAGE = 2
 HIPDECODE_VIOLATION_ROWS = 4
+HIPDECODE_VIOLATION_VALUE = 8
 
 # Bytes of the library's static scratch behind hipdecode_paged_attn_noalloc.
 HIPDECODE_NOALLOC_SCRATCH_BYTES = 16 << 20

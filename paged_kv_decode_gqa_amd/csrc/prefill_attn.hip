@@ -23,11 +23,12 @@
 // by in steps of 64 (four
 // pages), copied straight from the pools into a three-stage LDS ring
 // (global_load_lds, two steps ahead), both K and V row-major, and used in two
-// halves of 32.
+// halves of 32.  Before a step's barrier each wavefront rewrites the V rows
+// it copied as fp16, in place.
 //
-// Per 32-key half and wavefront, with v_mfma_f32_32x32x16_bf16 (A 32x16, B 16x32):
-//   S^T[key][row]  = sum_d K[key][d] Q[row][d]        8 MFMAs, A = K, B = Q^T
-//   O^T[dim][row] += sum_key V[key][dim] P[row][key]  16 MFMAs, A = V^T, B = P^T (hi, then lo)
+// Per 32-key half and wavefront, with 32x32x16 MFMAs (A 32x16, B 16x32):
+//   S^T[key][row]  = sum_d K[key][d] Q[row][d]        8 MFMAs (bf16), A = K, B = Q^T
+//   O^T[dim][row] += sum_key V[key][dim] P[row][key]  8 MFMAs (fp16), A = V^T, B = P^T
 // Lane l of the S^T accumulator holds row l % 32 and keys
 // 8(r/4) + 4(l/32) + r%4 for registers r = 0..15, which is exactly how the
 // B operand of the second product wants P^T, provided both products agree
@@ -36,10 +37,11 @@
 // online, in base 2 with scale*log2(e) folded in (one FMA and one v_exp_f32
 // per score), against a running maximum that moves only when the weights
 // grow large; the two lanes (l, l ^ 32) that share a row combine their
-// maxima and sums with v_permlane32_swap.  The matrix cores take each fp32
-// weight as two bf16 parts, hi and lo (two P.V products into the same
-// accumulators), so the weights they apply agree with the fp32 ones that the
-// running sum adds up to 2^-16 relative.
+// maxima and sums with v_permlane32_swap.  P.V runs in fp16: each weight is
+// rounded to the nearest fp16 (2^-11 relative, four times finer than bf16)
+// for the matrix cores, while the running sum adds up the fp32 weights, and
+// V is widened to fp16 in LDS by the wavefront that copied it (exact for
+// |V| < 2^16; larger values are reported as a contract violation).
 #include "hipdecode.h"
 #include "internal.h"
 
@@ -54,6 +56,8 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef short i16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kPfWaves = 8;
 constexpr int kPfThreads = 64 * kPfWaves;
@@ -64,7 +68,9 @@ constexpr int kStepBytes = kKeys * kRowBytes;
 constexpr int kStages = 3;                // LDS stages: the copy runs two steps ahead
 constexpr int kDimBlocks = kHeadDim / 32; // O^T is four 32x32 accumulators
 constexpr float kNegBig = -1.0e30f;       // running-max start: finite, so no inf - inf
-constexpr float kPsumMax = 65536.0f;      // a half's weights summing past this move the running max
+constexpr float kPsumMax = 32768.0f;      // a half's weights summing past this move the running max
+constexpr float kWeightBias = 4.0f;       // weights carry a factor 2^4: the running max sits 4 below the row max
+constexpr float kVMax = 65536.0f;         // |V| from here up has no exact fp16 form
 constexpr int64_t kMaxGrid = (int64_t)1 << 31;
 
 struct PrefillArgs {
@@ -131,6 +137,15 @@ __device__ inline uint32_t pack2_bf16(float x, float y)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
+// Two fp32 values to packed fp16, each rounded to nearest even (one
+// v_cvt_pk_f16_f32).
+__device__ inline uint32_t pack2_f16(float x, float y)
+{
+    const f32x2_t v = {x, y};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
+
+
 // Wait until at most N of this wavefront's vector-memory loads are
 // outstanding (the copies into LDS count among them).
 template <int N>
@@ -146,6 +161,13 @@ __device__ inline void wait_vm()
 // copies still running for later steps.  The memory clobber keeps LDS accesses
 // on their side of it.
 __device__ inline void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// The same barrier after this wavefront's own LDS writes have completed, so
+// that the other wavefronts read them once past it.
+__device__ inline void stage_barrier_after_writes()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 // Copy 16 bytes per lane from global memory (uniform base + 32-bit lane
 // offset) straight into LDS: lane i lands at byte lds_addr + 16 i.  Written
@@ -339,12 +361,11 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qop[ks], s, 0, 0, 0);
         return s;
     };
-    // The softmax weights of one 32-key half, and their bf16 parts.
+    // The softmax weights of one 32-key half, and their fp16 forms.
     struct Half {
         float pw[16];      // 2^(c s - m) per key of this lane
         float psum;        // their sum
-        uint32_t pp[8];    // hi parts, packed pairs (keys in the S^T accumulator's order)
-        uint32_t pl[8];    // lo parts
+        uint32_t pp[8];    // fp16 forms, packed pairs (keys in the S^T accumulator's order)
     };
     // Online softmax in base 2 (row j; keys 8(r/4) + 4 half + r%4).  With
     // c = |scale| log2(e) > 0, the row maximum of c s is c max(s) and
@@ -356,23 +377,22 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
     // computes p = 2^(c s - m) against the m in hand, with no branch; only
     // when some lane's half sums past kPsumMax -- a row maximum well above m,
     // or m still at its start value on a row's first half -- does settle()
-    // find the row maxima, move m, rescale l and the accumulators, and
-    // recompute the weights.  Every weight is then at most kPsumMax, which
-    // fp32 sums and bf16 operands carry with unchanged relative rounding; out
-    // and lse share the reference m.
+    // find the row maxima, move m to 4 below the largest (kWeightBias), rescale
+    // l and the accumulators, and recompute the weights.  Every weight is
+    // then 2^4 times its value against the row maximum; out and lse share the
+    // reference m, so the factor cancels in both.
     //
-    // Each weight goes to the matrix cores as two bf16 parts, hi = the
-    // nearest bf16 and lo = the nearest bf16 of the remainder (exact in
-    // fp32), so hi + lo is within 2^-16 of it (relative) and the weights in
-    // P.V agree with the fp32 ones in l_run.
-    auto split = [&](Half &w) __attribute__((always_inline)) {
+    // Each weight goes to the matrix cores as its nearest fp16, within 2^-11
+    // of it (relative), while l_run adds up the fp32 weights, so out is off
+    // by at most 2^-11 times the weighted mean of |V| over the row's keys.  A
+    // half's fp32 weights sum to at most 2^15 once settled, so none rounds
+    // to an fp16 inf.  With the factor 2^4, weights down to 2^-18 of the row
+    // maximum stay normal fp16 numbers; smaller ones keep an absolute error
+    // under 2^-29 of it, against l >= 2^4 of it.
+    auto pack = [&](Half &w) __attribute__((always_inline)) {
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-            w.pp[r / 2] = pack2_bf16(w.pw[r], w.pw[r + 1]);
-            const float h0 = __uint_as_float(w.pp[r / 2] << 16);
-            const float h1 = __uint_as_float(w.pp[r / 2] & 0xFFFF0000u);
-            w.pl[r / 2] = pack2_bf16(w.pw[r] - h0, w.pw[r + 1] - h1);
-        }
+        for (int r = 0; r < 16; r += 2)
+            w.pp[r / 2] = pack2_f16(w.pw[r], w.pw[r + 1]);
     };
     auto exps = [&](Half &w, const f32x16_t &s, float m) __attribute__((always_inline)) {
         const float c = a.scale_log2;
@@ -393,7 +413,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
             }
         }
         exps(w, s, m_run);
-        split(w);
+        pack(w);
     };
     auto settle = [&](const f32x16_t &s, Half &w) __attribute__((always_inline)) {
         if (__any(!(w.psum <= kPsumMax))) {
@@ -401,7 +421,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 mx = fmaxf(mx, s[r]);
-            const float m_new = fmaxf(m_run, pair_max(mx) * a.scale_log2);
+            const float m_new = fmaxf(m_run, pair_max(mx) * a.scale_log2 - kWeightBias);
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
             m_run = m_new;
             l_run *= alpha;
@@ -409,7 +429,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
             for (int db = 0; db < kDimBlocks; ++db)
                 acc[db] *= alpha;
             exps(w, s, m_new);
-            split(w);
+            pack(w);
         }
         l_run += w.psum;
     };
@@ -432,15 +452,12 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
     auto pv = [&](const i16x8_t (&vv)[2][kDimBlocks], const Half &w) __attribute__((always_inline)) {
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
-            const bf16x8_t phi = __builtin_bit_cast(
-                bf16x8_t, make_uint4(w.pp[4 * kh], w.pp[4 * kh + 1], w.pp[4 * kh + 2], w.pp[4 * kh + 3]));
-            const bf16x8_t plo = __builtin_bit_cast(
-                bf16x8_t, make_uint4(w.pl[4 * kh], w.pl[4 * kh + 1], w.pl[4 * kh + 2], w.pl[4 * kh + 3]));
+            const f16x8_t pop = __builtin_bit_cast(
+                f16x8_t, make_uint4(w.pp[4 * kh], w.pp[4 * kh + 1], w.pp[4 * kh + 2], w.pp[4 * kh + 3]));
 #pragma unroll
             for (int db = 0; db < kDimBlocks; ++db) {
-                const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, vv[kh][db]);
-                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, plo, acc[db], 0, 0, 0);
-                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, phi, acc[db], 0, 0, 0);
+                const f16x8_t vop = __builtin_bit_cast(f16x8_t, vv[kh][db]);
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop, pop, acc[db], 0, 0, 0);
             }
         }
     };
@@ -456,7 +473,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
     };
     // Both halves: the scores of both are issued first, so the matrix cores
     // work on the second half's S while the first half's weights are formed;
-    // the second half's weights and their parts (branch-free) are formed
+    // the second half's weights and their fp16 forms (branch-free) are formed
     // beside the first half's P.V products, whose V^T operands, and the second
     // half's, are read before them; only then can the second half's rare
     // rescale (which needs the first half's products in the accumulators)
@@ -492,6 +509,31 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
         pv(vv1, w1);
     };
 
+    // V rows to fp16, in place in LDS: this wavefront's eight rows of a step
+    // (the ones it copied: bytes 2048 w .. 2048 w + 2047 of the stage), 32
+    // bytes per lane.  A bf16 value has 8 significant bits, so its fp16 form
+    // is exact for 2^-17 <= |v| < 2^16; below that the fp16 subnormals keep it
+    // to within 2^-25.  The largest |v| met is kept, and values from 2^16 up
+    // (inf included) are reported at the end.
+    float v_abs_max = 0.f;
+    auto widen_v = [&](int stg) __attribute__((always_inline)) {
+        uint4 *p = reinterpret_cast<uint4 *>(&v_lds[stg][8 * w * kRowBytes]) + lane;
+        uint4 x[2] = {p[0], p[64]};
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            uint32_t *u = reinterpret_cast<uint32_t *>(&x[i]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float lo = __uint_as_float(u[e] << 16);
+                const float hi = __uint_as_float(u[e] & 0xFFFF0000u);
+                v_abs_max = fmaxf(v_abs_max, fmaxf(fabsf(lo), fabsf(hi)));
+                u[e] = pack2_f16(lo, hi);
+            }
+        }
+        p[0] = x[0];
+        p[64] = x[1];
+    };
+
     // Pipeline: step kb + 2 is copied into LDS while step kb is computed.
     // Per step each wavefront issues four copies; before the barrier of step
     // kb it waits until only step kb + 1's four may still be in flight.
@@ -516,7 +558,8 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
             wait_vm<4>();
         else
             wait_vm<0>();
-        stage_barrier();
+        widen_v(stage);
+        stage_barrier_after_writes();
         if (kb + 2 < nblk)
             issue(kb + 2, stage == 0 ? 2 : stage - 1);
     };
@@ -643,8 +686,10 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
     }
     if (upper)
         write_rows();
-    if (bad_page && lane == 0)
-        report_violation(a.violations, HIPDECODE_VIOLATION_PAGE);
+    const bool big_v = __any(v_abs_max >= kVMax);
+    if ((bad_page || big_v) && lane == 0)
+        report_violation(a.violations,
+                         (bad_page ? HIPDECODE_VIOLATION_PAGE : 0u) | (big_v ? HIPDECODE_VIOLATION_VALUE : 0u));
 }
 
 hipdecode_status check_prefill(const hipdecode_prefill_params *pp)

@@ -464,10 +464,11 @@ def test_fused_call_rejects_before_any_launch():
 def test_header_constants_match_the_binding():
     text = open(HEADER).read()
     defines = {k: v for k, v in re.findall(r"#define (HIPDECODE_\w+) \(?\(?(?:size_t\))?\s*([0-9]+)u?", text)}
-    for name in ("HIPDECODE_VIOLATION_CONTEXT", "HIPDECODE_VIOLATION_PAGE", "HIPDECODE_VIOLATION_ROWS"):
+    names = ("HIPDECODE_VIOLATION_CONTEXT", "HIPDECODE_VIOLATION_PAGE", "HIPDECODE_VIOLATION_ROWS",
+             "HIPDECODE_VIOLATION_VALUE")
+    for name in names:
         assert int(defines[name]) == getattr(hd, name), name
-    bits = [hd.HIPDECODE_VIOLATION_CONTEXT, hd.HIPDECODE_VIOLATION_PAGE, hd.HIPDECODE_VIOLATION_ROWS]
-    assert sorted(bits) == [1, 2, 4]
+    assert sorted(getattr(hd, name) for name in names) == [1, 2, 4, 8]
 
 
 def test_contract_violations_rejects_null_before_any_hip_call():

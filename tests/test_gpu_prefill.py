@@ -7,13 +7,13 @@ correctly rounded result only below 4 in magnitude (half the bf16 spacing is
 at most 2^-7 there, 2^-5 from 4 to 8), so it binds every element with
 |oracle| < 4; every element, those above 4 included, must also meet a
 rounding-level bound derived from the kernel's arithmetic.  The matrix
-cores take every softmax weight p as two bf16 parts, hi (nearest bf16 of p)
-and lo (nearest bf16 of p - hi), so |hi + lo - p| <= 2^-16 p; the running sum
-l is the fp32 sum of the weights themselves.  The weighted mean of V is
-therefore off by at most 2^-16 * max|V| (under 1e-4 for every pool here, all
-|V| < 6.5), and a bf16 output adds its own rounding, at most 2^-8 |out|:
+cores take every softmax weight p as its nearest fp16 (|p~ - p| <= 2^-11 p,
+the weights kept in fp16's normal range) and V exactly, while the running sum
+l adds up the fp32 weights.  The result sum_i p~_i v_i / l is therefore off
+by at most 2^-11 sum_i w_i |v_i| <= 2^-11 Vmax, and a bf16 output adds its
+own rounding, at most 2^-8 |out|:
 
-    |out - oracle| <= 2^-8 |oracle| (bf16 out) + 2^-16 Vmax + 2e-5
+    |out - oracle| <= 2^-8 |oracle| (bf16 out) + 2^-11 (1 + 2^-10) Vmax + 2e-5
 
 with 2e-5 for the fp32 scores, sums and accumulation.  Rows that no request
 names must be left exactly as they were.
@@ -35,7 +35,7 @@ from workloads import (bf16_bits_to_f32, f32_to_bf16_bits, make_append_inputs, m
 pytestmark = pytest.mark.gpu
 
 BF16_EPS = 2.0 ** -8      # unit roundoff of bf16 (8 significant bits, nearest even)
-SPLIT_EPS = 2.0 ** -16    # relative error of a weight given as hi + lo bf16 parts
+F16_EPS = 2.0 ** -11 * (1 + 2.0 ** -10)   # fp16-rounded weights in P.V: error per unit of max |V|
 OUT_ATOL = 1e-2           # max |out - oracle|, as for decode
 BF16_REACH = 4.0          # below this magnitude a correctly rounded bf16 is within 2^-7 of any value
 LSE_RTOL = 1e-4
@@ -70,7 +70,7 @@ def v_max(v_pool):
 
 
 def rounding_bound(ref_o, vmax, bf16_out=True):
-    return (BF16_EPS * np.abs(ref_o) if bf16_out else 0.0) + SPLIT_EPS * vmax + 2e-5
+    return (BF16_EPS * np.abs(ref_o) if bf16_out else 0.0) + F16_EPS * vmax + 2e-5
 
 
 def check_rows(o, l, ref_o, ref_l, what, vmax, bf16_out=True):
@@ -262,6 +262,44 @@ def test_prefill_skips_what_breaks_the_contract():
                                        inp.new_start, case.scale)
     check_rows(o[ok_rows], l[ok_rows], ref_o[ok_rows], ref_l[ok_rows], "valid requests", v_max(case.v_pool))
     assert np.all(o[20:30] == SENTINEL) and np.all(l[20:30] == SENTINEL), "a broken request wrote rows"
+
+
+def _with_v_entries(case, value, seed):
+    """A copy of the case with `value` (and -value) at 16 dims of each
+    request's first key, which every chunk row attends to."""
+    v = bf16_bits_to_f32(case.v_pool).astype(np.float32)
+    rng = np.random.default_rng(seed)
+    for b in range(case.B):
+        page, slot = case.block_table[b, 0], 0
+        dims = rng.choice(case.D, 16, replace=False)
+        v[page, slot, :, dims[:8]] = value
+        v[page, slot, :, dims[8:]] = -value
+    return replace(case, v_pool=f32_to_bf16_bits(v))
+
+
+def test_prefill_v_at_the_top_of_the_fp16_range():
+    """V entries of +-65,280, the largest bf16 below 2^16, enter the fp16
+    products exactly: a one-token context returns its V bit for bit (its
+    weight is exact), the rows that attend to them match the oracle at the
+    rounding-level bound, and no violation is reported.  An entry of 2^16
+    sets HIPDECODE_VIOLATION_VALUE."""
+    case, inp = make_prefill_case([300, 200, 1], [100, 200, 1], seed=50)
+    big = _with_v_entries(case, 65280.0, 500)
+    assert v_max(big.v_pool) == 65280.0
+    hd.hipdecode_contract_violations()
+    o, l = run_gpu(big, inp)
+    assert hd.hipdecode_contract_violations() == 0
+    G = case.Hq // case.Hkv
+    v_one = bf16_bits_to_f32(big.v_pool)[big.block_table[2, 0], 0]          # [Hkv, D]
+    assert np.array_equal(o[inp.new_start[2]], np.repeat(v_one, G, axis=0)), "a one-token context must return V"
+    ref_o, ref_l = oracle.prefill_attn(inp.q, big.k_pool, big.v_pool, big.block_table, big.context_lens,
+                                       inp.new_start, big.scale)
+    assert np.abs(ref_o).max() > 100.0, "the large entries must reach the outputs"
+    # the rounding-level bound with Vmax = 65,280: 2^-11 of it, plus bf16 rounding of out
+    check_rows(o, l, ref_o, ref_l, "V at 65,280", 65280.0)
+    over = _with_v_entries(case, 65536.0, 500)
+    run_gpu(over, inp)
+    assert hd.hipdecode_contract_violations() == hd.HIPDECODE_VIOLATION_VALUE
 
 
 def test_chunked_prefill_pipeline_with_append():
