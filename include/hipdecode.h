@@ -275,8 +275,8 @@ hipdecode_status hipdecode_kv_append(const hipdecode_append_params *params,
  * max_blocks_per_seq, blocks in the pool; and |V| < 2^16 for the entries
  * read.  A request that breaks the first conditions writes nothing; pages
  * outside the pool read as page 0, so memory outside the buffers is never
- * touched; V past the range turns into inf in the products of the rows that
- * attend to it.
+ * touched; V past the range turns into inf in the products of the rows of
+ * its step.
  * ------------------------------------------------------------------------ */
 
 typedef struct {
@@ -474,9 +474,10 @@ hipdecode_status hipdecode_paged_attn_noalloc(const hipdecode_params *params,
  *   HIPDECODE_VIOLATION_ROWS: append or prefill: a request with more new
  *       tokens than its context or than max_new_tokens, or rows outside
  *       [0, num_rows) (new_start decreasing included);
- *   HIPDECODE_VIOLATION_VALUE: prefill: a V entry that a workgroup read
- *       has magnitude 2^16 or more (inf included), past the range its
- *       fp16 products carry exactly.
+ *   HIPDECODE_VIOLATION_VALUE: prefill: a workgroup's weighted sums of V
+ *       came out inf or NaN: a V entry of magnitude 2^16 or more, which
+ *       fp16 cannot hold, reached its products, or q, K or V held inf or
+ *       NaN.
  * ------------------------------------------------------------------------ */
 
 #define HIPDECODE_VIOLATION_CONTEXT 1u

@@ -70,7 +70,6 @@ constexpr int kDimBlocks = kHeadDim / 32; // O^T is four 32x32 accumulators
 constexpr float kNegBig = -1.0e30f;       // running-max start: finite, so no inf - inf
 constexpr float kPsumMax = 32768.0f;      // a half's weights summing past this move the running max
 constexpr float kWeightBias = 4.0f;       // weights carry a factor 2^4: the running max sits 4 below the row max
-constexpr float kVMax = 65536.0f;         // |V| from here up has no exact fp16 form
 constexpr int64_t kMaxGrid = (int64_t)1 << 31;
 
 struct PrefillArgs {
@@ -513,9 +512,9 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
     // (the ones it copied: bytes 2048 w .. 2048 w + 2047 of the stage), 32
     // bytes per lane.  A bf16 value has 8 significant bits, so its fp16 form
     // is exact for 2^-17 <= |v| < 2^16; below that the fp16 subnormals keep it
-    // to within 2^-25.  The largest |v| met is kept, and values from 2^16 up
-    // (inf included) are reported at the end.
-    float v_abs_max = 0.f;
+    // to within 2^-25.  A value of 2^16 or more becomes inf, which makes
+    // every product sum of the step's rows inf or NaN (0 * inf is NaN for
+    // masked keys); write_rows finds that, once per wavefront.
     auto widen_v = [&](int stg) __attribute__((always_inline)) {
         uint4 *p = reinterpret_cast<uint4 *>(&v_lds[stg][8 * w * kRowBytes]) + lane;
         uint4 x[2] = {p[0], p[64]};
@@ -526,7 +525,6 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
             for (int e = 0; e < 4; ++e) {
                 const float lo = __uint_as_float(u[e] << 16);
                 const float hi = __uint_as_float(u[e] & 0xFFFF0000u);
-                v_abs_max = fmaxf(v_abs_max, fmaxf(fabsf(lo), fabsf(hi)));
                 u[e] = pack2_f16(lo, hi);
             }
         }
@@ -583,7 +581,21 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
         stage = stage == kStages - 1 ? 0 : stage + 1;
     }
     // Rows: out[row][h][dim], dims 32 db + 8 (r/4) + 4 half + r%4.
+    // A non-finite product sum: a V entry past fp16's range (or inf or NaN
+    // among q, K and V) reached this wavefront's products.  The sums stay far
+    // below fp32's range otherwise, so their total is finite exactly when
+    // each is.
+    bool nonfinite = false;
     auto write_rows = [&]() __attribute__((always_inline)) {
+        {
+            float t = 0.f;
+#pragma unroll
+            for (int db = 0; db < kDimBlocks; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    t += acc[db][r];
+            nonfinite |= !(fabsf(t) <= 3.0e38f);
+        }
         const float l_tot = pair_sum(l_run);
         if (!row_ok)
             return;
@@ -686,7 +698,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(PrefillArgs a)
     }
     if (upper)
         write_rows();
-    const bool big_v = __any(v_abs_max >= kVMax);
+    const bool big_v = __any(nonfinite);
     if ((bad_page || big_v) && lane == 0)
         report_violation(a.violations,
                          (bad_page ? HIPDECODE_VIOLATION_PAGE : 0u) | (big_v ? HIPDECODE_VIOLATION_VALUE : 0u));

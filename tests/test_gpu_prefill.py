@@ -133,7 +133,10 @@ def test_prefill_poisoned_unused_slots():
     new = [301, 5, 64, 16, 128, 1000]
     case, inp = make_prefill_case(ctx, new, seed=44, poison=True,
                                   pool_pages=sum((c + 15) // 16 for c in ctx) + 9)
+    hd.hipdecode_contract_violations()
     o, l = run_gpu(case, inp)
+    # no NaN reaches the products, so no non-finite sum is reported either
+    assert hd.hipdecode_contract_violations() == 0
     check_full(case, inp, o, l, "poisoned unused slots")
 
 
