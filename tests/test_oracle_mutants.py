@@ -70,12 +70,14 @@ APPEND_MUTANTS = {
 
 # Slips in the prefill oracle: the causal cut off by one, positions counted
 # from the chunk start, the query of the request instead of the row, the
-# first request's table row for everyone.
+# first request's table row for everyone, and (in the listed-pairs entry
+# point) a pair's neighbouring query head.
 PREFILL_MUTANTS = {
     "cut_excludes_own_token": [("const int32_t visible = pos + 1;", "const int32_t visible = pos;")],
     "positions_from_chunk_start": [("*pos_out = context_lens[b] - n + (r - start);", "*pos_out = r - start;")],
     "query_of_request": [("q + (size_t)r * s->num_q_heads * s->head_dim", "q + (size_t)b * s->num_q_heads * s->head_dim")],
     "first_table_row": [("block_table + (size_t)b * s->max_blocks, &visible", "block_table, &visible")],
+    "pairs_neighbouring_head": [("pairs[2 * i + 1], scale,", "pairs[2 * i + 1] ^ 1, scale,")],
 }
 
 
