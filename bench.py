@@ -207,6 +207,9 @@ def main(argv=None) -> int:
     ap.add_argument("--configs", default="c3,c3b,c5",
                     help="decode, default workload only: further workloads timed the same way after c4 and "
                          "reported under \"configs\" (comma-separated; \"none\" to skip)")
+    ap.add_argument("--no-other-ops", dest="other_ops", action="store_false",
+                    help="decode, default workload only: skip timing prefill p1 and append a2 after the "
+                         "decode workloads (reported under \"other_ops\")")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for the traffic counters)")
@@ -346,6 +349,29 @@ def main(argv=None) -> int:
         }
         del c, mw
         torch.cuda.empty_cache()
+    # the other entry points on their named workloads, timed the same way in
+    # the same run: the last 4,096-token prefill chunk of a 28,672-token
+    # prompt, and the append of such a chunk with RoPE
+    if args.other_ops and not (args.context > 0 or named):
+        result["other_ops"] = {}
+        for key, fn, w in (("prefill_p1", run_prefill, "p1"), ("append_a2", run_append, "a2")):
+            r = fn(args, dev, name=w, emit=False)
+            rr = r["roofline"]
+            result["other_ops"][key] = {
+                "metric": r["metric"],
+                "workload": r["config"]["workload"],
+                "tokens_per_s": r["value"],
+                "us_per_layer": r["us_per_layer"],
+                "achieved": rr["achieved"],
+                "unit": rr["unit"],
+                "peak": rr["peak"],
+                "bound": rr["bound"],
+                "frac": rr["frac"],
+                "traffic": rr["traffic"],
+                "kernel": rr["kernel"],
+            }
+            del r
+            torch.cuda.empty_cache()
     result["setup_s"] = round(t_gen, 2)
     print(json.dumps(result), flush=True)
     return 0
@@ -475,14 +501,16 @@ def measure_decode(case, workload: str, args, dev) -> dict:
     return m
 
 
-def run_append(args, dev) -> int:
+def run_append(args, dev, name=None, emit=True):
+    """Time the append workload `name` (default a2); print its JSON line, or
+    return the result without the CPU baseline when `emit` is false."""
     import numpy as np
     import torch
 
     import paged_kv_decode_gqa_amd as hd
     from workloads import APPEND_CONFIGS, make_append_config
 
-    name = args.workload or "a2"
+    name = name or args.workload or "a2"
     if name not in APPEND_CONFIGS:
         print(f"unknown append workload {name}", file=sys.stderr)
         return 2
@@ -592,6 +620,8 @@ def run_append(args, dev) -> int:
     traffic = read_traffic("kv_append_kernel", name)
     if traffic is not None:
         result["roofline"]["traffic"] = round(traffic)
+    if not emit:
+        return result
     if not args.no_cpu_baseline:
         import oracle
         reps, t_cpu = 0, 0.0
@@ -747,14 +777,16 @@ def run_step(args, dev) -> int:
     return 0
 
 
-def run_prefill(args, dev) -> int:
+def run_prefill(args, dev, name=None, emit=True):
+    """Time the prefill workload `name` (default p1); print its JSON line, or
+    return the result without the CPU baseline when `emit` is false."""
     import numpy as np
     import torch
 
     import paged_kv_decode_gqa_amd as hd
     from workloads import PREFILL_CONFIGS, make_prefill_config
 
-    name = args.workload or "p1"
+    name = name or args.workload or "p1"
     if name not in PREFILL_CONFIGS:
         print(f"unknown prefill workload {name}", file=sys.stderr)
         return 2
@@ -860,6 +892,8 @@ def run_prefill(args, dev) -> int:
     traffic = read_traffic("prefill_attn_kernel", name)
     if traffic is not None:
         result["roofline"]["traffic"] = round(traffic)
+    if not emit:
+        return result
     if not args.no_cpu_baseline:
         import oracle
         rng = np.random.default_rng(0)
