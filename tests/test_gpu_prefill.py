@@ -200,6 +200,40 @@ def test_prefill_dominant_key():
     assert big.sum() > 1000, "the dominated rows must put outputs in [2, 4)"
 
 
+def _random_prefill_shapes(seed, n):
+    """Seeded random small prefill shapes: group size, KV heads, chunk and
+    context lengths around the half-tile sizes, output type, scale sign and
+    size, poisoned slots."""
+    rng = np.random.default_rng(seed)
+    shapes = []
+    for i in range(n):
+        G, Hkv = [(1, 8), (2, 8), (4, 4), (2, 2), (1, 1), (4, 1)][rng.integers(6)]
+        reqs = []
+        for _ in range(int(rng.integers(1, 5))):
+            c = int(rng.choice([1, 15, 16, 17, 63, 64, 65, 127, 300, 1000, 2100]))
+            n_new = int(rng.choice([c, 1, 33, 64, 129, c // 2]))
+            reqs.append((c, min(c, n_new)))
+        shapes.append(dict(i=i, G=G, Hkv=Hkv, reqs=reqs, f32=bool(rng.random() < 0.3),
+                           scale=float(rng.choice([1 / np.sqrt(128), -0.05, 0.0, 0.3])),
+                           poison=bool(rng.random() < 0.5)))
+    return shapes
+
+
+@pytest.mark.parametrize("shape", _random_prefill_shapes(77, 20), ids=lambda s: f"r{s['i']}")
+def test_prefill_random_small_shapes(shape):
+    ctx = [c for c, _ in shape["reqs"]]
+    new = [n for _, n in shape["reqs"]]
+    case, inp = make_prefill_case(ctx, new, seed=700 + shape["i"], Hq=shape["G"] * shape["Hkv"], Hkv=shape["Hkv"],
+                                  poison=shape["poison"], pool_pages=sum((c + 15) // 16 for c in ctx) + 3,
+                                  extra_rows=shape["i"] % 3)
+    case = replace(case, scale=shape["scale"])
+    what = (f"random {shape['i']}: G={shape['G']} Hkv={shape['Hkv']} (ctx, chunk)={shape['reqs']} "
+            f"scale={shape['scale']:.3g} {'f32' if shape['f32'] else 'bf16'}{' poisoned' if shape['poison'] else ''}")
+    log(f"[prefill] {what}")
+    o, l = run_gpu(case, inp, out_dtype=torch.float32 if shape["f32"] else torch.bfloat16)
+    check_full(case, inp, o, l, what, bf16_out=not shape["f32"])
+
+
 def test_prefill_fp32_out():
     case, inp = make_prefill_case([450, 97], [160, 97], seed=43)
     o, l = run_gpu(case, inp, out_dtype=torch.float32)
