@@ -14,6 +14,9 @@ given disagrees with an independent fact:
   out = v_0 exactly and lse = z_0;
 * splitting a chunk into two smaller chunks, the second after the first has
   been cached, gives the same rows;
+* closed form: when every key of a request is the same, the softmax is
+  uniform over the visible keys, so chunk row j returns the mean of V over
+  positions 0 .. p_j and its LSE is z + ln(p_j + 1), z being the one score;
 * argument validation.
 
 Dense keys and values are scattered into a shuffled pool by this file's own
@@ -30,7 +33,7 @@ import sys
 import numpy as np
 
 import oracle
-from tests.oracle_pins import Dense, _bits, _close, _f64
+from tests.oracle_pins import Dense, _bits, _close, _f64  # noqa: F401
 
 SHAPES = [  # (Hq, Hkv, D, page, [(context, chunk) per request])
     (2, 1, 4, 4, [(9, 9)]),
@@ -121,6 +124,31 @@ def pin_rechunking(lib):
         np.array_equal(np.concatenate([a_lse, b_lse]), whole_lse[:n]), "re-chunking changed the rows"
 
 
+def pin_equal_keys_prefix_mean(lib):
+    rng = np.random.default_rng(307)
+    Hq, Hkv, D, page = 4, 2, 16, 4
+    reqs = [(13, 13), (9, 4)]
+    G = Hq // Hkv
+    ks = [np.repeat(_bits(rng, (1, Hkv, D)), c, axis=0) for c, _ in reqs]   # one key row per request
+    vs = [_bits(rng, (c, Hkv, D)) for c, _ in reqs]
+    dn = Dense(_bits(rng, (len(reqs), Hq, D)), ks, vs, page, rng)
+    ns = np.concatenate([[0], np.cumsum([n for _, n in reqs])]).astype(np.int32)
+    q = _bits(rng, (int(ns[-1]), Hq, D))
+    scale = 0.25
+    out, lse = oracle.prefill_attn(q, dn.k_pool, dn.v_pool, dn.table, dn.ctx, ns, scale, lib=lib)
+    for b, (c, n) in enumerate(reqs):
+        for j in range(n):
+            r, p = int(ns[b]) + j, c - n + j
+            for h in range(Hq):
+                g = h // G
+                mean = _f64(vs[b][: p + 1, g]).mean(axis=0)
+                assert np.allclose(out[r, h], mean, rtol=0.0, atol=1e-12), \
+                    f"equal keys: row {r} head {h} must be the mean of V over positions 0..{p}"
+                z = scale * float(_f64(q[r, h]) @ _f64(ks[b][0, g]))
+                want = z + math.log(p + 1)
+                assert abs(lse[r, h] - want) <= 1e-12 * max(1.0, abs(want)), f"equal keys: LSE of row {r} head {h}"
+
+
 def pin_pairs_match_full(lib):
     rng = np.random.default_rng(305)
     dn, q, ns = _case(rng, 16, 8, 128, 16, [(50, 30), (20, 3)])
@@ -155,6 +183,7 @@ PINS = [
     pin_last_row_is_decode,
     pin_first_row_sees_one_token,
     pin_rechunking,
+    pin_equal_keys_prefix_mean,
     pin_pairs_match_full,
     pin_validation,
 ]

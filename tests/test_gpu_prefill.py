@@ -234,6 +234,26 @@ def test_prefill_random_small_shapes(shape):
     check_full(case, inp, o, l, what, bf16_out=not shape["f32"])
 
 
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_prefill_equal_keys(out_dtype):
+    """Every key of a request the same: the softmax is uniform over the
+    visible keys, and chunk row j returns the mean of V over positions
+    0 .. p_j (the oracle's closed-form pin).  All of a row's fp16 weights are
+    then equal, so their rounding errors all point the same way."""
+    ctx, new = [700, 300], [256, 300]
+    case, inp = make_prefill_case(ctx, new, seed=51)
+    k = bf16_bits_to_f32(case.k_pool).astype(np.float32)
+    rng = np.random.default_rng(510)
+    for b, c in enumerate(ctx):
+        key = rng.standard_normal((case.Hkv, case.D)).astype(np.float32)
+        for t in range(c):
+            k[case.block_table[b, t // 16], t % 16] = key
+    case = replace(case, k_pool=f32_to_bf16_bits(k))
+    o, l = run_gpu(case, inp, out_dtype=out_dtype)
+    f32 = out_dtype == torch.float32
+    check_full(case, inp, o, l, "equal keys" + (", fp32 out" if f32 else ""), bf16_out=not f32)
+
+
 def test_prefill_fp32_out():
     case, inp = make_prefill_case([450, 97], [160, 97], seed=43)
     o, l = run_gpu(case, inp, out_dtype=torch.float32)
